@@ -1,0 +1,183 @@
+/*
+ * pa.h -- C ABI of libpa, the paged KV-cache decode path for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources (web pages on PagedAttention, cited by title and section):
+ *   P1  Ultralytics glossary page "PagedAttention" (Turkish): introduction;
+ *       "Sayfalama Nasıl Çalışır" (how paging works, with a PyTorch code
+ *       sketch of a block pool, a free list and a block table);
+ *       "Diziler Arasında Blokları Paylaşma" (sharing blocks between
+ *       sequences); "İlgili Teknikler" (related techniques: FlashAttention,
+ *       grouped-query attention, FP8 cache quantisation).
+ *   P3  gyaansetu.com page on KV memory and PagedAttention (Persian),
+ *       article A "how PagedAttention solves it" (on-demand pages, shared
+ *       prefix with copy-on-write) and article B "the solution" (page table).
+ *
+ * Data layout (all device memory, row-major, owned by the caller):
+ *   K pool, V pool   [num_blocks][block_size][Hkv][D] of the KV dtype.  A
+ *                    physical block holds block_size consecutive tokens of
+ *                    one sequence for every KV head (P1 "Sayfalama Nasıl
+ *                    Çalışır": fixed-size blocks, 16 tokens by default).
+ *   block_tables     int32 [B][max_blocks_per_seq]: entry j of row b is the
+ *                    physical block holding tokens [j*bs, (j+1)*bs) of
+ *                    sequence b (P1 introduction: one block table per
+ *                    request, like an OS page table; P3 article B).  Only the
+ *                    first ceil(seq_lens[b] / bs) entries are read.
+ *   seq_lens         int32 [B]: tokens in each sequence's context.
+ *   flat slot        block * block_size + offset, the index of one token row
+ *                    of one block (P1 code sketch, write loop).
+ *
+ * Conventions:
+ *   - Every call is a host function that validates its arguments, then
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns without synchronising.  The library never
+ *     allocates, frees or synchronises device memory; it keeps no state
+ *     except a per-device cache of the compute-unit count.
+ *   - Host-side validation failures return a pa_status other than PA_OK,
+ *     enqueue nothing and print nothing.  PA_ERR_LAUNCH reports a failed
+ *     kernel launch (hipGetLastError).  Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - Device-side index checks: block ids outside [0, num_blocks), slots
+ *     outside [0, num_blocks*block_size) and block-copy pairs outside the
+ *     pool are skipped (nothing read or written for them); seq_lens are
+ *     clamped to [0, max_blocks_per_seq*block_size].  Results for a sequence
+ *     whose table holds such ids are then meaningless, but no access leaves
+ *     the caller's buffers.
+ *   - Calls on one stream are ordered; the library is thread-safe.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+/* Element types.  PA_FP8_E4M3 is OCP e4m3 "fn": 1 sign, 4 exponent (bias 7),
+ * 3 mantissa bits, S.1111.111 = NaN, max +-448, no infinities; a stored code
+ * c means value(c) * scale with one fp32 scale per pool (P1 "İlgili
+ * Teknikler": an 8-bit KV cache, about half the memory of 16-bit). */
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  PA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent              */
+  PA_ERR_UNSUPPORTED = 3, /* dtype / head dim / block size / group not built     */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required          */
+  PA_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch            */
+} pa_status;
+
+/* Arguments of one decode step over a batch (one layer). */
+typedef struct pa_decode_args {
+  void* out;                   /* [B][Hq][D] out_dtype, written                       */
+  const void* q;               /* [B][Hq][D] q_dtype                                  */
+  const void* k_cache;         /* [num_blocks][block_size][Hkv][D] kv_dtype           */
+  const void* v_cache;         /* same shape and dtype as k_cache                     */
+  const int32_t* block_tables; /* [B][max_blocks_per_seq]                             */
+  const int32_t* seq_lens;     /* [B]                                                 */
+  int32_t B, Hq, Hkv, D;
+  int32_t block_size, num_blocks, max_blocks_per_seq;
+  float scale;                 /* softmax scale, e.g. 1/sqrt(D)                       */
+  float k_scale, v_scale;      /* fp8 dequantisation scales; must be 1 otherwise      */
+  pa_dtype q_dtype, kv_dtype, out_dtype;
+  int32_t partition_size;      /* tokens per split-K partition, a multiple of         */
+                               /* block_size; 0 = library default (512)               */
+  void* workspace;             /* device scratch for split-K partials                 */
+  size_t workspace_bytes;      /* >= pa_decode_workspace_size(args)                   */
+} pa_decode_args;
+
+/* Supported decode combinations (others return PA_ERR_UNSUPPORTED):
+ *   D in {64, 128}; block_size in {16, 32}; G = Hq/Hkv in {1, 2, 4, 8};
+ *   (q, kv) in {(F32,F32), (F16,F16), (BF16,BF16), (BF16,FP8_E4M3),
+ *   (F16,FP8_E4M3)}; out_dtype = q_dtype or PA_F32. */
+
+/* Bytes of workspace pa_decode needs: 4*B*Hq*P*(D+2) with
+ * P = ceil(max_blocks_per_seq*block_size / partition_size), or 0 when one
+ * partition covers every sequence.  Returns 0 for invalid arguments. */
+size_t pa_decode_workspace_size(const pa_decode_args* a);
+
+/* Validate decode arguments without touching the GPU. */
+pa_status pa_decode_check(const pa_decode_args* a);
+
+/* Paged decode attention (P1 "Sayfalama Nasıl Çalışır": the attention kernel
+ * follows the block table to gather keys and values block by block; P1
+ * "İlgili Teknikler": FlashAttention-style tiling, the score matrix never
+ * reaches device memory; grouped-query attention).  For every sequence b and
+ * query head h, with g = h / (Hq/Hkv) and L = seq_lens[b]:
+ *   s_t   = scale * k_scale * sum_d q[b,h,d] * K[t,g,d]      for t < L
+ *   out   = v_scale * sum_t exp(s_t - max s) V[t,g,:] / sum_t exp(s_t - max s)
+ * where K[t,g,:] is row (t mod bs, g) of block block_tables[b][t / bs].
+ * L = 0 gives zeros.  fp32 accumulation; out rounded to nearest even.
+ * Equivalent to pa_decode_partition followed by pa_decode_reduce. */
+pa_status pa_decode(const pa_decode_args* a, void* stream);
+
+/* Split-K step 1: one work-group per (sequence, KV head, partition of
+ * partition_size tokens) computes the partition's running max m, sum l and
+ * unnormalised V-weighted sum with an online softmax.  Sequences that fit in
+ * one partition are finished here (out written); others leave fp32 partials
+ * in the workspace. */
+pa_status pa_decode_partition(const pa_decode_args* a, void* stream);
+
+/* Split-K step 2: for sequences longer than one partition, combine the
+ * partials: M = max_p m_p, out = sum_p e^(m_p-M) acc_p / sum_p e^(m_p-M) l_p.
+ * Enqueues nothing when one partition covers every sequence. */
+pa_status pa_decode_reduce(const pa_decode_args* a, void* stream);
+
+/* Slot of each sequence's new token (P1 "Sayfalama Nasıl Çalışır", code
+ * sketch: position pos goes to block table[pos / bs] at offset pos % bs):
+ *   slots[b] = block_tables[b][positions[b] / block_size] * block_size
+ *              + positions[b] % block_size
+ * and -1 when positions[b] < 0, when positions[b] / block_size >=
+ * max_blocks_per_seq or when that table entry is negative.
+ * block_tables int32 [B][max_blocks_per_seq], positions and slots int32 [B],
+ * device memory. */
+pa_status pa_slot_mapping(const int32_t* block_tables, const int32_t* positions, int32_t B,
+                          int32_t max_blocks_per_seq, int32_t block_size, int32_t* slots,
+                          void* stream);
+
+/* Cache write (P1 "Sayfalama Nasıl Çalışır", code sketch write loop): for
+ * every i < T with 0 <= slot_mapping[i] < num_blocks*block_size,
+ *   k_cache[slot / bs][slot % bs][:][:] = enc(k_new[i][:][:]), same for V.
+ * k_new, v_new: [T][Hkv][D] of src_dtype.  enc is the identity (a bit copy)
+ * when src_dtype == kv_dtype.  For kv_dtype == PA_FP8_E4M3 and src_dtype in
+ * {F32, F16, BF16}: enc(x) = e4m3(fl32(x * fl32(1/k_scale))) (v_scale for V),
+ * rounded to nearest even, saturating to +-448 (also +-inf), NaN -> 0x7F
+ * with the NaN's sign.  Other combinations return PA_ERR_UNSUPPORTED. */
+pa_status pa_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
+                               int32_t block_size, int32_t num_blocks, pa_dtype src_dtype,
+                               pa_dtype kv_dtype, float k_scale, float v_scale, void* stream);
+
+/* Copy-on-write block copy (P1 "Diziler Arasında Blokları Paylaşma": a
+ * sequence about to write into a block that other sequences still use gets a
+ * copy first; P3 article A, shared prefix support).  For each of the P rows
+ * (src, dst) of block_mapping (int32 [P][2], device memory), copies the whole
+ * block -- every slot, every head, K and V -- from src to dst.
+ * Precondition: dst blocks are distinct and no dst is also a src in the same
+ * call (otherwise the result depends on scheduling).  P == 0 enqueues
+ * nothing. */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int32_t P,
+                         int32_t num_blocks, int32_t block_size, int32_t Hkv, int32_t D,
+                         pa_dtype kv_dtype, void* stream);
+
+/* Static description of a status code. */
+const char* pa_status_str(pa_status s);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

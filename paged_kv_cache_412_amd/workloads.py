@@ -1,0 +1,259 @@
+"""Seeded synthetic inputs for the paged decode path.
+
+This module makes inputs only: shapes, sequence lengths, scattered block
+tables, pool contents, new K/V rows and queries.  It holds none of the path's
+arithmetic (no slot computation, no attention, no quantiser of its own), so the
+GPU library and the CPU oracle can both be fed from it.
+
+Workloads (shapes follow the pages' examples; P1 = Ultralytics glossary page
+"PagedAttention", P3 = gyaansetu.com page on KV memory and PagedAttention):
+
+* ``tiny``   -- 4 sequences of {40, 17, 64, 1} tokens, 8 heads, head dim 64,
+  block size 16 (P1 "Sayfalama Nasıl Çalışır": the default block size, and the
+  40-token request of the code sketch), fp32, a pool of 64 blocks.
+* ``llama13b`` -- a LLaMA-13B-shaped layer (P1 "Çözdüğü Bellek Sorunu"): 40 heads,
+  head dim 128, fp16, batch 64, lengths uniform in [128, 2048].
+* ``llama70b`` -- a Llama-3.1-70B-shaped GQA layer (P3 article A, the memory
+  problem): 64 query / 8 KV heads, head dim 128, bf16, batch 256, 4,096
+  tokens each.
+* ``shared`` -- shared-prefix parallel sampling (P1 "Diziler Arasında Blokları
+  Paylaşma"): 32 prompts x 3 samples, a 1,024-token prefix held once,
+  per-prompt stems of 64..512 tokens shared by the 3 samples, 40 heads,
+  head dim 128, fp16.
+* ``long_fp8`` / ``long_fp8_bs32`` -- long context with an e4m3 cache and one
+  fp32 scale per pool (P1 "İlgili Teknikler": GQA and FP8 cache), 32 query /
+  8 KV heads, head dim 128, batch 16, lengths uniform in [16384, 32768],
+  block size 16 or 32, bf16 queries and new rows.
+
+State handed to the step (the "pre-step" state): every sequence's cache holds
+its first L-1 tokens; the decode step appends token L-1 and then attends over
+all L tokens.  Tables hold ceil((L-1)/bs) blocks; the host block manager
+adds a block where the new token starts one, or copies a shared last block.
+
+Poisoning (correctness runs): free blocks, the slots after the last cached
+token of each sequence, and table padding (-1) are filled with NaN (0x7F for
+e4m3), so a kernel that reads a slot it must not read produces NaN.
+
+Randomness: structure (lengths, free-list shuffle, stems) comes from
+``numpy.random.default_rng(seed)``; values (pools, rows, queries) from a
+``torch.Generator`` on the target device seeded with the same number, drawn
+N(0, 1) in fp32 and rounded to the storage dtype.  The e4m3 pools use
+``scale = amax / 448`` of the drawn fp32 data and torch's own e4m3 cast of
+``x / scale`` (the values are inputs; the path's quantiser is the cache
+write, which this module never performs).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+F32, F16, BF16, E4M3 = "f32", "f16", "bf16", "e4m3"
+TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, E4M3: torch.uint8}
+ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    config_id: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    block_size: int
+    kv_dtype: str
+    q_dtype: str
+    out_dtype: str
+    src_dtype: str              # dtype of the new K/V rows handed to the cache write
+    lens: tuple = ()            # fixed lengths (tiny) ...
+    len_range: tuple = ()       # ... or inclusive uniform range
+    pool_blocks: int = 0        # fixed pool size, else needed * (1 + slack)
+    slack: float = 0.10
+    shared: dict = field(default_factory=dict)  # shared-prefix layout parameters
+    partition_size: int = 512
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def seed(self) -> int:
+        return 412_000 + self.config_id
+
+
+CONFIGS = {
+    "tiny": Config("tiny", 1, B=4, Hq=8, Hkv=8, D=64, block_size=16, kv_dtype=F32, q_dtype=F32,
+                   out_dtype=F32, src_dtype=F32, lens=(40, 17, 64, 1), pool_blocks=64),
+    "llama13b": Config("llama13b", 2, B=64, Hq=40, Hkv=40, D=128, block_size=16, kv_dtype=F16,
+                       q_dtype=F16, out_dtype=F16, src_dtype=F16, len_range=(128, 2048)),
+    "llama70b": Config("llama70b", 3, B=256, Hq=64, Hkv=8, D=128, block_size=16, kv_dtype=BF16,
+                       q_dtype=BF16, out_dtype=BF16, src_dtype=BF16, lens=(4096,) * 256),
+    "shared": Config("shared", 4, B=96, Hq=40, Hkv=40, D=128, block_size=16, kv_dtype=F16,
+                     q_dtype=F16, out_dtype=F16, src_dtype=F16,
+                     shared=dict(prompts=32, samples=3, prefix=1024, stem=(64, 512))),
+    "long_fp8": Config("long_fp8", 5, B=16, Hq=32, Hkv=8, D=128, block_size=16, kv_dtype=E4M3,
+                       q_dtype=BF16, out_dtype=BF16, src_dtype=BF16, len_range=(16384, 32768)),
+    "long_fp8_bs32": Config("long_fp8_bs32", 6, B=16, Hq=32, Hkv=8, D=128, block_size=32,
+                            kv_dtype=E4M3, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
+                            len_range=(16384, 32768)),
+}
+
+
+def small(cfg: Config, **kw) -> Config:
+    """A reduced copy of a config for oracle-speed parity runs."""
+    return replace(cfg, **kw)
+
+
+@dataclass
+class Workload:
+    """Pre-step state of one decode step plus the new token's rows.
+
+    Host-side structure (NumPy): ``seq_lens`` (L, including the new token),
+    ``tables`` (list of lists: pre-step block tables), ``refs`` (block ->
+    number of tables that reference it), ``free`` (remaining free list, FIFO
+    order).  Device tensors: ``q [B,Hq,D]``, ``k_pool``/``v_pool``
+    ``[NB,bs,Hkv,D]``, ``k_new``/``v_new`` ``[B,Hkv,D]``.
+    """
+
+    cfg: Config
+    seq_lens: np.ndarray
+    tables: list
+    refs: dict
+    free: list
+    num_blocks: int
+    q: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    scale: float = 0.0
+
+    @property
+    def max_blocks(self) -> int:
+        bs = self.cfg.block_size
+        return max(1, max(-(-int(L) // bs) for L in self.seq_lens))
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-int(a) // int(b))
+
+
+def _poison_value(dtype: str):
+    return 0x7F if dtype == E4M3 else float("nan")
+
+
+def _fill_values(shape, dtype: str, gen: torch.Generator, device, sigma: float = 1.0):
+    """N(0, sigma^2) draws rounded to ``dtype``; e4m3 returns (codes, scale)."""
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    if dtype == E4M3:
+        scale = float(x.abs().max()) / 448.0
+        codes = (x / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        return codes, scale
+    return x.to(TORCH_DTYPE[dtype]), 1.0
+
+
+def _lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
+    if cfg.lens:
+        return np.array(cfg.lens[: cfg.B], dtype=np.int64)
+    lo, hi = cfg.len_range
+    return rng.integers(lo, hi, size=cfg.B, endpoint=True).astype(np.int64)
+
+
+def make(cfg: Config, device="cpu", poison: bool = True, q_sigma: float = 1.0) -> Workload:
+    """Build the seeded pre-step state of ``cfg`` on ``device``."""
+    if cfg.shared:
+        return _make_shared(cfg, device, poison, q_sigma)
+    rng = np.random.default_rng(cfg.seed)
+    gen = torch.Generator(device=device).manual_seed(cfg.seed)
+    bs = cfg.block_size
+    lens = _lengths(cfg, rng)
+    cached = np.maximum(lens - 1, 0)                 # tokens already in the cache
+    need_total = int(sum(_ceil_div(L, bs) for L in lens))
+    NB = cfg.pool_blocks or int(np.ceil(need_total * (1.0 + cfg.slack)))
+    if NB < need_total:
+        raise ValueError("pool too small")
+    free = [int(b) for b in rng.permutation(NB)]
+    tables, refs = [], {}
+    for c in cached:
+        row = [free.pop(0) for _ in range(_ceil_div(int(c), bs))]
+        for blk in row:
+            refs[blk] = 1
+        tables.append(row)
+    wl = _values(cfg, device, gen, lens, tables, NB, free, refs, poison, q_sigma)
+    return wl
+
+
+def _make_shared(cfg: Config, device, poison: bool, q_sigma: float) -> Workload:
+    sh = cfg.shared
+    rng = np.random.default_rng(cfg.seed)
+    gen = torch.Generator(device=device).manual_seed(cfg.seed)
+    bs = cfg.block_size
+    P, S, prefix = sh["prompts"], sh["samples"], sh["prefix"]
+    stems = rng.integers(sh["stem"][0], sh["stem"][1], size=P, endpoint=True).astype(np.int64)
+    lens = np.repeat(prefix + stems + 1, S)           # L includes the new token
+    # blocks: prefix + stems + one possible new/copied block per sample
+    need_shared = _ceil_div(prefix, bs) + int(sum(_ceil_div(int(c), bs) for c in stems))
+    NB = int(np.ceil((need_shared + P * S) * (1.0 + cfg.slack)))
+    free = [int(b) for b in rng.permutation(NB)]
+    refs = {}
+    prefix_row = [free.pop(0) for _ in range(_ceil_div(prefix, bs))]
+    if prefix % bs:
+        raise ValueError("the shared prefix is assumed to fill whole blocks")
+    for blk in prefix_row:
+        refs[blk] = P * S
+    tables = []
+    for p in range(P):
+        stem_row = [free.pop(0) for _ in range(_ceil_div(int(stems[p]), bs))]
+        for blk in stem_row:
+            refs[blk] = S
+        for _ in range(S):
+            tables.append(prefix_row + stem_row)
+    return _values(cfg, device, gen, lens, tables, NB, free, refs, poison, q_sigma)
+
+
+def _values(cfg, device, gen, lens, tables, NB, free, refs, poison, q_sigma) -> Workload:
+    bs, Hkv, D = cfg.block_size, cfg.Hkv, cfg.D
+    k_pool, k_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device)
+    v_pool, v_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device)
+    if poison:
+        pv = _poison_value(cfg.kv_dtype)
+        used = np.zeros(NB, dtype=bool)
+        for row in tables:
+            used[row] = True
+        free_ids = torch.as_tensor(np.nonzero(~used)[0], device=device, dtype=torch.long)
+        k_pool.index_fill_(0, free_ids, pv)
+        v_pool.index_fill_(0, free_ids, pv)
+        # slots after the last cached token of each distinct table
+        seen = set()
+        for row, L in zip(tables, lens):
+            cached = max(int(L) - 1, 0)
+            if not row or cached % bs == 0:
+                continue
+            key = (row[-1], cached % bs)
+            if key in seen:
+                continue
+            seen.add(key)
+            k_pool[row[-1], cached % bs:] = pv
+            v_pool[row[-1], cached % bs:] = pv
+    B, Hq = cfg.B, cfg.Hq
+    k_new, _ = _fill_values((B, Hkv, D), cfg.src_dtype, gen, device)
+    v_new, _ = _fill_values((B, Hkv, D), cfg.src_dtype, gen, device)
+    q, _ = _fill_values((B, Hq, D), cfg.q_dtype, gen, device, sigma=q_sigma)
+    return Workload(cfg=cfg, seq_lens=np.asarray(lens, dtype=np.int64), tables=tables, refs=refs,
+                    free=free, num_blocks=NB, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new,
+                    v_new=v_new, k_scale=k_scale, v_scale=v_scale, scale=1.0 / float(np.sqrt(D)))
+
+
+def pad_tables(tables: list, width: int) -> np.ndarray:
+    """Rows of block ids padded with -1 to ``width`` (int32)."""
+    out = np.full((len(tables), width), -1, dtype=np.int32)
+    for i, row in enumerate(tables):
+        out[i, : len(row)] = row
+    return out

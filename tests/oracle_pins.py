@@ -1,0 +1,269 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``check_*`` takes the oracle function(s) it exercises as arguments and
+raises ``AssertionError`` when they disagree with the pages, a closed form, a
+library routine or brute force.  ``tests/test_oracle_*.py`` runs them on the
+oracle; ``tests/test_oracle_mutants.py`` runs them on deliberately broken
+copies of oracle functions and requires each copy to be caught.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name: str) -> dict:
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# P1 "Sayfalama Nasıl Çalışır": the worked example (code sketch + its output)
+# --------------------------------------------------------------------------
+
+def check_worked_example(BlockPool, allocate_sequence, slot_mapping, write_cache, gather,
+                         paged_unused_slots, reserved_unused_slots, seed=0):
+    g = load_golden("worked_example.json")
+    ex = g["expected"]
+    bs, D, NB = g["block_size"], g["head_dim"], g["pool_blocks"]
+    pool = BlockPool(free=list(g["free_blocks"]))
+    table = allocate_sequence(pool, g["num_keys"], bs)
+    assert len(table) == ex["blocks_needed"], table
+    assert list(table) == ex["block_table"], table
+    rng = np.random.default_rng(seed)
+    keys = rng.standard_normal((g["num_keys"], 1, D)).astype(np.float32)
+    key_pool = np.zeros((NB, bs, 1, D), dtype=np.float32)
+    tables = np.array([table], dtype=np.int32)
+    for pos in range(g["num_keys"]):
+        slot = slot_mapping(tables, np.array([pos]), bs)
+        key_pool = write_cache(key_pool, keys[pos:pos + 1], slot, bs)
+    back = gather(key_pool, tables[0], g["num_keys"], bs)
+    intact = back.shape == keys.shape and np.array_equal(back.view(np.uint32), keys.view(np.uint32))
+    assert intact == ex["keys_intact"]
+    # nothing outside the three blocks was touched
+    others = np.setdiff1d(np.arange(NB), table)
+    assert not key_pool[others].any()
+    assert paged_unused_slots(g["num_keys"], bs) == ex["unused_slots_paged"]
+    assert reserved_unused_slots(g["num_keys"], g["reservation"]) == ex["unused_slots_reserved"]
+
+
+# --------------------------------------------------------------------------
+# attention: library special case, brute force and closed forms
+# --------------------------------------------------------------------------
+
+def random_paged(rng, B, Hq, Hkv, D, bs, lens, NB=None, poison=True):
+    """Random pools + scattered tables for oracle checks (float64 values)."""
+    need = sum(-(-int(L) // bs) for L in lens)
+    NB = NB or need + 3
+    perm = rng.permutation(NB)
+    tables = np.full((B, max(1, max(-(-int(L) // bs) for L in lens)) + 1), -1, dtype=np.int64)
+    k = 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // bs)
+        tables[b, :n] = perm[k:k + n]
+        k += n
+    kp = rng.standard_normal((NB, bs, Hkv, D))
+    vp = rng.standard_normal((NB, bs, Hkv, D))
+    if poison:
+        used = np.zeros(NB, bool)
+        for b, L in enumerate(lens):
+            n = -(-int(L) // bs)
+            used[tables[b, :n]] = True
+            if L % bs:
+                kp[tables[b, n - 1], L % bs:] = np.nan
+                vp[tables[b, n - 1], L % bs:] = np.nan
+        kp[~used] = np.nan
+        vp[~used] = np.nan
+    q = rng.standard_normal((B, Hq, D))
+    return q, kp, vp, tables, np.asarray(lens, dtype=np.int64)
+
+
+def contiguous(pool, tables, lens, bs):
+    """Per-sequence contiguous [L, Hkv, D] by explicit slot indexing (not the oracle's gather)."""
+    out = []
+    for b, L in enumerate(lens):
+        rows = [pool[tables[b, t // bs], t % bs] for t in range(int(L))]
+        out.append(np.stack(rows) if rows else np.zeros((0,) + pool.shape[2:]))
+    return out
+
+
+def check_decode_vs_sdpa(decode, seed=1, B=3, Hq=8, Hkv=2, D=16, bs=4, lens=(1, 7, 13)):
+    """fp64 torch scaled_dot_product_attention on contiguous K/V, with KV heads
+    repeated for consecutive query heads (h -> h // G)."""
+    rng = np.random.default_rng(seed)
+    q, kp, vp, tables, lens = random_paged(rng, B, Hq, Hkv, D, bs, lens)
+    scale = 0.37
+    out = decode(q, kp, vp, tables, lens, bs, scale)
+    G = Hq // Hkv
+    ks, vs = contiguous(kp, tables, lens, bs), contiguous(vp, tables, lens, bs)
+    for b in range(B):
+        K = torch.from_numpy(ks[b]).permute(1, 0, 2).repeat_interleave(G, dim=0)   # [Hq, L, D]
+        V = torch.from_numpy(vs[b]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        Q = torch.from_numpy(q[b]).unsqueeze(1)                                      # [Hq, 1, D]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)[:, 0, :].numpy()
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
+
+
+def check_decode_vs_bruteforce(decode, seed=2, B=2, Hq=4, Hkv=2, D=5, bs=3, lens=(5, 8)):
+    """Pure-Python loops with math.exp over explicit slot indices."""
+    rng = np.random.default_rng(seed)
+    q, kp, vp, tables, lens = random_paged(rng, B, Hq, Hkv, D, bs, lens)
+    scale = 0.61
+    out = decode(q, kp, vp, tables, lens, bs, scale)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            scores = []
+            for t in range(int(lens[b])):
+                blk, off = int(tables[b, t // bs]), t % bs
+                scores.append(scale * sum(float(q[b, h, d]) * float(kp[blk, off, g, d]) for d in range(D)))
+            mx = max(scores)
+            w = [math.exp(s - mx) for s in scores]
+            tot = sum(w)
+            for d in range(D):
+                acc = 0.0
+                for t in range(int(lens[b])):
+                    blk, off = int(tables[b, t // bs]), t % bs
+                    acc += w[t] * float(vp[blk, off, g, d])
+                assert abs(out[b, h, d] - acc / tot) <= 1e-12 * max(1.0, abs(acc / tot)), (b, h, d)
+
+
+def check_closed_forms(decode, seed=3):
+    rng = np.random.default_rng(seed)
+    bs, D = 4, 8
+    # L = 1: a single weight of exactly 1, so out equals v_0 bit for bit
+    q, kp, vp, tables, lens = random_paged(rng, 2, 4, 4, D, bs, (1, 1))
+    out = decode(q, kp, vp, tables, lens, bs, 0.5)
+    for b in range(2):
+        assert np.array_equal(out[b], vp[tables[b, 0], 0]), "L=1 must return v_0 exactly"
+    # q = 0: uniform weights, out = mean of the L value rows
+    q, kp, vp, tables, lens = random_paged(rng, 1, 2, 2, D, bs, (11,))
+    q[:] = 0.0
+    out = decode(q, kp, vp, tables, lens, bs, 0.5)
+    rows = np.stack([vp[tables[0, t // bs], t % bs] for t in range(11)])
+    np.testing.assert_allclose(out[0], rows.mean(axis=0), rtol=0, atol=1e-14)
+    # planted dominant key: out -> that key's value row
+    q, kp, vp, tables, lens = random_paged(rng, 1, 1, 1, D, bs, (9,))
+    t0 = 6
+    kp[tables[0, t0 // bs], t0 % bs, 0] = 60.0 * q[0, 0] / np.linalg.norm(q[0, 0])
+    out = decode(q, kp, vp, tables, lens, bs, 1.0)
+    np.testing.assert_allclose(out[0, 0], vp[tables[0, t0 // bs], t0 % bs, 0], rtol=0, atol=1e-12)
+    # L = 0: zeros
+    q, kp, vp, tables, lens = random_paged(rng, 2, 2, 2, D, bs, (0, 3))
+    out = decode(q, kp, vp, tables, lens, bs, 0.5)
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+
+
+def check_placement_invariance(decode, seed=4):
+    """Any permutation of physical blocks, applied to pool and tables, leaves
+    the output bit-identical (P1: blocks may sit anywhere in memory)."""
+    rng = np.random.default_rng(seed)
+    bs = 4
+    q, kp, vp, tables, lens = random_paged(rng, 3, 4, 2, 8, bs, (9, 16, 3))
+    out = decode(q, kp, vp, tables, lens, bs, 0.3)
+    NB = kp.shape[0]
+    pi = rng.permutation(NB)
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[pi], vp2[pi] = kp, vp
+    t2 = np.where(tables >= 0, pi[np.maximum(tables, 0)], -1)
+    out2 = decode(q, kp2, vp2, t2, lens, bs, 0.3)
+    assert np.array_equal(out.view(np.uint64), out2.view(np.uint64))
+
+
+def check_sharing_invariance(decode, seed=5):
+    """Sequences pointing at shared prefix blocks give bit-identical results to
+    the same sequences with private copies (P1 "Diziler Arasında Blokları
+    Paylaşma")."""
+    rng = np.random.default_rng(seed)
+    bs, Hkv, D = 4, 2, 8
+    prefix_blocks, NB = 3, 40
+    kp = rng.standard_normal((NB, bs, Hkv, D))
+    vp = rng.standard_normal((NB, bs, Hkv, D))
+    shared = [0, 1, 2]
+    tails = [[3, 4], [5], [6, 7]]
+    lens = np.array([prefix_blocks * bs + 5, prefix_blocks * bs + 2, prefix_blocks * bs + 8])
+    tables = np.full((3, 6), -1)
+    for b in range(3):
+        row = shared + tails[b]
+        tables[b, :len(row)] = row
+    q = rng.standard_normal((3, 4, D))
+    out = decode(q, kp, vp, tables, lens, bs, 0.4)
+    # twin: private copies of the prefix for each sequence
+    kp2, vp2 = kp.copy(), vp.copy()
+    t2 = tables.copy()
+    nxt = 10
+    for b in range(3):
+        for j in range(prefix_blocks):
+            kp2[nxt], vp2[nxt] = kp[shared[j]], vp[shared[j]]
+            t2[b, j] = nxt
+            nxt += 1
+    out2 = decode(q, kp2, vp2, t2, lens, bs, 0.4)
+    assert np.array_equal(out.view(np.uint64), out2.view(np.uint64))
+
+
+# --------------------------------------------------------------------------
+# e4m3 codec
+# --------------------------------------------------------------------------
+
+def torch_e4m3_values() -> np.ndarray:
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def check_e4m3_decode(decode_table):
+    ref = torch_e4m3_values()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(decode_table), nan)
+    assert np.array_equal(decode_table[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(decode_table[~nan]), np.signbit(ref[~nan]))
+
+
+def check_e4m3_encode(encode, decode_table):
+    codes = np.arange(256)
+    ok = ~np.isnan(decode_table)
+    assert np.array_equal(encode(decode_table[ok]), codes[ok].astype(np.uint8))
+    # every midpoint between neighbouring positive codes goes to the even code
+    vals = decode_table[:0x7F]                       # 0x00 .. 0x7E, increasing
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    got = encode(mids)
+    even = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F))
+    assert np.array_equal(got, even.astype(np.uint8)), "ties must round to even"
+    assert np.array_equal(encode(-mids), (even | 0x80).astype(np.uint8))
+    # just off the midpoints: nearest
+    assert np.array_equal(encode(np.nextafter(mids, 0)), np.arange(0x7E).astype(np.uint8))
+    assert np.array_equal(encode(np.nextafter(mids, np.inf)), np.arange(1, 0x7F).astype(np.uint8))
+    # saturation, infinities, NaN, signed zero
+    sat = encode(np.array([448.0, 463.99, 464.0, 464.01, 479.0, 480.0, 1e30, np.inf,
+                           -1e30, -np.inf]))
+    assert list(sat) == [0x7E] * 8 + [0xFE] * 2, [hex(x) for x in sat]
+    assert encode(np.array([np.nan]))[0] == 0x7F
+    assert encode(np.array([-np.nan]))[0] == 0xFF
+    assert encode(np.array([-0.0]))[0] == 0x80 and encode(np.array([0.0]))[0] == 0x00
+    # agreement with torch's cast where torch is defined to saturate-free RNE
+    rng = np.random.default_rng(6)
+    y = np.concatenate([rng.standard_normal(20000) * 50, rng.uniform(-464, 464, 20000),
+                        rng.standard_normal(5000) * 0.01, mids, -mids]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(encode(y.astype(np.float64)), ref)
+
+
+def check_e4m3_quantize(quantize):
+    """encode(fl32(x * fl32(1/scale))): compare with torch doing the same fp32
+    multiply and its own e4m3 cast, inside torch's non-saturating range."""
+    rng = np.random.default_rng(7)
+    for scale in (0.0117, 0.5, 3.0, 1.0 / 448.0):
+        x = rng.standard_normal(4096).astype(np.float32) * np.float32(scale * 300.0)
+        inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32)
+        y = torch.from_numpy(x) * inv
+        keep = y.abs() <= 464
+        ref = y[keep].to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = quantize(x[keep.numpy()], scale)
+        assert np.array_equal(got, ref)
