@@ -1,0 +1,197 @@
+"""Benchmark of the paged decode path on one MI355X.
+
+One step = the whole hot path over one batch: slot mapping, copy-on-write
+block copies (when the workload shares blocks), the cache write of one new
+token per sequence, the split-K decode partitions and their reduce.  Inputs
+are seeded synthetic data already resident in HBM; the timed region holds
+exactly ``--steps`` steps between a synchronise and two HIP events.
+
+Printed: one JSON line with the metric (effective KV GB/s: bytes of the valid
+tokens' K and V, sum_b L_b * 2 * Hkv * D * elem, per step time), the roofline
+of the dominant kernel (the decode partition kernel, timed with HIP events on
+the stream it runs on) and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "paged decode attention: effective KV GB/s and % of HBM peak; seqs/s per layer"
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["paged_kv_cache_412_amd/csrc/pa_decode.hip", "paged_kv_cache_412_amd/csrc/pa_device.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kv_bytes(wl) -> int:
+    from paged_kv_cache_412_amd.workloads import ELEM_BYTES
+    c = wl.cfg
+    return int(np.sum(wl.seq_lens)) * 2 * c.Hkv * c.D * ELEM_BYTES[c.kv_dtype]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed PMC counter runs, if they were taken
+    on the current kernel source."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_decode_partition_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, step, budget_s: float):
+    """The oracle as it stands, on host copies of the pools, over as many
+    sequences as fit in ``budget_s`` seconds (at least one)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+    from tests import parity
+
+    cfg = wl.cfg
+    k = parity.storage(wl.k_pool)
+    v = parity.storage(wl.v_pool)
+    q = parity.widen(parity.storage(wl.q), cfg.q_dtype)
+    tab = step.tables_np
+    order = np.random.default_rng(0).permutation(cfg.B)
+    done, nbytes = [], 0
+    from paged_kv_cache_412_amd.workloads import ELEM_BYTES
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for b in order:
+            paged.decode(q, k, v, tab, wl.seq_lens, cfg.block_size, wl.scale, seqs=[int(b)],
+                         widen_k=lambda x: parity.widen(x, cfg.kv_dtype, wl.k_scale),
+                         widen_v=lambda x: parity.widen(x, cfg.kv_dtype, wl.v_scale))
+            done.append(int(b))
+            nbytes += int(wl.seq_lens[b]) * 2 * cfg.Hkv * cfg.D * ELEM_BYTES[cfg.kv_dtype]
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {cfg.B} sequences (all {cfg.Hq} heads), {dt:.1f} s, "
+                      f"fp64 NumPy, BLAS limited to 1 thread",
+            "seconds": round(dt, 3), "seq_layers_per_s": round(len(done) / dt, 3)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama13b")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode path is measured on one GPU's share of "
+              f"the batch; --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_412_amd import binding, workloads
+    from paged_kv_cache_412_amd.step import DecodeStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    binding.lib()
+    cfg = workloads.CONFIGS[args.workload]
+    print(f"[bench] building workload {cfg.name}", file=sys.stderr, flush=True)
+    wl = workloads.make(cfg, device="cuda")
+    step = DecodeStep(wl, partition_size=args.partition_size)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    # timed region: exactly --steps whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # per-stage durations, events on the same stream around each C-ABI call
+    stages = ["slot_mapping", "copy_blocks", "cache_write", "decode_partition", "decode_reduce"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, s in enumerate(stages):
+            getattr(step, s)()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, s in enumerate(stages)}
+
+    nbytes = kv_bytes(wl)
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    part_ms = stage_ms["decode_partition"]
+    achieved = nbytes / (part_ms * 1e-3) / 1e9
+    traffic = measured_traffic(cfg.name)
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.kv_dtype,
+        "accum_dtype": "f32",
+        "data": "synthetic (seeded N(0,1) queries and caches, scattered block tables)",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
+                   "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype,
+                   "seq_lens": (f"U[{cfg.len_range[0]},{cfg.len_range[1]}]" if cfg.len_range
+                                else "fixed"),
+                   "total_tokens": int(np.sum(wl.seq_lens)), "pool_blocks": wl.num_blocks,
+                   "partition_size": args.partition_size or 512, "cow_copies": len(step.copies)},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "seq_layers_per_s": round(cfg.B / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": nbytes,
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "roofline": {"kernel": "decode_partition_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": nbytes, "avg_launch_ms": round(part_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, step, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

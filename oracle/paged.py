@@ -125,7 +125,8 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndar
 
 
 def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables: np.ndarray,
-           seq_lens: np.ndarray, block_size: int, scale: float, seqs=None) -> np.ndarray:
+           seq_lens: np.ndarray, block_size: int, scale: float, seqs=None,
+           widen_k=None, widen_v=None) -> np.ndarray:
     """Paged decode attention for a batch, float64.
 
     ``q [B, Hq, D]``; pools ``[NB, bs, Hkv, D]`` float64 (already dequantised);
@@ -137,7 +138,10 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables: 
     consecutive query heads share one: head h uses KV head h // G.
 
     ``seqs`` restricts the work to some sequence indices; the other rows of
-    the result are NaN.
+    the result are NaN.  ``widen_k`` / ``widen_v`` map a gathered block of
+    raw storage to float64 values (e.g. bf16 bits, or e4m3 codes times the
+    pool's scale), so pools can be passed in their storage form and only
+    the gathered tokens are widened.
     """
     B, Hq, D = q.shape
     Hkv = k_pool.shape[2]
@@ -149,6 +153,8 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables: 
         L = int(seq_lens[b])
         kb = gather(k_pool, block_tables[b], L, block_size)   # [L, Hkv, D]
         vb = gather(v_pool, block_tables[b], L, block_size)
+        kb = np.asarray(kb, dtype=np.float64) if widen_k is None else widen_k(kb)
+        vb = np.asarray(vb, dtype=np.float64) if widen_v is None else widen_v(vb)
         for g in range(Hkv):
             out[b, g * G:(g + 1) * G] = attend(q[b, g * G:(g + 1) * G], kb[:, g, :], vb[:, g, :], scale)
     return out

@@ -1,0 +1,242 @@
+"""ctypes binding of libpa (``include/pa.h``): argument marshalling only.
+
+Every function here takes torch tensors that already live on the GPU, checks
+shapes on the host, passes raw device pointers and the current HIP stream to
+the C ABI and raises :class:`PaError` on a non-OK status.  No arithmetic of
+the path happens here; there is no CPU fallback.  If ``libpa.so`` is missing
+the first call raises :class:`LibraryNotBuilt`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpa.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "pa.h")
+
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
+          4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH"}
+DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "e4m3": PA_FP8_E4M3}
+TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+               torch.uint8: PA_FP8_E4M3, torch.float8_e4m3fn: PA_FP8_E4M3}
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, what: str, message: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({message})")
+        self.status = status
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``pa_decode_args``."""
+
+    _fields_ = [
+        ("out", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p), ("block_tables", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("scale", ctypes.c_float), ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float), ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
+        ("out_dtype", ctypes.c_int), ("partition_size", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def declared_functions() -> list:
+    """Names of the functions ``include/pa.h`` declares."""
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so (once)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryNotBuilt(f"{LIB_PATH} is missing: run `python -m paged_kv_cache_412_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    argp = ctypes.POINTER(DecodeArgs)
+    L.pa_decode_workspace_size.argtypes = [argp]
+    L.pa_decode_workspace_size.restype = ctypes.c_size_t
+    for name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce"):
+        getattr(L, name).argtypes = [argp, vp]
+        getattr(L, name).restype = ctypes.c_int
+    L.pa_decode_check.argtypes = [argp]
+    L.pa_decode_check.restype = ctypes.c_int
+    L.pa_slot_mapping.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    L.pa_slot_mapping.restype = ctypes.c_int
+    L.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                       ctypes.c_int, f32, f32, vp]
+    L.pa_reshape_and_cache.restype = ctypes.c_int
+    L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_status_str.argtypes = [ctypes.c_int]
+    L.pa_status_str.restype = ctypes.c_char_p
+    L.pa_abi_version.argtypes = []
+    L.pa_abi_version.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise PaError(status, what, lib().pa_status_str(status).decode())
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _pa_dtype(t: torch.Tensor, override=None) -> int:
+    if override is not None:
+        return DTYPE_NAMES[override] if isinstance(override, str) else int(override)
+    return TORCH_TO_PA[t.dtype]
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0, v_scale=1.0,
+                partition_size=0, workspace=None, kv_dtype=None) -> DecodeArgs:
+    """Build ``pa_decode_args`` from tensors (shapes per include/pa.h)."""
+    for t, n, nd in ((out, "out", 3), (q, "q", 3), (k_cache, "k_cache", 4), (v_cache, "v_cache", 4)):
+        _require(t, n, ndim=nd)
+    _require(block_tables, "block_tables", torch.int32, 2)
+    _require(seq_lens, "seq_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    NB, bs, Hkv, Dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or Dk != D or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("inconsistent shapes")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables / seq_lens batch mismatch")
+    a = DecodeArgs()
+    a.out, a.q, a.k_cache, a.v_cache = _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    a.block_tables, a.seq_lens = _ptr(block_tables), _ptr(seq_lens)
+    a.B, a.Hq, a.Hkv, a.D = B, Hq, Hkv, D
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = bs, NB, block_tables.shape[1]
+    a.scale, a.k_scale, a.v_scale = float(scale), float(k_scale), float(v_scale)
+    a.q_dtype = _pa_dtype(q)
+    a.kv_dtype = _pa_dtype(k_cache, kv_dtype)
+    a.out_dtype = _pa_dtype(out)
+    a.partition_size = int(partition_size)
+    if workspace is not None:
+        _require(workspace, "workspace")
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return a
+
+
+def workspace_size(args: DecodeArgs) -> int:
+    return int(lib().pa_decode_workspace_size(ctypes.byref(args)))
+
+
+def alloc_workspace(args: DecodeArgs, device=None) -> torch.Tensor | None:
+    """A workspace tensor of the size ``pa_decode_workspace_size`` asks for (or None)."""
+    n = workspace_size(args)
+    if n == 0:
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), n
+    return ws
+
+
+def decode_check(args: DecodeArgs) -> int:
+    return int(lib().pa_decode_check(ctypes.byref(args)))
+
+
+def decode_run(args: DecodeArgs, stream=None) -> None:
+    _check(lib().pa_decode(ctypes.byref(args), _stream(stream)), "pa_decode")
+
+
+def decode_partition_run(args: DecodeArgs, stream=None) -> None:
+    _check(lib().pa_decode_partition(ctypes.byref(args), _stream(stream)), "pa_decode_partition")
+
+
+def decode_reduce_run(args: DecodeArgs, stream=None) -> None:
+    _check(lib().pa_decode_reduce(ctypes.byref(args), _stream(stream)), "pa_decode_reduce")
+
+
+def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0, v_scale=1.0,
+           partition_size=0, workspace=None, kv_dtype=None, stream=None):
+    """pa_decode on tensors; allocates the workspace with torch when none is given."""
+    a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale,
+                    partition_size, workspace, kv_dtype)
+    keep = None
+    if workspace is None:
+        keep = alloc_workspace(a, q.device)
+    decode_run(a, stream)
+    return out, keep
+
+
+def slot_mapping(block_tables, positions, block_size, slots, stream=None):
+    _require(block_tables, "block_tables", torch.int32, 2)
+    _require(positions, "positions", torch.int32, 1)
+    _require(slots, "slots", torch.int32, 1)
+    B = positions.shape[0]
+    if block_tables.shape[0] != B or slots.shape[0] != B:
+        raise ValueError("batch mismatch")
+    _check(lib().pa_slot_mapping(_ptr(block_tables), _ptr(positions), B, block_tables.shape[1],
+                                 int(block_size), _ptr(slots), _stream(stream)), "pa_slot_mapping")
+    return slots
+
+
+def reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, k_scale=1.0, v_scale=1.0,
+                      kv_dtype=None, stream=None):
+    _require(k_new, "k_new", ndim=3)
+    _require(v_new, "v_new", ndim=3)
+    _require(k_cache, "k_cache", ndim=4)
+    _require(v_cache, "v_cache", ndim=4)
+    _require(slots, "slots", torch.int32, 1)
+    T, Hkv, D = k_new.shape
+    NB, bs, Hkv2, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or tuple(v_new.shape) != tuple(k_new.shape) or slots.shape[0] != T:
+        raise ValueError("inconsistent shapes")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_new.dtype != k_new.dtype:
+        raise ValueError("K and V must match")
+    _check(lib().pa_reshape_and_cache(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(slots), T, Hkv, D, bs, NB, _pa_dtype(k_new),
+                                      _pa_dtype(k_cache, kv_dtype), float(k_scale), float(v_scale),
+                                      _stream(stream)), "pa_reshape_and_cache")
+
+
+def copy_blocks(k_cache, v_cache, block_mapping, kv_dtype=None, stream=None):
+    _require(k_cache, "k_cache", ndim=4)
+    _require(v_cache, "v_cache", ndim=4)
+    _require(block_mapping, "block_mapping", torch.int32, 2)
+    if block_mapping.shape[1] != 2 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("block_mapping must be [P, 2] and K/V pools must match")
+    NB, bs, Hkv, D = k_cache.shape
+    _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
+                                block_mapping.shape[0], NB, bs, Hkv, D, _pa_dtype(k_cache, kv_dtype),
+                                _stream(stream)), "pa_copy_blocks")

@@ -1,0 +1,202 @@
+// pa_cache.hip -- cache-side kernels for gfx950: slot mapping, the cache
+// write (reshape_and_cache) and the copy-on-write block copy.
+//
+// P1 = Ultralytics glossary page "PagedAttention".
+//   * Slot of a token: block table entry pos / bs, offset pos % bs (P1
+//     "Sayfalama Nasıl Çalışır", code sketch write loop).
+//   * Cache write: the new token's K and V rows go to that slot; an fp8 cache
+//     quantises them with the pool's scale (P1 "İlgili Teknikler").
+//   * Block copy: a block that other sequences still use is copied before a
+//     sequence writes into it (P1 "Diziler Arasında Blokları Paylaşma").
+// All three are pure data movement; every byte is moved with 16-byte vector
+// loads and stores.
+
+#include <hip/hip_runtime.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ slot mapping
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* __restrict__ tables,
+                                                           const int32_t* __restrict__ positions,
+                                                           int32_t B, int32_t max_blocks,
+                                                           int32_t bs, int32_t* __restrict__ slots) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int pos = positions[b];
+  int slot = -1;
+  if (pos >= 0 && pos / bs < max_blocks) {
+    const int blk = tables[static_cast<size_t>(b) * max_blocks + pos / bs];
+    const int64_t s = static_cast<int64_t>(blk) * bs + pos % bs;
+    if (blk >= 0 && s <= INT32_MAX) slot = static_cast<int>(s);
+  }
+  slots[b] = slot;
+}
+
+// ------------------------------------------------------------------ cache write
+
+// Same dtype on both sides: a bit copy of each token's [Hkv][D] row, K and V.
+// grid (T, 2): y selects K or V; 16-byte chunks strided over the work-group.
+__global__ __launch_bounds__(256) void cache_copy_kernel(const u32x4* __restrict__ k_new,
+                                                         const u32x4* __restrict__ v_new,
+                                                         u32x4* __restrict__ k_cache,
+                                                         u32x4* __restrict__ v_cache,
+                                                         const int32_t* __restrict__ slots,
+                                                         int32_t row_chunks, int64_t num_slots) {
+  const int t = blockIdx.x;
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const u32x4* src = (blockIdx.y == 0 ? k_new : v_new) + static_cast<size_t>(t) * row_chunks;
+  u32x4* dst = (blockIdx.y == 0 ? k_cache : v_cache) + static_cast<size_t>(slot) * row_chunks;
+  for (int i = threadIdx.x; i < row_chunks; i += blockDim.x) dst[i] = src[i];
+}
+
+// Quantise 8 source elements to 8 e4m3 codes: code = e4m3(fl32(x * inv_scale)).
+template <int SRC>
+__device__ __forceinline__ u32x2 quantize8(const void* src8, float inv) {
+  float x[8];
+  if constexpr (SRC == PA_F32) {
+    const u32x4* p = static_cast<const u32x4*>(src8);
+    const u32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = u2f(a[i]);
+      x[4 + i] = u2f(b[i]);
+    }
+  } else {
+    const u32x4 a = *static_cast<const u32x4*>(src8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (SRC == PA_BF16) {
+        x[2 * i] = u2f(a[i] << 16);
+        x[2 * i + 1] = u2f(a[i] & 0xffff0000u);
+      } else {
+        f16x2 h = __builtin_bit_cast(f16x2, a[i]);
+        x[2 * i] = static_cast<float>(h[0]);
+        x[2 * i + 1] = static_cast<float>(h[1]);
+      }
+    }
+  }
+  u32x2 out;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // one correctly rounded fp32 multiply, then the e4m3 rounding
+      word |= f32_to_e4m3_rne_sat(x[4 * w + i] * inv) << (8 * i);
+    }
+    out[w] = word;
+  }
+  return out;
+}
+
+// grid (T, 2); each thread quantises groups of 8 elements of one row.
+template <int SRC>
+__global__ __launch_bounds__(256) void cache_quant_kernel(const char* __restrict__ k_new,
+                                                          const char* __restrict__ v_new,
+                                                          u32x2* __restrict__ k_cache,
+                                                          u32x2* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ slots,
+                                                          int32_t row_elems, int64_t num_slots,
+                                                          float k_inv, float v_inv) {
+  constexpr int SB = Elem<SRC>::bytes;
+  const int t = blockIdx.x;
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const bool is_k = blockIdx.y == 0;
+  const char* src = (is_k ? k_new : v_new) + static_cast<size_t>(t) * row_elems * SB;
+  u32x2* dst = (is_k ? k_cache : v_cache) + static_cast<size_t>(slot) * (row_elems / 8);
+  const float inv = is_k ? k_inv : v_inv;
+  for (int i = threadIdx.x; i < row_elems / 8; i += blockDim.x)
+    dst[i] = quantize8<SRC>(src + static_cast<size_t>(i) * 8 * SB, inv);
+}
+
+// ------------------------------------------------------------------ block copy
+
+// Flat grid of P * 2 * slices work-groups: (pair, K or V, slice), where a
+// slice is kSliceChunks 16-byte chunks of one block.
+constexpr int kSliceChunks = kCopySliceChunks;
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_cache,
+                                                          u32x4* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ mapping,
+                                                          int32_t num_blocks, int64_t block_chunks,
+                                                          int32_t slices) {
+  const int slice = blockIdx.x % slices;
+  const int kv = (blockIdx.x / slices) & 1;
+  const int pair = blockIdx.x / (2 * slices);
+  const int src = mapping[2 * pair];
+  const int dst = mapping[2 * pair + 1];
+  if (static_cast<unsigned>(src) >= static_cast<unsigned>(num_blocks) ||
+      static_cast<unsigned>(dst) >= static_cast<unsigned>(num_blocks))
+    return;
+  u32x4* pool = kv == 0 ? k_cache : v_cache;
+  const u32x4* s = pool + static_cast<size_t>(src) * block_chunks;
+  u32x4* d = pool + static_cast<size_t>(dst) * block_chunks;
+  const int64_t beg = static_cast<int64_t>(slice) * kSliceChunks;
+  const int64_t end = beg + kSliceChunks < block_chunks ? beg + kSliceChunks : block_chunks;
+  for (int64_t i = beg + threadIdx.x; i < end; i += blockDim.x) d[i] = s[i];
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* positions, int32_t B,
+                               int32_t max_blocks, int32_t block_size, int32_t* slots,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, block_tables,
+                     positions, B, max_blocks, block_size, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache,
+                                    void* v_cache, const int32_t* slots, int32_t T, int32_t Hkv,
+                                    int32_t D, int32_t block_size, int32_t num_blocks,
+                                    pa_dtype src_dtype, pa_dtype kv_dtype, float k_inv_scale,
+                                    float v_inv_scale, hipStream_t stream) {
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  const int32_t row_elems = Hkv * D;
+  dim3 grid(T, 2);
+  if (src_dtype == kv_dtype) {
+    int ebytes = kv_dtype == PA_F32 ? 4 : (kv_dtype == PA_FP8_E4M3 ? 1 : 2);
+    const int32_t row_chunks = row_elems * ebytes / 16;
+    hipLaunchKernelGGL(cache_copy_kernel, grid, dim3(256), 0, stream,
+                       static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new),
+                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slots, row_chunks,
+                       num_slots);
+  } else if (src_dtype == PA_F32) {
+    hipLaunchKernelGGL(cache_quant_kernel<PA_F32>, grid, dim3(256), 0, stream,
+                       static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+                       static_cast<u32x2*>(k_cache), static_cast<u32x2*>(v_cache), slots, row_elems,
+                       num_slots, k_inv_scale, v_inv_scale);
+  } else if (src_dtype == PA_F16) {
+    hipLaunchKernelGGL(cache_quant_kernel<PA_F16>, grid, dim3(256), 0, stream,
+                       static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+                       static_cast<u32x2*>(k_cache), static_cast<u32x2*>(v_cache), slots, row_elems,
+                       num_slots, k_inv_scale, v_inv_scale);
+  } else {
+    hipLaunchKernelGGL(cache_quant_kernel<PA_BF16>, grid, dim3(256), 0, stream,
+                       static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+                       static_cast<u32x2*>(k_cache), static_cast<u32x2*>(v_cache), slots, row_elems,
+                       num_slots, k_inv_scale, v_inv_scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int32_t P,
+                              int32_t num_blocks, size_t block_bytes, hipStream_t stream) {
+  const int64_t block_chunks = static_cast<int64_t>(block_bytes / 16);
+  const int32_t slices = static_cast<int32_t>((block_chunks + kSliceChunks - 1) / kSliceChunks);
+  dim3 grid(static_cast<unsigned>(static_cast<int64_t>(P) * 2 * slices));
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, static_cast<u32x4*>(k_cache),
+                     static_cast<u32x4*>(v_cache), mapping, num_blocks, block_chunks, slices);
+  return hipGetLastError();
+}
+
+}  // namespace pa

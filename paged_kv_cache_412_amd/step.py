@@ -1,0 +1,78 @@
+"""One decode step of the paged KV cache on the GPU, through the C ABI.
+
+A step, for a batch whose caches hold L-1 tokens each:
+
+1. the host block manager gives every sequence room for its new token (a new
+   block when the last one is full, a copy-on-write when the last block is
+   shared) -- done once, when the step is prepared;
+2. ``pa_slot_mapping``     slot of each new token from the block tables;
+3. ``pa_copy_blocks``      copy-on-write block copies (when there are any);
+4. ``pa_reshape_and_cache`` write the new K/V rows to their slots;
+5. ``pa_decode_partition`` split-K partitions of paged attention;
+6. ``pa_decode_reduce``    combine the partitions (long sequences only).
+
+Steps 2-6 run on the GPU and are what :meth:`DecodeStep.run` enqueues; they
+are idempotent, so the same prepared step can be replayed for timing.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding
+from .blocks import BlockManager
+from .workloads import TORCH_DTYPE, Workload, pad_tables
+
+
+class DecodeStep:
+    def __init__(self, wl: Workload, partition_size: int = 0, out_dtype=None, device="cuda"):
+        cfg = wl.cfg
+        self.wl = wl
+        bs = cfg.block_size
+        mgr = BlockManager(wl.num_blocks, bs, free=wl.free, refs=wl.refs)
+        self.tables_list, self.copies = mgr.plan_step(wl.tables, wl.seq_lens - 1)
+        width = max(1, max(len(r) for r in self.tables_list))
+        self.tables_np = pad_tables(self.tables_list, width)
+        dev = torch.device(device)
+        self.block_tables = torch.from_numpy(self.tables_np).to(dev)
+        self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev)
+        pos = np.where(wl.seq_lens > 0, wl.seq_lens - 1, -1).astype(np.int32)
+        self.positions = torch.from_numpy(pos).to(dev)
+        self.slots = torch.empty(cfg.B, dtype=torch.int32, device=dev)
+        self.mapping = (torch.tensor(self.copies, dtype=torch.int32, device=dev).reshape(-1, 2)
+                        if self.copies else torch.empty((0, 2), dtype=torch.int32, device=dev))
+        odt = out_dtype or cfg.out_dtype
+        self.out = torch.empty((cfg.B, cfg.Hq, cfg.D), dtype=TORCH_DTYPE[odt], device=dev)
+        self.kv_dtype = cfg.kv_dtype
+        self.args = binding.decode_args(self.out, wl.q, wl.k_pool, wl.v_pool, self.block_tables,
+                                        self.seq_lens, wl.scale, wl.k_scale, wl.v_scale,
+                                        partition_size, None, cfg.kv_dtype)
+        self.workspace = binding.alloc_workspace(self.args, dev)
+
+    # individual stages (each one C-ABI call)
+    def slot_mapping(self, stream=None):
+        binding.slot_mapping(self.block_tables, self.positions, self.wl.cfg.block_size, self.slots, stream)
+
+    def copy_blocks(self, stream=None):
+        if self.mapping.shape[0]:
+            binding.copy_blocks(self.wl.k_pool, self.wl.v_pool, self.mapping, self.kv_dtype, stream)
+
+    def cache_write(self, stream=None):
+        wl = self.wl
+        binding.reshape_and_cache(wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, self.slots, wl.k_scale,
+                                  wl.v_scale, self.kv_dtype, stream)
+
+    def decode_partition(self, stream=None):
+        binding.decode_partition_run(self.args, stream)
+
+    def decode_reduce(self, stream=None):
+        binding.decode_reduce_run(self.args, stream)
+
+    def run(self, stream=None):
+        self.slot_mapping(stream)
+        self.copy_blocks(stream)
+        self.cache_write(stream)
+        self.decode_partition(stream)
+        self.decode_reduce(stream)
+        return self.out

@@ -1,0 +1,125 @@
+"""Oracle expectations for one decode step, and the comparisons the GPU
+parity tests make.
+
+Everything expected here comes from the oracle applied to the step's inputs
+(the pre-step state from the seeded generator); nothing the GPU produced is
+fed back into the oracle.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from oracle import blocks as oblocks
+from oracle import fp8, numerics, paged
+
+#: attention tolerance (max abs error vs the fp64 oracle) by KV dtype; the
+#: output rounding (half an ulp of the output dtype) is added on top.
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2, "e4m3": 3e-2}
+OUT_FORMAT = {"f32": (numerics.F32_P, numerics.F32_EMIN), "f16": (numerics.F16_P, numerics.F16_EMIN),
+              "bf16": (numerics.BF16_P, numerics.BF16_EMIN)}
+
+
+def storage(t: torch.Tensor) -> np.ndarray:
+    """Raw bits of a tensor as a NumPy array (uint32 / uint16 / uint8)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.uint8:
+        return t.numpy()
+    raise TypeError(t.dtype)
+
+
+def widen(raw: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    if dtype == "f32":
+        return numerics.f32_bits_to_f64(raw)
+    if dtype == "f16":
+        return numerics.f16_bits_to_f64(raw)
+    if dtype == "bf16":
+        return numerics.bf16_bits_to_f64(raw)
+    if dtype == "e4m3":
+        return fp8.decode(raw, scale)
+    raise ValueError(dtype)
+
+
+@dataclass
+class PreStep:
+    """Host copies of a workload's inputs, taken before the GPU step runs."""
+
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+    q: np.ndarray
+
+
+def snapshot(wl) -> PreStep:
+    return PreStep(storage(wl.k_pool), storage(wl.v_pool), storage(wl.k_new), storage(wl.v_new),
+                   storage(wl.q))
+
+
+@dataclass
+class Expected:
+    tables: list
+    copies: list
+    slots: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    out: np.ndarray       # float64, NaN rows for sequences not computed
+
+
+def oracle_step(wl, pre: PreStep, seqs=None) -> Expected:
+    cfg = wl.cfg
+    bs = cfg.block_size
+    pool = oblocks.BlockPool(free=list(wl.free), refs=dict(wl.refs))
+    tables = [list(r) for r in wl.tables]
+    copies = []
+    for i, L in enumerate(wl.seq_lens):
+        if L >= 1:
+            _, cow = oblocks.append_slot(pool, tables[i], int(L) - 1, bs)
+            if cow is not None:
+                copies.append(cow)
+    width = max(1, max(len(r) for r in tables))
+    tab = np.full((len(tables), width), -1, dtype=np.int64)
+    for i, r in enumerate(tables):
+        tab[i, :len(r)] = r
+    positions = np.where(wl.seq_lens > 0, wl.seq_lens - 1, -1)
+    slots = paged.slot_mapping(tab, positions, bs)
+
+    def enc(rows, scale):
+        if cfg.src_dtype == cfg.kv_dtype:
+            return rows
+        return fp8.quantize(widen(rows, cfg.src_dtype), scale)
+
+    k = paged.copy_blocks(pre.k_pool, np.array(copies).reshape(-1, 2))
+    v = paged.copy_blocks(pre.v_pool, np.array(copies).reshape(-1, 2))
+    k = paged.write_cache(k, enc(pre.k_new, wl.k_scale), slots, bs)
+    v = paged.write_cache(v, enc(pre.v_new, wl.v_scale), slots, bs)
+    q = widen(pre.q, cfg.q_dtype)
+    out = paged.decode(q, k, v, tab, wl.seq_lens, bs, wl.scale, seqs=seqs,
+                       widen_k=lambda x: widen(x, cfg.kv_dtype, wl.k_scale),
+                       widen_v=lambda x: widen(x, cfg.kv_dtype, wl.v_scale))
+    return Expected(tables, copies, slots, k, v, out)
+
+
+def gpu_out(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, out_dtype: str, what=""):
+    """|got - ref| <= TOL[kv] + half an ulp of the output dtype at ref."""
+    p, emin = OUT_FORMAT[out_dtype]
+    bound = TOL[kv_dtype] + numerics.half_ulp(ref, p, emin)
+    err = np.abs(got - ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; max err "
+                             f"{np.nanmax(err):.3e}; first {idx.tolist()} got "
+                             f"{got[tuple(idx[0])]} ref {ref[tuple(idx[0])]}")
+    return float(np.max(err)) if err.size else 0.0

@@ -1,0 +1,116 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and its host-side validation returns the documented status codes.  No kernel
+is launched here."""
+
+import ctypes
+import os
+
+import pytest
+
+from paged_kv_cache_412_amd import binding
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from paged_kv_cache_412_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_header_declares_the_path_entry_points():
+    names = set(binding.declared_functions())
+    for n in ("pa_decode", "pa_decode_partition", "pa_decode_reduce", "pa_decode_workspace_size",
+              "pa_decode_check", "pa_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
+              "pa_status_str", "pa_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in binding.declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.pa_abi_version() == 1
+    for s in range(6):
+        assert L.pa_status_str(s)
+    assert L.pa_status_str(99) == b"unknown status"
+
+
+FAKE = 0x100000  # a 16-byte aligned non-null address; never dereferenced by validation
+
+
+def valid_args(**kw):
+    a = binding.DecodeArgs()
+    a.out = a.q = a.k_cache = a.v_cache = a.block_tables = a.seq_lens = FAKE
+    a.B, a.Hq, a.Hkv, a.D = 4, 8, 8, 64
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = 16, 64, 4
+    a.scale, a.k_scale, a.v_scale = 0.125, 1.0, 1.0
+    a.q_dtype = a.kv_dtype = a.out_dtype = binding.PA_F32
+    a.partition_size = 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def check(L, **kw):
+    return L.pa_decode_check(ctypes.byref(valid_args(**kw)))
+
+
+def test_decode_check_accepts_valid(L):
+    assert check(L) == 0
+    assert check(L, B=0, out=0, q=0) == 0                           # empty batch
+    assert check(L, q_dtype=binding.PA_BF16, kv_dtype=binding.PA_FP8_E4M3,
+                 out_dtype=binding.PA_BF16, k_scale=0.01, v_scale=0.02) == 0
+    assert check(L, q_dtype=binding.PA_F16, kv_dtype=binding.PA_F16, out_dtype=binding.PA_F32) == 0
+    assert check(L, Hq=64, Hkv=8, D=128) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(seq_lens=0), 1), (dict(block_tables=0), 1),
+    (dict(Hq=6, Hkv=4), 2), (dict(B=-1), 2), (dict(num_blocks=0), 2),
+    (dict(max_blocks_per_seq=0), 2), (dict(partition_size=24), 2),
+    (dict(q=FAKE + 4), 2), (dict(k_scale=2.0), 2), (dict(scale=float("inf")), 2),
+    (dict(B=70000), 2),
+    (dict(D=96), 3), (dict(block_size=8), 3), (dict(Hq=24, Hkv=8), 3), (dict(Hq=32, Hkv=2), 3),
+    (dict(q_dtype=binding.PA_F16), 3), (dict(out_dtype=binding.PA_BF16), 3),
+    (dict(kv_dtype=binding.PA_FP8_E4M3, q_dtype=binding.PA_F32), 3), (dict(q_dtype=7), 3),
+    (dict(max_blocks_per_seq=64), 4),                 # 1024 tokens > one 512-token partition
+    (dict(kv_dtype=binding.PA_FP8_E4M3, q_dtype=binding.PA_BF16, out_dtype=binding.PA_BF16,
+          k_scale=0.0), 2),
+])
+def test_decode_check_rejects(L, kw, status):
+    assert check(L, **kw) == status
+
+
+def test_workspace_size_formula(L):
+    a = valid_args(max_blocks_per_seq=64)                    # 1024 tokens -> 2 partitions
+    assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 2 * (64 + 2)
+    a = valid_args(max_blocks_per_seq=64, partition_size=256)   # 4 partitions
+    assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 4 * (64 + 2)
+    assert L.pa_decode_workspace_size(ctypes.byref(valid_args())) == 0   # one partition
+    assert L.pa_decode_workspace_size(ctypes.byref(valid_args(Hq=6, Hkv=4))) == 0
+    assert L.pa_decode_workspace_size(None) == 0
+
+
+def test_decode_with_bad_args_enqueues_nothing(L):
+    # validation fails before any HIP call, so this is safe without a GPU
+    assert L.pa_decode(ctypes.byref(valid_args(D=96)), None) == 3
+    assert L.pa_decode(None, None) == 1
+
+
+def test_cache_and_copy_validation(L):
+    vp = FAKE
+    # T = 0 / P = 0 are no-ops; bad sizes and dtypes are rejected before launching
+    assert L.pa_reshape_and_cache(vp, vp, vp, vp, vp, 0, 8, 64, 16, 64, 0, 0, 1.0, 1.0, None) == 0
+    assert L.pa_reshape_and_cache(vp, vp, vp, vp, vp, 4, 8, 64, 16, 64, 1, 0, 1.0, 1.0, None) == 3
+    assert L.pa_reshape_and_cache(vp, vp, vp, vp, vp, 4, 8, 64, 16, 64, 2, 3, 0.0, 1.0, None) == 2
+    assert L.pa_reshape_and_cache(vp, vp, vp, vp, vp, 4, 1, 4, 16, 64, 0, 0, 1.0, 1.0, None) == 3
+    assert L.pa_reshape_and_cache(0, vp, vp, vp, vp, 4, 8, 64, 16, 64, 0, 0, 1.0, 1.0, None) == 1
+    assert L.pa_copy_blocks(vp, vp, vp, 0, 64, 16, 8, 64, 0, None) == 0
+    assert L.pa_copy_blocks(vp, vp, 0, 3, 64, 16, 8, 64, 0, None) == 1
+    assert L.pa_copy_blocks(vp, vp, vp, -1, 64, 16, 8, 64, 0, None) == 2
+    assert L.pa_slot_mapping(vp, vp, 0, 4, 16, vp, None) == 0
+    assert L.pa_slot_mapping(0, vp, 4, 4, 16, vp, None) == 1
+    assert L.pa_slot_mapping(vp, vp, 4, 0, 16, vp, None) == 2
