@@ -77,7 +77,10 @@ __device__ __forceinline__ u32x2 quantize8(const void* src8, float inv) {
         x[2 * i] = u2f(a[i] << 16);
         x[2 * i + 1] = u2f(a[i] & 0xffff0000u);
       } else {
-        f16x2 h = __builtin_bit_cast(f16x2, a[i]);
+        // bind the vector element to a scalar first: __builtin_bit_cast applied
+        // to an ext-vector element expression reads element 0 whatever the index
+        const uint32_t word = a[i];
+        const f16x2 h = __builtin_bit_cast(f16x2, word);
         x[2 * i] = static_cast<float>(h[0]);
         x[2 * i + 1] = static_cast<float>(h[1]);
       }
