@@ -1,349 +1,24 @@
-// pa_decode.hip -- paged decode attention for gfx950: split-K partition
-// kernel with an online softmax, and the partition reduce kernel.
+// pa_decode.hip -- split-K reduce kernel for paged decode attention, and the
+// choice between the two partition kernels.
 //
-// What is computed (P1 = Ultralytics glossary page "PagedAttention"):
-//   * the kernel follows each sequence's block table and gathers K and V
-//     block by block, so the cache need not be contiguous (P1 "Sayfalama
-//     Nasıl Çalışır");
-//   * attention is exact softmax attention computed in tiles, FlashAttention
-//     style: scores live only in registers, never in device memory (P1
-//     "İlgili Teknikler");
-//   * grouped-query attention: the G = Hq/Hkv query heads that share a KV
-//     head are served by one work-group, so each K/V block is read once for
-//     all of them (P1 "İlgili Teknikler");
-//   * fp8 e4m3 caches carry one fp32 scale per pool (P1 "İlgili Teknikler").
-//
-// Work decomposition.  One work-group of NW wave64s per (partition p of
-// partition_size tokens, KV head g, sequence b).  Waves take the partition's
-// blocks round-robin.  Inside a wave, a K/V row of D elements is split into
-// 16-byte chunks: LPT = D*elem/16 lanes cover one token row, so one wave load
-// instruction covers TPL = 64/LPT token rows as whole contiguous row segments
-// (coalesced), and each lane owns the same chunk of NL = bs/TPL rows of the
-// block.  q.k partial sums are reduced across the LPT lanes of a row with DPP
-// (bitwise identical in every lane), so every lane holds the scores of its own
-// rows.  Each lane keeps an online-softmax state (m, l, acc[G][chunk]) over
-// its own rows; no cross-lane exchange happens inside the block loop.  At the
-// end the per-lane states are merged across the TPL row groups (shuffles) and
-// across waves (LDS), using the same max-rescaled merge as the reduce kernel.
-// Scores are kept in log2 units (scale * k_scale * log2 e folded in) so the
-// exponentials are single v_exp_f32 instructions.
+// A sequence longer than one partition leaves, per query head and partition
+// p, the partition's running max m_p (log2 units), running sum l_p and
+// unnormalised V-weighted sum acc_p in the workspace.  Softmax over the whole
+// sequence follows from rescaling every partition to the common maximum:
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,
+// the same identity the FlashAttention-style tiling uses inside a partition
+// (P1 = Ultralytics glossary page "PagedAttention", section "İlgili
+// Teknikler").
 
 #include <hip/hip_runtime.h>
 
+#include "pa_decode_common.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 
-// Running-max start value: finite, so that exp2(m_old - m_new) is 1 (not NaN)
-// while a lane has seen no valid token; any real score is far above it.
-constexpr float kMaxInit = -1.0e30f;
-
-// ------------------------------------------------------------------ q . k ops
-
-template <int KV, int Q>
-struct Ops;
-
-template <>
-struct Ops<PA_F32, PA_F32> {
-  static constexpr int CE = 4;  // elements per 16-byte chunk
-  struct QReg {
-    float f[4];
-  };
-  __device__ static QReg load_q(const char* row, int e0) {
-    QReg r;
-    Chunk c = *reinterpret_cast<const Chunk*>(row + e0 * 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.f[i] = u2f(c.w[i]);
-    return r;
-  }
-  __device__ static float dot(const QReg& q, const Chunk& k) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = __builtin_fmaf(q.f[i], u2f(k.w[i]), s);
-    return s;
-  }
-  __device__ static void to_f32(const Chunk& v, float* o) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = u2f(v.w[i]);
-  }
-};
-
-template <>
-struct Ops<PA_F16, PA_F16> {
-  static constexpr int CE = 8;
-  struct QReg {
-    uint32_t w[4];
-  };
-  __device__ static QReg load_q(const char* row, int e0) {
-    Chunk c = *reinterpret_cast<const Chunk*>(row + e0 * 2);
-    QReg r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.w[i] = c.w[i];
-    return r;
-  }
-  // v_dot2_f32_f16: two exact fp16 products added into an fp32 accumulator
-  __device__ static float dot(const QReg& q, const Chunk& k) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q.w[i]), __builtin_bit_cast(f16x2, k.w[i]),
-                                 s, false);
-    return s;
-  }
-  __device__ static void to_f32(const Chunk& v, float* o) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f16x2 h = __builtin_bit_cast(f16x2, v.w[i]);
-      o[2 * i] = static_cast<float>(h[0]);
-      o[2 * i + 1] = static_cast<float>(h[1]);
-    }
-  }
-};
-
-template <>
-struct Ops<PA_BF16, PA_BF16> {
-  static constexpr int CE = 8;
-  struct QReg {
-    uint32_t w[4];
-  };
-  __device__ static QReg load_q(const char* row, int e0) {
-    Chunk c = *reinterpret_cast<const Chunk*>(row + e0 * 2);
-    QReg r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.w[i] = c.w[i];
-    return r;
-  }
-  // v_dot2_f32_bf16: two exact bf16 products added into an fp32 accumulator
-  __device__ static float dot(const QReg& q, const Chunk& k) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w[i]),
-                                          __builtin_bit_cast(bf16x2, k.w[i]), s, false);
-    return s;
-  }
-  __device__ static void to_f32(const Chunk& v, float* o) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = u2f(v.w[i] << 16);
-      o[2 * i + 1] = u2f(v.w[i] & 0xffff0000u);
-    }
-  }
-};
-
-// e4m3 cache with 16-bit queries: codes decoded to fp32, fp32 FMAs.
-template <int Q>
-struct OpsE4M3 {
-  static constexpr int CE = 16;
-  struct QReg {
-    float f[16];
-  };
-  __device__ static QReg load_q(const char* row, int e0) {
-    QReg r;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r.f[i] = load_elem<Q>(row, e0 + i);
-    return r;
-  }
-  __device__ static void to_f32(const Chunk& v, float* o) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e4m3x4_to_f32(v.w[i], o + 4 * i);
-  }
-  __device__ static float dot(const QReg& q, const Chunk& k) {
-    float kf[16];
-    to_f32(k, kf);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s = __builtin_fmaf(q.f[i], kf[i], s);
-    return s;
-  }
-};
-template <>
-struct Ops<PA_FP8_E4M3, PA_BF16> : OpsE4M3<PA_BF16> {};
-template <>
-struct Ops<PA_FP8_E4M3, PA_F16> : OpsE4M3<PA_F16> {};
-
-// ------------------------------------------------------------------ partition kernel
-
-template <int KV, int Q, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(const DecodeParams p) {
-  using O = Ops<KV, Q>;
-  constexpr int CE = O::CE;
-  constexpr int KVB = Elem<KV>::bytes;
-  constexpr int QB = Elem<Q>::bytes;
-  constexpr int LPT = D / CE;    // lanes per token row
-  constexpr int TPL = 64 / LPT;  // token rows per wave load
-  constexpr int NL = BS / TPL;   // rows per lane per block
-  static_assert(D % CE == 0 && 64 % LPT == 0 && BS % TPL == 0, "unsupported tile shape");
-
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_acc[NW][G][D];
-
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int max_tokens = p.max_blocks_per_seq * BS;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
-  const int PB = p.partition_size / BS;  // blocks per partition
-  const int nblk = (L + BS - 1) / BS;
-  const int jbeg = part * PB;
-  if (part > 0 && jbeg >= nblk) return;  // partition past the end of this sequence
-  const int jend = min(jbeg + PB, nblk);
-  const bool single = L <= p.partition_size;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane % LPT;   // chunk of the row this lane owns
-  const int tg = lane / LPT;  // row within a wave load
-
-  typename O::QReg qr[G];
-  {
-    const char* qrow = static_cast<const char*>(p.q) + (static_cast<size_t>(b) * p.Hq + g * G) * D * QB;
-#pragma unroll
-    for (int h = 0; h < G; ++h) qr[h] = O::load_q(qrow + h * D * QB, c * CE);
-  }
-
-  float m[G], l[G], acc[G][CE];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kMaxInit;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < CE; ++e) acc[h][e] = 0.f;
-  }
-
-  const size_t row_stride = static_cast<size_t>(p.Hkv) * D * KVB;  // bytes between token rows
-  const size_t blk_stride = row_stride * BS;
-  const size_t lane_off = static_cast<size_t>(g) * D * KVB + c * 16 + tg * row_stride;
-  const char* kbase = static_cast<const char*>(p.k_cache) + lane_off;
-  const char* vbase = static_cast<const char*>(p.v_cache) + lane_off;
-  const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
-  const float qk = p.qk_scale_log2;
-
-  for (int j = jbeg + wave; j < jend; j += NW) {
-    const int blk = table[j];
-    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(p.num_blocks)) continue;
-    Chunk kc[NL], vc[NL];
-    const char* kp = kbase + static_cast<size_t>(blk) * blk_stride;
-    const char* vp = vbase + static_cast<size_t>(blk) * blk_stride;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) kc[i] = load_chunk(kp + i * TPL * row_stride);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) vc[i] = load_chunk(vp + i * TPL * row_stride);
-
-    // valid rows of this block (only the last block of a sequence is partial)
-    const int valid = min(BS, L - j * BS);
-
-    float s[NL][G];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[i][h] = group_sum<LPT>(O::dot(qr[h], kc[i])) * qk;
-    }
-    float vf[NL][CE];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) O::to_f32(vc[i], vf[i]);
-    if (valid < BS) {
-      // rows past the end are excluded outright: their V may hold anything
-      // (NaN included), so they get weight 0 and a zeroed V row.
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        if (i * TPL + tg >= valid) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) s[i][h] = -__builtin_inff();
-#pragma unroll
-          for (int e = 0; e < CE; ++e) vf[i][e] = 0.f;
-        }
-      }
-    }
-
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = m[h];
-#pragma unroll
-      for (int i = 0; i < NL; ++i) mx = fmaxf(mx, s[i][h]);
-      const float alpha = fast_exp2(m[h] - mx);
-      m[h] = mx;
-      float lh = l[h] * alpha;
-#pragma unroll
-      for (int e = 0; e < CE; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const float pw = fast_exp2(s[i][h] - mx);
-        lh += pw;
-#pragma unroll
-        for (int e = 0; e < CE; ++e) acc[h][e] = __builtin_fmaf(pw, vf[i][e], acc[h][e]);
-      }
-      l[h] = lh;
-    }
-  }
-
-  // merge the per-lane states of the TPL row groups that own the same chunk
-#pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off, 64);
-      const float lo = __shfl_xor(l[h], off, 64);
-      const float M = fmaxf(m[h], mo);
-      const float a = fast_exp2(m[h] - M);
-      const float ao = fast_exp2(mo - M);
-      l[h] = l[h] * a + lo * ao;
-#pragma unroll
-      for (int e = 0; e < CE; ++e) acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], off, 64) * ao;
-      m[h] = M;
-    }
-  }
-
-  if (tg == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < CE; ++e) sm_acc[wave][h][c * CE + e] = acc[h][e];
-      if (c == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
-      }
-    }
-  }
-  __syncthreads();
-
-  // merge across waves; one thread per (head, element)
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float M = kMaxInit;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-    float Ls = 0.f, A = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float a = fast_exp2(sm_m[w][h] - M);
-      Ls = __builtin_fmaf(sm_l[w][h], a, Ls);
-      A = __builtin_fmaf(sm_acc[w][h][d], a, A);
-    }
-    const size_t hq = static_cast<size_t>(b) * p.Hq + g * G + h;
-    if (single) {
-      const float o = Ls > 0.f ? (A / Ls) * p.v_scale : 0.f;
-      store_out(p.out, hq * D + d, o, p.out_dtype);
-    } else {
-      const size_t pi = hq * p.num_partitions + part;
-      p.ws_acc[pi * D + d] = A * p.v_scale;
-      if (d == 0) {
-        p.ws_m[pi] = M;
-        p.ws_l[pi] = Ls;
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ reduce kernel
-
-// One work-group per (query head, sequence): combine the partitions of a
-// sequence longer than one partition.  out = sum_p 2^(m_p-M) acc_p /
-// sum_p 2^(m_p-M) l_p with M = max_p m_p (m in log2 units).
+// One work-group per (query head, sequence).
 __global__ __launch_bounds__(128) void decode_reduce_kernel(const DecodeParams p) {
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
@@ -356,7 +31,8 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const DecodeParams p
   float M = kMaxInit;
   for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_m[base + i]);
   float Ls = 0.f;
-  for (int i = 0; i < n; ++i) Ls = __builtin_fmaf(p.ws_l[base + i], fast_exp2(p.ws_m[base + i] - M), Ls);
+  for (int i = 0; i < n; ++i)
+    Ls = __builtin_fmaf(p.ws_l[base + i], fast_exp2(p.ws_m[base + i] - M), Ls);
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
   for (int d = threadIdx.x; d < p.D; d += blockDim.x) {
     float A = 0.f;
@@ -367,63 +43,11 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const DecodeParams p
   }
 }
 
-// ------------------------------------------------------------------ dispatch
-
-namespace {
-
-constexpr int kWaves = 4;
-
-template <int KV, int Q, int D, int BS, int G>
-hipError_t launch_part(const DecodeParams& p, hipStream_t s) {
-  dim3 grid(p.num_partitions, p.Hkv, p.B);
-  hipLaunchKernelGGL((decode_partition_kernel<KV, Q, D, BS, G, kWaves>), grid, dim3(kWaves * 64), 0,
-                     s, p);
-  return hipGetLastError();
-}
-
-template <int KV, int Q, int D, int BS>
-hipError_t by_group(const DecodeParams& p, hipStream_t s, bool* ok) {
-  switch (p.Hq / p.Hkv) {
-    case 1: return launch_part<KV, Q, D, BS, 1>(p, s);
-    case 2: return launch_part<KV, Q, D, BS, 2>(p, s);
-    case 4: return launch_part<KV, Q, D, BS, 4>(p, s);
-    case 8: return launch_part<KV, Q, D, BS, 8>(p, s);
-    default: *ok = false; return hipSuccess;
-  }
-}
-
-template <int KV, int Q, int D>
-hipError_t by_block(const DecodeParams& p, hipStream_t s, bool* ok) {
-  switch (p.block_size) {
-    case 16: return by_group<KV, Q, D, 16>(p, s, ok);
-    case 32: return by_group<KV, Q, D, 32>(p, s, ok);
-    default: *ok = false; return hipSuccess;
-  }
-}
-
-template <int KV, int Q>
-hipError_t by_dim(const DecodeParams& p, hipStream_t s, bool* ok) {
-  switch (p.D) {
-    case 64: return by_block<KV, Q, 64>(p, s, ok);
-    case 128: return by_block<KV, Q, 128>(p, s, ok);
-    default: *ok = false; return hipSuccess;
-  }
-}
-
-}  // namespace
-
 hipError_t launch_decode_partition(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
                                    hipStream_t stream, bool* supported) {
-  *supported = true;
-  if (kv_dtype == PA_F32 && q_dtype == PA_F32) return by_dim<PA_F32, PA_F32>(p, stream, supported);
-  if (kv_dtype == PA_F16 && q_dtype == PA_F16) return by_dim<PA_F16, PA_F16>(p, stream, supported);
-  if (kv_dtype == PA_BF16 && q_dtype == PA_BF16) return by_dim<PA_BF16, PA_BF16>(p, stream, supported);
-  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16)
-    return by_dim<PA_FP8_E4M3, PA_BF16>(p, stream, supported);
-  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16)
-    return by_dim<PA_FP8_E4M3, PA_F16>(p, stream, supported);
-  *supported = false;
-  return hipSuccess;
+  if (decode_mfma_serves(q_dtype, kv_dtype, p.Hq / p.Hkv))
+    return launch_decode_mfma(p, q_dtype, kv_dtype, stream, supported);
+  return launch_decode_valu(p, q_dtype, kv_dtype, stream, supported);
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {

@@ -1,0 +1,417 @@
+// pa_decode_mfma.hip -- decode-partition kernel on the matrix cores, used for
+// grouped-query attention with G = Hq/Hkv of 4 or 8 and 16-bit or e4m3 caches.
+//
+// With grouped-query attention (P1 = Ultralytics glossary page
+// "PagedAttention", section "İlgili Teknikler") the G query heads that share
+// a KV head read the same K/V block, so per 16-token tile the scores are a
+// dense G x 16 x D contraction and the weighted sum a G x D x 16 one: at G = 8
+// and 16-bit caches that is 8 flop per byte of K/V, more than the vector ALUs
+// sustain at full HBM bandwidth.  Both contractions run here as 16x16 MFMAs
+// with the query group padded to 16 rows; the softmax between them runs on
+// the MFMA result layout.  The paging itself is as in the VALU kernel: each
+// wave follows the block table, one block at a time, and the scores never
+// leave registers (P1 "Sayfalama Nasıl Çalışır"; "İlgili Teknikler",
+// FlashAttention-style tiling).
+//
+// Lane layout of a 16x16 MFMA on gfx950 (lane l, lo = l % 16, grp = l / 16):
+//   A (16 x K): row lo, a run of K/4 values picked by (grp, element);
+//   B (K x 16): column lo, the same (grp, element) -> k pairing as A;
+//   D (16 x 16, four fp32 per lane): D[4*grp + r][lo] in element r.
+// Only the pairing of A and B slots matters for a contraction, so each side
+// may assign head-dim positions (or tokens) to (grp, element) slots freely as
+// long as both use the same assignment.
+//
+// Scores:  S^T[t][q] = sum_d K[t][d] Q[q][d], one v_mfma_f32_16x16x32 per 32
+//   head-dim values: A = 16 token rows of K (lane: token lo), B = Q^T (lane:
+//   query lo; zero for lo >= G).  Lane l then holds the scores of query lo
+//   for tokens 4*grp + r, r = 0..3.
+// Weighted sum: O[q][d] += sum_t P[q][t] V[t][d], one v_mfma_f32_16x16x16 per
+//   16 output columns: A = P straight from the score layout (lane: query lo,
+//   tokens 4*grp + e), B = V with lane l holding tokens 4*grp + e of column
+//   lo, where MFMA number mm maps column lo to head-dim d = (D/16)*lo + mm.
+//   Each lane therefore loads one contiguous D/16-element run of four token
+//   rows, and the 16 lanes of a group cover each row whole (coalesced).
+// The running maximum is kept exact per query: when a block raises it, the
+// accumulators of the affected queries are rescaled (rare after the first
+// blocks).  e4m3 codes are widened to the operand type (bf16 or f16, both
+// hold every e4m3 value exactly) in registers before the MFMAs.
+
+#include <hip/hip_runtime.h>
+
+#include "pa_decode_common.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// MFMA operand type (the query dtype): contractions, packing of fp32 weights
+// and widening of e4m3 codes.
+template <int MT>
+struct Mfma;
+
+template <>
+struct Mfma<PA_BF16> {
+  __device__ static f32x4 qk(const uint32_t* a, const uint32_t* b, f32x4 c) {
+    const u32x4 av = {a[0], a[1], a[2], a[3]};
+    const u32x4 bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                   __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+  }
+  __device__ static f32x4 pv(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+    const u32x2 av = {a0, a1};
+    const u32x2 bv = {b0, b1};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, av),
+                                                     __builtin_bit_cast(s16x4, bv), c, 0, 0, 0);
+  }
+  // two fp32 -> bf16 pair, round to nearest even
+  __device__ static uint32_t pack2(float x, float y) {
+    const bf16x2 v = {static_cast<__bf16>(x), static_cast<__bf16>(y)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  // four e4m3 codes -> two dwords of bf16 pairs (exact)
+  __device__ static void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  }
+};
+
+template <>
+struct Mfma<PA_F16> {
+  __device__ static f32x4 qk(const uint32_t* a, const uint32_t* b, f32x4 c) {
+    const u32x4 av = {a[0], a[1], a[2], a[3]};
+    const u32x4 bv = {b[0], b[1], b[2], b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+                                                  __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
+  }
+  __device__ static f32x4 pv(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+    const u32x2 av = {a0, a1};
+    const u32x2 bv = {b0, b1};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
+                                                 __builtin_bit_cast(f16x4, bv), c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float x, float y) {
+    const f16x2 v = {static_cast<_Float16>(x), static_cast<_Float16>(y)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  }
+};
+
+// Non-temporal load of N dwords (N = 1, 2 or 4) at a 4N-byte aligned address.
+template <int N>
+__device__ __forceinline__ void load_dwords(const char* p, uint32_t* out) {
+  if constexpr (N == 4) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    out[0] = v[0];
+    out[1] = v[1];
+    out[2] = v[2];
+    out[3] = v[3];
+  } else if constexpr (N == 2) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    out[0] = v[0];
+    out[1] = v[1];
+  } else {
+    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+}
+
+// Half `sel` (0 = low, 1 = high) of dwords a and b, packed as (a_half, b_half).
+__device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int sel) {
+  return sel ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+}
+
+template <int KV, int Q, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams p) {
+  using M = Mfma<Q>;
+  constexpr bool FP8 = KV == PA_FP8_E4M3;
+  constexpr int KVB = FP8 ? 1 : 2;
+  constexpr int SS = D / 32;                    // score MFMAs per tile (32 head-dim values each)
+  constexpr int EPL = D / 16;                   // V elements per lane per row = PV MFMAs per tile
+  constexpr int TT = BS / 16;                   // 16-token tiles per block
+  constexpr int KW = D / 8;                     // dwords of 16-bit K per lane per tile
+  constexpr int KR = FP8 ? D / 16 : D / 8;      // dwords of stored K per lane per tile
+  constexpr int VW = EPL / 2;                   // dwords of 16-bit V per lane per row
+  constexpr int VR = FP8 ? EPL / 4 : EPL / 2;   // dwords of stored V per lane per row
+  constexpr int KLD = KR >= 4 ? 4 : KR;         // dwords per K load instruction
+  static_assert(G == 4 || G == 8, "MFMA path serves query groups of 4 or 8");
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(BS % 16 == 0, "block size");
+
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_acc[NW][G][D];
+
+  const int g = blockIdx.x;
+  const int part = blockIdx.y;
+  const int b = blockIdx.z;
+  const PartitionSpan span = partition_span<BS>(p, b, part);
+  if (span.skip) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lo = lane & 15;
+  const int grp = lane >> 4;
+
+  // Head-dim chunk (8 values) that lane group grp feeds into score MFMA s.
+  // 16-bit caches: chunk 4s+grp, so each K load instruction reads 64
+  // contiguous bytes of every one of the tile's 16 rows.  e4m3: chunk
+  // SS*grp+s, so a lane's K bytes for the tile are one contiguous run.
+  auto chunk_of = [&](int s) { return FP8 ? SS * grp + s : 4 * s + grp; };
+
+  // Q^T operand: query lo of the group, zero rows beyond G.
+  uint32_t qw[KW];
+  if (lo < G) {
+    const char* qrow =
+        static_cast<const char*>(p.q) + ((static_cast<size_t>(b) * p.Hq + g * G + lo) * D) * 2;
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      const Chunk c = *reinterpret_cast<const Chunk*>(qrow + chunk_of(s) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qw[4 * s + i] = c.w[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KW; ++i) qw[i] = 0u;
+  }
+
+  f32x4 O[EPL];
+#pragma unroll
+  for (int mm = 0; mm < EPL; ++mm) O[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kMaxInit;  // running max of query lo (log2 units), same in all four groups
+  float l_part = 0.f;      // this lane's share of the running sum of query lo
+
+  const size_t row_stride = static_cast<size_t>(p.Hkv) * D * KVB;
+  const size_t blk_stride = row_stride * BS;
+  const size_t head_off = static_cast<size_t>(g) * D * KVB;
+  // K: token row lo of each tile; e4m3 lanes start at their contiguous run
+  const size_t k_off = head_off + lo * row_stride + (FP8 ? static_cast<size_t>(grp) * (D / 4) : 0);
+  // V: token rows 4*grp + e of each tile, elements [EPL*lo, EPL*lo + EPL)
+  const size_t v_off = head_off + (4 * grp) * row_stride + static_cast<size_t>(EPL * lo) * KVB;
+  const char* kbase = static_cast<const char*>(p.k_cache) + k_off;
+  const char* vbase = static_cast<const char*>(p.v_cache) + v_off;
+  const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+  const float qk = p.qk_scale_log2;
+
+  struct Raw {
+    uint32_t k[TT][KR];
+    uint32_t v[TT][4][VR];
+  };
+
+  auto load_block = [&](int blk, Raw& r) -> bool {
+    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(p.num_blocks)) return false;
+    const char* kp = kbase + static_cast<size_t>(blk) * blk_stride;
+    const char* vp = vbase + static_cast<size_t>(blk) * blk_stride;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const char* kt = kp + static_cast<size_t>(tt) * 16 * row_stride;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < KR; i += KLD) load_dwords<KLD>(kt + i * 4, &r.k[tt][i]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < SS; ++s) load_dwords<4>(kt + chunk_of(s) * 16, &r.k[tt][4 * s]);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        load_dwords<VR>(vp + (static_cast<size_t>(tt) * 16 + e) * row_stride, r.v[tt][e]);
+    }
+    return true;
+  };
+
+  auto consume = [&](int j, Raw& r) {
+    const int valid = min(BS, span.L - j * BS);
+    float sc[TT][4];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      uint32_t kw[KW];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < KR; ++i) M::widen4(r.k[tt][i], kw[2 * i], kw[2 * i + 1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < KW; ++i) kw[i] = r.k[tt][i];
+      }
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < SS; ++s) S = M::qk(&kw[4 * s], &qw[4 * s], S);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // rows past the end may hold anything (NaN included): excluded outright
+        const int t = tt * 16 + 4 * grp + i;
+        sc[tt][i] = t < valid ? S[i] * qk : -__builtin_inff();
+      }
+    }
+    float bm = sc[0][0];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[tt][i]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m_run, bm);
+    if (__ballot(mn > m_run)) {
+      const float alpha = fast_exp2(m_run - mn);
+      l_part *= alpha;
+      float a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = __shfl(alpha, 4 * grp + i, 64);
+#pragma unroll
+      for (int mm = 0; mm < EPL; ++mm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[mm][i] *= a[i];
+      }
+      m_run = mn;
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      float pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] = fast_exp2(sc[tt][i] - m_run);
+        l_part += pw[i];
+      }
+      const uint32_t pa0 = M::pack2(pw[0], pw[1]);
+      const uint32_t pa1 = M::pack2(pw[2], pw[3]);
+      if (valid < BS) {
+        // zero the V rows past the end so that 0 * NaN cannot reach the sum
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (tt * 16 + 4 * grp + e >= valid) {
+#pragma unroll
+            for (int i = 0; i < VR; ++i) r.v[tt][e][i] = 0u;
+          }
+        }
+      }
+      uint32_t vw[4][VW];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (FP8) {
+#pragma unroll
+          for (int i = 0; i < VR; ++i) M::widen4(r.v[tt][e][i], vw[e][2 * i], vw[e][2 * i + 1]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VW; ++i) vw[e][i] = r.v[tt][e][i];
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < EPL; ++mm) {
+        const uint32_t b0 = pick_halves(vw[0][mm >> 1], vw[1][mm >> 1], mm & 1);
+        const uint32_t b1 = pick_halves(vw[2][mm >> 1], vw[3][mm >> 1], mm & 1);
+        O[mm] = M::pv(pa0, pa1, b0, b1, O[mm]);
+      }
+    }
+  };
+
+  const int nmine = wave_block_count<NW>(span, wave);
+  for (int base = 0; base < nmine; base += 64) {
+    const int cnt = min(64, nmine - base);
+    const int ids = prefetch_block_ids<NW>(table, span, wave, base, cnt, lane);
+    const int j0 = span.jbeg + wave + base * NW;
+    Raw ra, rb;
+    bool oka = load_block(block_id_at(ids, 0), ra);
+    bool okb = false;
+    for (int i = 0; i < cnt; i += 2) {
+      if (i + 1 < cnt) okb = load_block(block_id_at(ids, i + 1), rb);
+      if (oka) consume(j0 + i * NW, ra);
+      if (i + 1 >= cnt) break;
+      if (i + 2 < cnt) oka = load_block(block_id_at(ids, i + 2), ra);
+      if (okb) consume(j0 + (i + 1) * NW, rb);
+    }
+  }
+
+  float lt = l_part + __shfl_xor(l_part, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (grp == 0 && lo < G) {
+    sm_m[wave][lo] = m_run;
+    sm_l[wave][lo] = lt;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = 4 * grp + i;
+    if (q < G) {
+#pragma unroll
+      for (int mm = 0; mm < EPL; ++mm) sm_acc[wave][q][EPL * lo + mm] = O[mm][i];
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store<G, D, NW>(p, sm_m, sm_l, sm_acc, b, g, part, span.single);
+}
+
+// ------------------------------------------------------------------ dispatch
+
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int KV, int Q, int D, int BS, int G>
+hipError_t launch(const DecodeParams& p, hipStream_t s) {
+  dim3 grid(p.Hkv, p.num_partitions, p.B);
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, D, BS, G, kWaves>), grid, dim3(kWaves * 64), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+template <int KV, int Q, int D, int BS>
+hipError_t by_group(const DecodeParams& p, hipStream_t s, bool* ok) {
+  switch (p.Hq / p.Hkv) {
+    case 4: return launch<KV, Q, D, BS, 4>(p, s);
+    case 8: return launch<KV, Q, D, BS, 8>(p, s);
+    default: *ok = false; return hipSuccess;
+  }
+}
+
+template <int KV, int Q, int D>
+hipError_t by_block(const DecodeParams& p, hipStream_t s, bool* ok) {
+  switch (p.block_size) {
+    case 16: return by_group<KV, Q, D, 16>(p, s, ok);
+    case 32: return by_group<KV, Q, D, 32>(p, s, ok);
+    default: *ok = false; return hipSuccess;
+  }
+}
+
+template <int KV, int Q>
+hipError_t by_dim(const DecodeParams& p, hipStream_t s, bool* ok) {
+  switch (p.D) {
+    case 64: return by_block<KV, Q, 64>(p, s, ok);
+    case 128: return by_block<KV, Q, 128>(p, s, ok);
+    default: *ok = false; return hipSuccess;
+  }
+}
+
+}  // namespace
+
+bool decode_mfma_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t group) {
+  if (group != 4 && group != 8) return false;
+  return (kv_dtype == PA_F16 && q_dtype == PA_F16) || (kv_dtype == PA_BF16 && q_dtype == PA_BF16) ||
+         (kv_dtype == PA_FP8_E4M3 && (q_dtype == PA_BF16 || q_dtype == PA_F16));
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
+                              hipStream_t stream, bool* supported) {
+  *supported = true;
+  if (kv_dtype == PA_F16 && q_dtype == PA_F16) return by_dim<PA_F16, PA_F16>(p, stream, supported);
+  if (kv_dtype == PA_BF16 && q_dtype == PA_BF16)
+    return by_dim<PA_BF16, PA_BF16>(p, stream, supported);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16)
+    return by_dim<PA_FP8_E4M3, PA_BF16>(p, stream, supported);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16)
+    return by_dim<PA_FP8_E4M3, PA_F16>(p, stream, supported);
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace pa

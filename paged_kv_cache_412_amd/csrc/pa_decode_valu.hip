@@ -1,0 +1,398 @@
+// pa_decode_valu.hip -- decode-partition kernel on the vector ALUs, used when
+// few query heads share a KV head (G = Hq/Hkv of 1 or 2) and for fp32 caches.
+//
+// What is computed (P1 = Ultralytics glossary page "PagedAttention"):
+//   * the kernel follows each sequence's block table and gathers K and V
+//     block by block, so the cache need not be contiguous (P1 "Sayfalama
+//     Nasıl Çalışır");
+//   * attention is exact softmax attention computed in tiles, FlashAttention
+//     style: scores live only in registers, never in device memory (P1
+//     "İlgili Teknikler");
+//   * grouped-query attention: the G query heads that share a KV head are
+//     served by one work-group, so each K/V block is read once for all of
+//     them (P1 "İlgili Teknikler").
+//
+// Work decomposition.  One work-group of NW wave64s per (KV head g,
+// partition, sequence).  Waves take the partition's blocks round-robin.
+// Inside a wave, a K/V row of D elements is split into 16-byte chunks: LPT =
+// D*elem/16 lanes cover one token row, so one wave load instruction covers
+// TPL = 64/LPT token rows as whole contiguous row segments, and each lane owns
+// the same chunk of NL = bs/TPL rows of the block.  q.k partial sums are
+// reduced across the LPT lanes of a row with DPP (bitwise identical in every
+// lane), so every lane holds the scores of its own rows.  Each lane keeps an
+// online-softmax state (m, l, acc[G][chunk]) over its own rows; no cross-lane
+// exchange happens inside the block loop.  The loads of a wave's next block
+// are issued before the current block is consumed, so two blocks of K and V
+// are in flight per wave.  At the end the per-lane states are merged across
+// the TPL row groups (shuffles) and across waves (LDS).  Scores are kept in
+// log2 units (scale * k_scale * log2 e folded in) so the exponentials are
+// single v_exp_f32 instructions.
+
+#include <hip/hip_runtime.h>
+
+#include "pa_decode_common.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// ------------------------------------------------------------------ q . k ops
+
+template <int KV, int Q>
+struct Ops;
+
+template <>
+struct Ops<PA_F32, PA_F32> {
+  static constexpr int CE = 4;  // elements per 16-byte chunk
+  struct QReg {
+    float f[4];
+  };
+  __device__ static QReg load_q(const char* row, int e0) {
+    QReg r;
+    Chunk c = *reinterpret_cast<const Chunk*>(row + e0 * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.f[i] = u2f(c.w[i]);
+    return r;
+  }
+  __device__ static float dot(const QReg& q, const Chunk& k) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = __builtin_fmaf(q.f[i], u2f(k.w[i]), s);
+    return s;
+  }
+  __device__ static void to_f32(const Chunk& v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = u2f(v.w[i]);
+  }
+};
+
+template <>
+struct Ops<PA_F16, PA_F16> {
+  static constexpr int CE = 8;
+  struct QReg {
+    uint32_t w[4];
+  };
+  __device__ static QReg load_q(const char* row, int e0) {
+    Chunk c = *reinterpret_cast<const Chunk*>(row + e0 * 2);
+    QReg r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = c.w[i];
+    return r;
+  }
+  // v_dot2_f32_f16: two exact fp16 products added into an fp32 accumulator
+  __device__ static float dot(const QReg& q, const Chunk& k) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qw = q.w[i], kw = k.w[i];
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw), __builtin_bit_cast(f16x2, kw), s,
+                                 false);
+    }
+    return s;
+  }
+  __device__ static void to_f32(const Chunk& v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = v.w[i];
+      const f16x2 h = __builtin_bit_cast(f16x2, w);
+      o[2 * i] = static_cast<float>(h[0]);
+      o[2 * i + 1] = static_cast<float>(h[1]);
+    }
+  }
+};
+
+template <>
+struct Ops<PA_BF16, PA_BF16> {
+  static constexpr int CE = 8;
+  struct QReg {
+    uint32_t w[4];
+  };
+  __device__ static QReg load_q(const char* row, int e0) {
+    Chunk c = *reinterpret_cast<const Chunk*>(row + e0 * 2);
+    QReg r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = c.w[i];
+    return r;
+  }
+  // v_dot2_f32_bf16: two exact bf16 products added into an fp32 accumulator
+  __device__ static float dot(const QReg& q, const Chunk& k) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qw = q.w[i], kw = k.w[i];
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw),
+                                          __builtin_bit_cast(bf16x2, kw), s, false);
+    }
+    return s;
+  }
+  __device__ static void to_f32(const Chunk& v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = u2f(v.w[i] << 16);
+      o[2 * i + 1] = u2f(v.w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// e4m3 cache with 16-bit queries: codes decoded to fp32, fp32 FMAs.
+template <int Q>
+struct OpsE4M3 {
+  static constexpr int CE = 16;
+  struct QReg {
+    float f[16];
+  };
+  __device__ static QReg load_q(const char* row, int e0) {
+    QReg r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r.f[i] = load_elem<Q>(row, e0 + i);
+    return r;
+  }
+  __device__ static void to_f32(const Chunk& v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e4m3x4_to_f32(v.w[i], o + 4 * i);
+  }
+  __device__ static float dot(const QReg& q, const Chunk& k) {
+    float kf[16];
+    to_f32(k, kf);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = __builtin_fmaf(q.f[i], kf[i], s);
+    return s;
+  }
+};
+template <>
+struct Ops<PA_FP8_E4M3, PA_BF16> : OpsE4M3<PA_BF16> {};
+template <>
+struct Ops<PA_FP8_E4M3, PA_F16> : OpsE4M3<PA_F16> {};
+
+// ------------------------------------------------------------------ kernel
+
+template <int KV, int Q, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams p) {
+  using O = Ops<KV, Q>;
+  constexpr int CE = O::CE;
+  constexpr int KVB = Elem<KV>::bytes;
+  constexpr int QB = Elem<Q>::bytes;
+  constexpr int LPT = D / CE;    // lanes per token row
+  constexpr int TPL = 64 / LPT;  // token rows per wave load
+  constexpr int NL = BS / TPL;   // rows per lane per block
+  static_assert(D % CE == 0 && 64 % LPT == 0 && BS % TPL == 0, "unsupported tile shape");
+
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_acc[NW][G][D];
+
+  const int g = blockIdx.x;
+  const int part = blockIdx.y;
+  const int b = blockIdx.z;
+  const PartitionSpan span = partition_span<BS>(p, b, part);
+  if (span.skip) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane % LPT;   // chunk of the row this lane owns
+  const int tg = lane / LPT;  // row within a wave load
+
+  typename O::QReg qr[G];
+  {
+    const char* qrow =
+        static_cast<const char*>(p.q) + (static_cast<size_t>(b) * p.Hq + g * G) * D * QB;
+#pragma unroll
+    for (int h = 0; h < G; ++h) qr[h] = O::load_q(qrow + h * D * QB, c * CE);
+  }
+
+  float m[G], l[G], acc[G][CE];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kMaxInit;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < CE; ++e) acc[h][e] = 0.f;
+  }
+
+  const size_t row_stride = static_cast<size_t>(p.Hkv) * D * KVB;  // bytes between token rows
+  const size_t blk_stride = row_stride * BS;
+  const size_t lane_off = static_cast<size_t>(g) * D * KVB + c * 16 + tg * row_stride;
+  const char* kbase = static_cast<const char*>(p.k_cache) + lane_off;
+  const char* vbase = static_cast<const char*>(p.v_cache) + lane_off;
+  const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+  const float qk = p.qk_scale_log2;
+
+  // Issue the K and V loads of the block with id `blk`; false (nothing
+  // loaded) for an id outside the pool.
+  auto load_block = [&](int blk, Chunk (&kc)[NL], Chunk (&vc)[NL]) -> bool {
+    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(p.num_blocks)) return false;
+    const char* kp = kbase + static_cast<size_t>(blk) * blk_stride;
+    const char* vp = vbase + static_cast<size_t>(blk) * blk_stride;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) kc[i] = load_chunk(kp + i * TPL * row_stride);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vc[i] = load_chunk(vp + i * TPL * row_stride);
+    return true;
+  };
+
+  // Fold logical block j (its rows already loaded) into the running state.
+  auto consume = [&](int j, const Chunk (&kc)[NL], const Chunk (&vc)[NL]) {
+    // valid rows of this block (only the last block of a sequence is partial)
+    const int valid = min(BS, span.L - j * BS);
+    float s[NL][G];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[i][h] = group_sum<LPT>(O::dot(qr[h], kc[i])) * qk;
+    }
+    float vf[NL][CE];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) O::to_f32(vc[i], vf[i]);
+    if (valid < BS) {
+      // rows past the end are excluded outright: their K and V may hold
+      // anything (NaN included), so they get weight 0 and a zeroed V row.
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        if (i * TPL + tg >= valid) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[i][h] = -__builtin_inff();
+#pragma unroll
+          for (int e = 0; e < CE; ++e) vf[i][e] = 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = m[h];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) mx = fmaxf(mx, s[i][h]);
+      const float alpha = fast_exp2(m[h] - mx);
+      m[h] = mx;
+      float lh = l[h] * alpha;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float pw = fast_exp2(s[i][h] - mx);
+        lh += pw;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) acc[h][e] = __builtin_fmaf(pw, vf[i][e], acc[h][e]);
+      }
+      l[h] = lh;
+    }
+  };
+
+  // Two register sets in ping-pong: the loads of iteration i+1 are in flight
+  // while iteration i is consumed.
+  const int nmine = wave_block_count<NW>(span, wave);
+  for (int base = 0; base < nmine; base += 64) {
+    const int cnt = min(64, nmine - base);
+    const int ids = prefetch_block_ids<NW>(table, span, wave, base, cnt, lane);
+    const int j0 = span.jbeg + wave + base * NW;
+    Chunk ka[NL], va[NL], kb[NL], vb[NL];
+    bool oka = load_block(block_id_at(ids, 0), ka, va);
+    bool okb = false;
+    for (int i = 0; i < cnt; i += 2) {
+      if (i + 1 < cnt) okb = load_block(block_id_at(ids, i + 1), kb, vb);
+      if (oka) consume(j0 + i * NW, ka, va);
+      if (i + 1 >= cnt) break;
+      if (i + 2 < cnt) oka = load_block(block_id_at(ids, i + 2), ka, va);
+      if (okb) consume(j0 + (i + 1) * NW, kb, vb);
+    }
+  }
+
+  // merge the per-lane states of the TPL row groups that own the same chunk
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], off, 64);
+      const float lo = __shfl_xor(l[h], off, 64);
+      const float M = fmaxf(m[h], mo);
+      const float a = fast_exp2(m[h] - M);
+      const float ao = fast_exp2(mo - M);
+      l[h] = l[h] * a + lo * ao;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], off, 64) * ao;
+      m[h] = M;
+    }
+  }
+
+  if (tg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < CE; ++e) sm_acc[wave][h][c * CE + e] = acc[h][e];
+      if (c == 0) {
+        sm_m[wave][h] = m[h];
+        sm_l[wave][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store<G, D, NW>(p, sm_m, sm_l, sm_acc, b, g, part, span.single);
+}
+
+// ------------------------------------------------------------------ dispatch
+
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int KV, int Q, int D, int BS, int G>
+hipError_t launch(const DecodeParams& p, hipStream_t s) {
+  dim3 grid(p.Hkv, p.num_partitions, p.B);
+  hipLaunchKernelGGL((decode_valu_kernel<KV, Q, D, BS, G, kWaves>), grid, dim3(kWaves * 64), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+template <int KV, int Q, int D, int BS>
+hipError_t by_group(const DecodeParams& p, hipStream_t s, bool* ok) {
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch<KV, Q, D, BS, 1>(p, s);
+    case 2: return launch<KV, Q, D, BS, 2>(p, s);
+    case 4:
+      if constexpr (KV == PA_F32) return launch<KV, Q, D, BS, 4>(p, s);
+      break;
+    case 8:
+      if constexpr (KV == PA_F32) return launch<KV, Q, D, BS, 8>(p, s);
+      break;
+    default: break;
+  }
+  *ok = false;
+  return hipSuccess;
+}
+
+template <int KV, int Q, int D>
+hipError_t by_block(const DecodeParams& p, hipStream_t s, bool* ok) {
+  switch (p.block_size) {
+    case 16: return by_group<KV, Q, D, 16>(p, s, ok);
+    case 32: return by_group<KV, Q, D, 32>(p, s, ok);
+    default: *ok = false; return hipSuccess;
+  }
+}
+
+template <int KV, int Q>
+hipError_t by_dim(const DecodeParams& p, hipStream_t s, bool* ok) {
+  switch (p.D) {
+    case 64: return by_block<KV, Q, 64>(p, s, ok);
+    case 128: return by_block<KV, Q, 128>(p, s, ok);
+    default: *ok = false; return hipSuccess;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
+                              hipStream_t stream, bool* supported) {
+  *supported = true;
+  if (kv_dtype == PA_F32 && q_dtype == PA_F32) return by_dim<PA_F32, PA_F32>(p, stream, supported);
+  if (kv_dtype == PA_F16 && q_dtype == PA_F16) return by_dim<PA_F16, PA_F16>(p, stream, supported);
+  if (kv_dtype == PA_BF16 && q_dtype == PA_BF16)
+    return by_dim<PA_BF16, PA_BF16>(p, stream, supported);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16)
+    return by_dim<PA_FP8_E4M3, PA_BF16>(p, stream, supported);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16)
+    return by_dim<PA_FP8_E4M3, PA_F16>(p, stream, supported);
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace pa

@@ -32,11 +32,21 @@ struct DecodeParams {
 // Default tokens per split-K partition.
 constexpr int32_t kDefaultPartition = 512;
 
+// Grid limit on the partition axis (grid y).
+constexpr int32_t kMaxPartitions = 65535;
+
 // Block copy: 16-byte chunks handled by one work-group (16 KiB).
 constexpr int kCopySliceChunks = 1024;
 
 hipError_t launch_decode_partition(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
                                    hipStream_t stream, bool* supported);
+// The two partition kernels: matrix cores for query groups of 4 or 8 over
+// 16-bit or e4m3 caches, vector ALUs for everything else.
+bool decode_mfma_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t group);
+hipError_t launch_decode_mfma(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
+                              hipStream_t stream, bool* supported);
+hipError_t launch_decode_valu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
+                              hipStream_t stream, bool* supported);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* positions, int32_t B,

@@ -117,9 +117,12 @@ def test_peaked_attention(name, sigma):
     check_step(wl, step, exp, out_dtype="f32")
 
 
-def test_e4m3_decode_every_code_exactly():
-    """L = 1 puts all weight on one V row, so out = decode(code) * v_scale exactly."""
-    print("\n[case] e4m3 decode of all 256 codes", flush=True)
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("qdt", [torch.bfloat16, torch.float16])
+def test_e4m3_decode_every_code_exactly(G, qdt):
+    """L = 1 puts all weight on one V row, so out = decode(code) * v_scale
+    exactly, on the vector path (G <= 2) and the matrix-core path (G >= 4)."""
+    print(f"\n[case] e4m3 decode of all 256 codes, G={G} q={qdt}", flush=True)
     D, bs, NB = 128, 16, 4
     dev = "cuda"
     k = torch.full((NB, bs, 1, D), 0x38, dtype=torch.uint8, device=dev)      # 1.0
@@ -127,17 +130,36 @@ def test_e4m3_decode_every_code_exactly():
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
     v[1, 0, 0, :] = codes[:128].to(dev)
     v[2, 0, 0, :] = codes[128:].to(dev)
-    q = torch.ones((2, 1, D), dtype=torch.bfloat16, device=dev)
+    q = torch.ones((2, G, D), dtype=qdt, device=dev)
     tables = torch.tensor([[1], [2]], dtype=torch.int32, device=dev)
     lens = torch.tensor([1, 1], dtype=torch.int32, device=dev)
-    out = torch.empty((2, 1, D), dtype=torch.float32, device=dev)
+    out = torch.empty((2, G, D), dtype=torch.float32, device=dev)
     binding.decode(out, q, k, v, tables, lens, 0.1, 1.0, 1.0, kv_dtype="e4m3")
     torch.cuda.synchronize()
-    got = out.cpu().numpy().reshape(256).astype(np.float64)
     ref = fp8.DECODE_TABLE
     nan = np.isnan(ref)
-    assert np.array_equal(np.isnan(got), nan)
-    assert np.array_equal(got[~nan], ref[~nan])
+    for h in range(G):
+        got = out[:, h].cpu().numpy().reshape(256).astype(np.float64)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+
+
+# every (q, kv) pair, head dim, block size and group size the library builds
+DTYPE_PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3")]
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("pair", DTYPE_PAIRS, ids=["-".join(p) for p in DTYPE_PAIRS])
+def test_every_supported_shape(pair, D, bs, G):
+    qd, kvd = pair
+    cfg = workloads.Config(f"shape-{qd}-{kvd}-{D}-{bs}-{G}", 7, B=4, Hq=2 * G, Hkv=2, D=D,
+                           block_size=bs, kv_dtype=kvd, q_dtype=qd, out_dtype=qd, src_dtype=qd,
+                           lens=(1, bs + 3, 700, 1100))
+    wl, step, exp = run_step(cfg, partition_size=512)
+    err = check_step(wl, step, exp)
+    print(f"[ok] max abs err {err:.3e}", flush=True)
 
 
 def e4m3_sweep_values(rng):
