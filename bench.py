@@ -29,7 +29,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 METRIC = "paged decode attention: effective KV GB/s and % of HBM peak; seqs/s per layer"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["paged_kv_cache_412_amd/csrc/pa_decode.hip", "paged_kv_cache_412_amd/csrc/pa_device.h"]
+KERNEL_SOURCES = ["paged_kv_cache_412_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_412_amd/csrc/pa_decode_valu.hip",
+                  "paged_kv_cache_412_amd/csrc/pa_decode_mfma.hip",
+                  "paged_kv_cache_412_amd/csrc/pa_decode_common.h",
+                  "paged_kv_cache_412_amd/csrc/pa_device.h",
+                  "paged_kv_cache_412_amd/csrc/pa_api.hip"]
+CALIBRATION_BYTES = 1 << 30  # size of the plain copy used to scale the PMC byte counters
 
 
 def kernel_hash() -> str:
@@ -46,10 +52,17 @@ def kv_bytes(wl) -> int:
     return int(np.sum(wl.seq_lens)) * 2 * c.Hkv * c.D * ELEM_BYTES[c.kv_dtype]
 
 
-def measured_traffic(workload: str):
+def decode_kernel_name(cfg) -> str:
+    """The partition kernel the library dispatches for this workload: the
+    matrix-core kernel for query groups of 4 or 8 over 16-bit or e4m3 caches,
+    the vector-ALU kernel otherwise."""
+    return "decode_mfma_kernel" if cfg.G in (4, 8) and cfg.kv_dtype != "f32" else "decode_valu_kernel"
+
+
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed PMC counter runs, if they were taken
     on the current kernel source."""
-    path = os.path.join(TRAFFIC_DIR, f"traffic_decode_partition_{workload}.json")
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
@@ -57,6 +70,20 @@ def measured_traffic(workload: str):
     if rec.get("kernel_hash") != kernel_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain device-to-device copy of CALIBRATION_BYTES, three times: the
+    reference the PMC byte counters are scaled by."""
+    import torch
+    src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": CALIBRATION_BYTES, "copies": 3}), flush=True)
+    return 0
 
 
 def cpu_baseline(wl, step, budget_s: float):
@@ -101,6 +128,8 @@ def main(argv=None):
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the plain copy the PMC byte counters are scaled by")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -116,6 +145,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration()
     binding.lib()
     cfg = workloads.CONFIGS[args.workload]
     print(f"[bench] building workload {cfg.name}", file=sys.stderr, flush=True)
@@ -155,7 +186,9 @@ def main(argv=None):
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     part_ms = stage_ms["decode_partition"]
     achieved = nbytes / (part_ms * 1e-3) / 1e9
-    traffic = measured_traffic(cfg.name)
+    kernel = decode_kernel_name(cfg)
+    traffic = measured_traffic(kernel, cfg.name)
+    partition = binding.partition_size(step.args)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -175,12 +208,12 @@ def main(argv=None):
                    "seq_lens": (f"U[{cfg.len_range[0]},{cfg.len_range[1]}]" if cfg.len_range
                                 else "fixed"),
                    "total_tokens": int(np.sum(wl.seq_lens)), "pool_blocks": wl.num_blocks,
-                   "partition_size": args.partition_size or 512, "cow_copies": len(step.copies)},
+                   "partition_size": partition, "cow_copies": len(step.copies)},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_layers_per_s": round(cfg.B / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": nbytes,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
-        "roofline": {"kernel": "decode_partition_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": nbytes, "avg_launch_ms": round(part_ms, 5)},
     }

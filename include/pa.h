@@ -91,7 +91,7 @@ typedef struct pa_decode_args {
   float k_scale, v_scale;      /* fp8 dequantisation scales; must be 1 otherwise      */
   pa_dtype q_dtype, kv_dtype, out_dtype;
   int32_t partition_size;      /* tokens per split-K partition, a multiple of         */
-                               /* block_size; 0 = library default (512)               */
+                               /* block_size; 0 = library default (below)             */
   void* workspace;             /* device scratch for split-K partials                 */
   size_t workspace_bytes;      /* >= pa_decode_workspace_size(args)                   */
 } pa_decode_args;
@@ -101,10 +101,21 @@ typedef struct pa_decode_args {
  *   (q, kv) in {(F32,F32), (F16,F16), (BF16,BF16), (BF16,FP8_E4M3),
  *   (F16,FP8_E4M3)}; out_dtype = q_dtype or PA_F32. */
 
-/* Bytes of workspace pa_decode needs: 4*B*Hq*P*(D+2) with
+/* Default partition size (partition_size == 0): the largest of 1024 and 512
+ * tokens for which B * Hkv * ceil(max_blocks_per_seq*block_size / size) is at
+ * least 8192, else 256.  It depends only on these host-side sizes, never on
+ * the device contents.
+ *
+ * Bytes of workspace pa_decode needs: 4*B*Hq*P*(D+2) with
  * P = ceil(max_blocks_per_seq*block_size / partition_size), or 0 when one
- * partition covers every sequence.  Returns 0 for invalid arguments. */
+ * partition covers every sequence.  P may not exceed 65535.  Returns 0 for
+ * invalid arguments. */
 size_t pa_decode_workspace_size(const pa_decode_args* a);
+
+/* Tokens per split-K partition pa_decode will use for these arguments
+ * (partition_size, or the default above when it is 0); 0 for invalid
+ * arguments.  Host only. */
+int32_t pa_decode_partition_size(const pa_decode_args* a);
 
 /* Validate decode arguments without touching the GPU. */
 pa_status pa_decode_check(const pa_decode_args* a);

@@ -9,7 +9,7 @@ Quantisation uses one fp32 scale per tensor: the stored code c means
 ``decode(c) * scale``.
 
 Written from that definition, not from any library's source.  Pinned in
-``tests/test_oracle_fp8.py``: all 256 codes against torch's
+``tests/test_oracle.py``: all 256 codes against torch's
 ``float8_e4m3fn`` conversion (a library routine), encode(decode(c)) == c,
 every midpoint between neighbours rounding to the even code, saturation and
 NaN handling.

@@ -10,7 +10,7 @@ Decoding is exact: every fp32, fp16 and bf16 value is a float64 value.
 Encoding (:func:`round_to_format`) is written from the definition of a binary
 floating-point format with ``p`` significand bits and minimum normal exponent
 ``emin``: scale by the quantum of the value's binade, round half to even, scale
-back.  Pinned in ``tests/test_oracle_numerics.py`` against NumPy's and torch's
+back.  Pinned in ``tests/test_oracle.py`` against NumPy's and torch's
 own casts (library routines) on sweeps that include every tie.
 """
 

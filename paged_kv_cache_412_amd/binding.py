@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     argp = ctypes.POINTER(DecodeArgs)
     L.pa_decode_workspace_size.argtypes = [argp]
     L.pa_decode_workspace_size.restype = ctypes.c_size_t
+    L.pa_decode_partition_size.argtypes = [argp]
+    L.pa_decode_partition_size.restype = ctypes.c_int32
     for name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce"):
         getattr(L, name).argtypes = [argp, vp]
         getattr(L, name).restype = ctypes.c_int
@@ -159,6 +161,11 @@ def decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale
 
 def workspace_size(args: DecodeArgs) -> int:
     return int(lib().pa_decode_workspace_size(ctypes.byref(args)))
+
+
+def partition_size(args: DecodeArgs) -> int:
+    """Tokens per split-K partition the library uses for ``args``."""
+    return int(lib().pa_decode_partition_size(ctypes.byref(args)))
 
 
 def alloc_workspace(args: DecodeArgs, device=None) -> torch.Tensor | None:

@@ -18,8 +18,34 @@
 
 namespace pa {
 
-// One work-group per (query head, sequence).
-__global__ __launch_bounds__(128) void decode_reduce_kernel(const DecodeParams p) {
+// Partitions whose weights one pass of the reduce stages in LDS.
+constexpr int kReduceChunk = 256;
+
+// Block-wide reduction (max or sum) of one value per thread; blockDim.x is a
+// multiple of 64 and at most 256.  Every thread receives the result.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float* lds4) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(v, off, 64);
+    v = MAX ? fmaxf(v, o) : v + o;
+  }
+  const int nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = lds4[0];
+  for (int w = 1; w < nw; ++w) v = MAX ? fmaxf(v, lds4[w]) : v + lds4[w];
+  return v;
+}
+
+// One work-group of D threads per (query head, sequence); thread d owns
+// output element d.  The partition weights 2^(m_p - M) are computed once per
+// partition and shared through LDS, so the per-element loop is one fused
+// multiply-add and one coalesced load per partition.
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p) {
+  __shared__ float w_lds[kReduceChunk];
+  __shared__ float red[4];
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int max_tokens = p.max_blocks_per_seq * p.block_size;
@@ -28,19 +54,41 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const DecodeParams p
   if (L <= p.partition_size) return;  // finished by the partition kernel
   const int n = (L + p.partition_size - 1) / p.partition_size;
   const size_t base = (static_cast<size_t>(b) * p.Hq + hq) * p.num_partitions;
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+
   float M = kMaxInit;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_m[base + i]);
+  for (int i = tid; i < n; i += nt) M = fmaxf(M, p.ws_m[base + i]);
+  M = block_reduce<true>(M, red);
   float Ls = 0.f;
-  for (int i = 0; i < n; ++i)
-    Ls = __builtin_fmaf(p.ws_l[base + i], fast_exp2(p.ws_m[base + i] - M), Ls);
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  for (int d = threadIdx.x; d < p.D; d += blockDim.x) {
-    float A = 0.f;
-    for (int i = 0; i < n; ++i)
-      A = __builtin_fmaf(p.ws_acc[(base + i) * p.D + d], fast_exp2(p.ws_m[base + i] - M), A);
-    store_out(p.out, (static_cast<size_t>(b) * p.Hq + hq) * p.D + d, Ls > 0.f ? A * inv : 0.f,
-              p.out_dtype);
+  for (int i = tid; i < n; i += nt) Ls += p.ws_l[base + i] * fast_exp2(p.ws_m[base + i] - M);
+  Ls = block_reduce<false>(Ls, red);
+
+  float A = 0.f;
+  const float* acc = p.ws_acc + base * p.D + tid;
+  for (int c0 = 0; c0 < n; c0 += kReduceChunk) {
+    const int cn = min(kReduceChunk, n - c0);
+    __syncthreads();
+    for (int i = tid; i < cn; i += nt) w_lds[i] = fast_exp2(p.ws_m[base + c0 + i] - M);
+    __syncthreads();
+    if (tid < p.D) {
+      int i = 0;
+      for (; i + 4 <= cn; i += 4) {
+        const float a0 = acc[static_cast<size_t>(c0 + i) * p.D];
+        const float a1 = acc[static_cast<size_t>(c0 + i + 1) * p.D];
+        const float a2 = acc[static_cast<size_t>(c0 + i + 2) * p.D];
+        const float a3 = acc[static_cast<size_t>(c0 + i + 3) * p.D];
+        A = __builtin_fmaf(a0, w_lds[i], A);
+        A = __builtin_fmaf(a1, w_lds[i + 1], A);
+        A = __builtin_fmaf(a2, w_lds[i + 2], A);
+        A = __builtin_fmaf(a3, w_lds[i + 3], A);
+      }
+      for (; i < cn; ++i) A = __builtin_fmaf(acc[static_cast<size_t>(c0 + i) * p.D], w_lds[i], A);
+    }
   }
+  if (tid < p.D)
+    store_out(p.out, (static_cast<size_t>(b) * p.Hq + hq) * p.D + tid, Ls > 0.f ? A / Ls : 0.f,
+              p.out_dtype);
 }
 
 hipError_t launch_decode_partition(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
@@ -52,7 +100,8 @@ hipError_t launch_decode_partition(const DecodeParams& p, pa_dtype q_dtype, pa_d
 
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(p.Hq, p.B);
-  hipLaunchKernelGGL(decode_reduce_kernel, grid, dim3(128), 0, stream, p);
+  const int threads = (p.D + 63) / 64 * 64;
+  hipLaunchKernelGGL(decode_reduce_kernel, grid, dim3(threads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -1,8 +1,8 @@
 // pa_decode_common.h -- pieces shared by the two decode-partition kernels
 // (the VALU kernel for small query groups and the MFMA kernel for grouped
-// query attention): the work-group -> (KV head, partition, sequence) mapping,
-// the per-wave block-id prefetch, and the cross-wave merge that finishes a
-// partition.
+// query attention): the work-group -> (KV heads, partition, sequence)
+// mapping, the per-wave block-id prefetch, the load pipeline, and the store
+// of a finished partition.
 //
 // Both kernels compute, for one KV head g of one sequence b and one split-K
 // partition of the sequence's blocks, the online-softmax state of the G query
@@ -12,6 +12,13 @@
 // V-weighted sum acc.  A partition covering the whole sequence writes
 // out = v_scale * acc / l directly; otherwise (m, l, v_scale * acc) go to the
 // workspace for the reduce kernel.
+//
+// Work decomposition.  One wave64 per (KV head, partition, sequence); a
+// work-group holds the waves of up to NW consecutive KV heads of the same
+// partition (NW = 4 for the VALU kernel, 8 for the MFMA kernel).  All waves of a work-group walk the same blocks in the same
+// order, and a token row of a block stores every KV head contiguously, so
+// together they read each block as one contiguous sweep (DRAM pages stay
+// open) rather than D-element slices scattered over many rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,11 +32,14 @@ namespace pa {
 // (never NaN) while a wave has seen no valid token; real scores are far above.
 constexpr float kMaxInit = -1.0e30f;
 
-// Grid: x = KV head (fastest), y = partition, z = sequence.  Work-groups are
-// dispatched in x order, so the work-groups running at one moment read the
-// rows of every KV head of the same blocks: each token row of a block is one
-// contiguous Hkv*D run of the pool, and reading it in one sweep keeps DRAM
-// pages open instead of touching D-element slices of many rows.
+// Waves per work-group for Hkv KV heads: the smallest power of two covering
+// them, at most max_nw.
+inline int heads_per_group(int hkv, int max_nw) {
+  int nw = 1;
+  while (nw < hkv && nw < max_nw) nw <<= 1;
+  return nw;
+}
+
 struct PartitionSpan {
   int L;        // sequence length, clamped to the table's capacity
   int jbeg;     // first logical block of the partition
@@ -54,61 +64,111 @@ __device__ __forceinline__ PartitionSpan partition_span(const DecodeParams& p, i
   return s;
 }
 
-// Number of the partition's blocks that wave `wave` of NW handles (blocks
-// jbeg + wave, jbeg + wave + NW, ...).
-template <int NW>
-__device__ __forceinline__ int wave_block_count(const PartitionSpan& s, int wave) {
-  const int n = s.jend - s.jbeg;
-  return n > wave ? (n - wave + NW - 1) / NW : 0;
+// Grid: x = group of NW KV heads (fastest), y = sequence, z = partition;
+// block = NW wave64s, wave w serving KV head x*NW + w.  With the partition
+// slowest, every sequence's first partitions (always full) are dispatched
+// before the later, shorter or empty ones, which then fill the tail.
+struct WaveTask {
+  int g, part, b;
+  bool idle;  // KV head beyond Hkv (last group) or partition past the end
+  PartitionSpan span;
+};
+
+template <int BS>
+__device__ __forceinline__ WaveTask wave_task(const DecodeParams& p) {
+  WaveTask t;
+  const int nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  t.g = blockIdx.x * nw + wave;
+  t.b = blockIdx.y;
+  t.part = blockIdx.z;
+  t.span = partition_span<BS>(p, t.b, t.part);
+  t.idle = t.g >= p.Hkv || t.span.skip;
+  return t;
 }
 
-// Block ids of up to 64 consecutive iterations of one wave, one per lane
-// (lane i: iteration base + i), fetched with one vector load; each iteration
-// then takes its id with v_readlane, so no scalar load sits on the path
-// between two blocks.  Lanes past `cnt` hold -1.
-template <int NW>
-__device__ __forceinline__ int prefetch_block_ids(const int32_t* table, const PartitionSpan& s,
-                                                  int wave, int base, int cnt, int lane) {
-  return lane < cnt ? table[s.jbeg + wave + (base + lane) * NW] : -1;
-}
-
-__device__ __forceinline__ int block_id_at(int ids, int i) {
-  return __builtin_amdgcn_readlane(ids, i);
-}
-
-// Cross-wave merge of the per-wave states held in LDS, then the partition's
-// output: out (single partition) or the workspace partials.  One thread per
-// (query head of the group, element).
-template <int G, int D, int NW>
-__device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p,
-                                                      const float (&sm_m)[NW][G],
-                                                      const float (&sm_l)[NW][G],
-                                                      const float (&sm_acc)[NW][G][D], int b,
-                                                      int g, int part, bool single) {
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float M = kMaxInit;
+// Walk blocks jbeg..jend-1 of a partition with ST register sets in rotation:
+// the loads of the next ST-1 blocks are in flight while a block is consumed.
+// Block ids come 64 at a time, one per lane, from a single vector load, and
+// each iteration takes its id with v_readlane, so no scalar load sits between
+// two blocks.  `load(blk, buf)` issues the loads of block id blk into buf and
+// returns false (nothing loaded) for an id outside the pool; `consume(j, buf)`
+// folds logical block j into the running state.
+template <int ST, typename Buf, typename Load, typename Consume>
+__device__ __forceinline__ void walk_blocks(const int32_t* table, const PartitionSpan& s, int lane,
+                                            Load&& load, Consume&& consume) {
+  for (int base = s.jbeg; base < s.jend; base += 64) {
+    const int cnt = min(64, s.jend - base);
+    const int ids = lane < cnt ? table[base + lane] : -1;
+    Buf buf[ST];
+    bool ok[ST];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-    float Ls = 0.f, A = 0.f;
+    for (int u = 0; u < ST; ++u) ok[u] = false;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float a = fast_exp2(sm_m[w][h] - M);
-      Ls = __builtin_fmaf(sm_l[w][h], a, Ls);
-      A = __builtin_fmaf(sm_acc[w][h][d], a, A);
-    }
-    const size_t hq = static_cast<size_t>(b) * p.Hq + g * G + h;
-    if (single) {
-      const float o = Ls > 0.f ? (A / Ls) * p.v_scale : 0.f;
-      store_out(p.out, hq * D + d, o, p.out_dtype);
-    } else {
-      const size_t pi = hq * p.num_partitions + part;
-      p.ws_acc[pi * D + d] = A * p.v_scale;
-      if (d == 0) {
-        p.ws_m[pi] = M;
-        p.ws_l[pi] = Ls;
+    for (int u = 0; u < ST - 1; ++u) ok[u] = u < cnt && load(__builtin_amdgcn_readlane(ids, u), buf[u]);
+    for (int i = 0; i < cnt; i += ST) {
+#pragma unroll
+      for (int u = 0; u < ST; ++u) {
+        const int ii = i + u;
+        if (ii >= cnt) break;
+        const int nx = ii + ST - 1;
+        const int slot = (u + ST - 1) % ST;
+        if (nx < cnt) ok[slot] = load(__builtin_amdgcn_readlane(ids, nx), buf[slot]);
+        if (ok[u]) consume(base + ii, buf[u]);
       }
+    }
+  }
+}
+
+// Store N consecutive output elements (out_dtype F32, F16 or BF16) starting at
+// element i; i is a multiple of N, N*elem a multiple of 4 bytes.
+template <int N>
+__device__ __forceinline__ void store_out_n(void* base, size_t i, const float* v, int out_dtype) {
+  if (out_dtype == PA_F32) {
+    float* o = static_cast<float*>(base) + i;
+#pragma unroll
+    for (int k = 0; k < N; ++k) o[k] = v[k];
+  } else {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+      uint32_t lo, hi;
+      if (out_dtype == PA_F16) {
+        lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * k]));
+        hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * k + 1]));
+      } else {
+        lo = f32_to_bf16_rne(v[2 * k]);
+        hi = f32_to_bf16_rne(v[2 * k + 1]);
+      }
+      w[k] = lo | (hi << 16);
+    }
+    uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + i);
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) o[k] = w[k];
+  }
+}
+
+// Finish N elements [d0, d0+N) of query head h (of the group of KV head g)
+// for one partition: out (single partition) or the workspace partials.
+// m, l: the head's final running max and sum; acc: its unnormalised sums.
+template <int N>
+__device__ __forceinline__ void store_partition(const DecodeParams& p, int b, int g, int G, int h,
+                                                int part, bool single, int d0, float m, float l,
+                                                const float* acc) {
+  const size_t hq = static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G + h;
+  float v[N];
+  if (single) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = l > 0.f ? (acc[k] / l) * p.v_scale : 0.f;
+    store_out_n<N>(p.out, hq * p.D + d0, v, p.out_dtype);
+  } else {
+    const size_t pi = hq * p.num_partitions + part;
+    float* o = p.ws_acc + pi * p.D + d0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) o[k] = acc[k] * p.v_scale;
+    if (d0 == 0) {
+      p.ws_m[pi] = m;
+      p.ws_l[pi] = l;
     }
   }
 }

@@ -130,8 +130,11 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int sel)
   return sel ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
 }
 
-template <int KV, int Q, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams p) {
+// KV heads (waves) per work-group
+constexpr int kMfmaHeads = 8;
+
+template <int KV, int Q, int D, int BS, int G, int ST>
+__global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const DecodeParams p) {
   using M = Mfma<Q>;
   constexpr bool FP8 = KV == PA_FP8_E4M3;
   constexpr int KVB = FP8 ? 1 : 2;
@@ -147,18 +150,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BS % 16 == 0, "block size");
 
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_acc[NW][G][D];
-
-  const int g = blockIdx.x;
-  const int part = blockIdx.y;
-  const int b = blockIdx.z;
-  const PartitionSpan span = partition_span<BS>(p, b, part);
-  if (span.skip) return;
+  const WaveTask task = wave_task<BS>(p);
+  if (task.idle) return;
+  const int g = task.g, b = task.b;
+  const PartitionSpan& span = task.span;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lo = lane & 15;
   const int grp = lane >> 4;
 
@@ -207,7 +204,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     uint32_t v[TT][4][VR];
   };
 
-  auto load_block = [&](int blk, Raw& r) -> bool {
+  auto load = [&](int blk, Raw& r) -> bool {
     if (static_cast<unsigned>(blk) >= static_cast<unsigned>(p.num_blocks)) return false;
     const char* kp = kbase + static_cast<size_t>(blk) * blk_stride;
     const char* vp = vbase + static_cast<size_t>(blk) * blk_stride;
@@ -316,52 +313,38 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     }
   };
 
-  const int nmine = wave_block_count<NW>(span, wave);
-  for (int base = 0; base < nmine; base += 64) {
-    const int cnt = min(64, nmine - base);
-    const int ids = prefetch_block_ids<NW>(table, span, wave, base, cnt, lane);
-    const int j0 = span.jbeg + wave + base * NW;
-    Raw ra, rb;
-    bool oka = load_block(block_id_at(ids, 0), ra);
-    bool okb = false;
-    for (int i = 0; i < cnt; i += 2) {
-      if (i + 1 < cnt) okb = load_block(block_id_at(ids, i + 1), rb);
-      if (oka) consume(j0 + i * NW, ra);
-      if (i + 1 >= cnt) break;
-      if (i + 2 < cnt) oka = load_block(block_id_at(ids, i + 2), ra);
-      if (okb) consume(j0 + (i + 1) * NW, rb);
-    }
-  }
+  walk_blocks<ST, Raw>(table, span, lane, load, consume);
 
+  // l of query lo summed over the four lane groups; every lane then fetches
+  // m and l of the queries whose accumulators it holds (4*grp + i)
   float lt = l_part + __shfl_xor(l_part, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
-  if (grp == 0 && lo < G) {
-    sm_m[wave][lo] = m_run;
-    sm_l[wave][lo] = lt;
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = 4 * grp + i;
+    const float lq = __shfl(lt, q, 64);
+    const float mq = __shfl(m_run, q, 64);
     if (q < G) {
+      float o[EPL];
 #pragma unroll
-      for (int mm = 0; mm < EPL; ++mm) sm_acc[wave][q][EPL * lo + mm] = O[mm][i];
+      for (int mm = 0; mm < EPL; ++mm) o[mm] = O[mm][i];
+      store_partition<EPL>(p, b, g, G, q, task.part, span.single, EPL * lo, mq, lq, o);
     }
   }
-  __syncthreads();
-  merge_waves_and_store<G, D, NW>(p, sm_m, sm_l, sm_acc, b, g, part, span.single);
 }
 
 // ------------------------------------------------------------------ dispatch
 
 namespace {
 
-constexpr int kWaves = 4;
+// register sets in the load pipeline (blocks in flight per wave, plus one)
+constexpr int kStages = 2;
 
 template <int KV, int Q, int D, int BS, int G>
 hipError_t launch(const DecodeParams& p, hipStream_t s) {
-  dim3 grid(p.Hkv, p.num_partitions, p.B);
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, D, BS, G, kWaves>), grid, dim3(kWaves * 64), 0, s,
-                     p);
+  const int nw = heads_per_group(p.Hkv, kMfmaHeads);
+  dim3 grid((p.Hkv + nw - 1) / nw, p.B, p.num_partitions);
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, D, BS, G, kStages>), grid, dim3(nw * 64), 0, s, p);
   return hipGetLastError();
 }
 

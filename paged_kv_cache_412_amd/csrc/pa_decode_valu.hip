@@ -12,8 +12,8 @@
 //     served by one work-group, so each K/V block is read once for all of
 //     them (P1 "İlgili Teknikler").
 //
-// Work decomposition.  One work-group of NW wave64s per (KV head g,
-// partition, sequence).  Waves take the partition's blocks round-robin.
+// Work decomposition.  One wave64 per (KV head g, partition, sequence),
+// grouped into work-groups of consecutive KV heads (see pa_decode_common.h).
 // Inside a wave, a K/V row of D elements is split into 16-byte chunks: LPT =
 // D*elem/16 lanes cover one token row, so one wave load instruction covers
 // TPL = 64/LPT token rows as whole contiguous row segments, and each lane owns
@@ -22,9 +22,8 @@
 // lane), so every lane holds the scores of its own rows.  Each lane keeps an
 // online-softmax state (m, l, acc[G][chunk]) over its own rows; no cross-lane
 // exchange happens inside the block loop.  The loads of a wave's next block
-// are issued before the current block is consumed, so two blocks of K and V
-// are in flight per wave.  At the end the per-lane states are merged across
-// the TPL row groups (shuffles) and across waves (LDS).  Scores are kept in
+// are issued before the current block is consumed.  At the end the per-lane
+// states are merged across the TPL row groups with shuffles.  Scores are kept in
 // log2 units (scale * k_scale * log2 e folded in) so the exponentials are
 // single v_exp_f32 instructions.
 
@@ -167,8 +166,11 @@ struct Ops<PA_FP8_E4M3, PA_F16> : OpsE4M3<PA_F16> {};
 
 // ------------------------------------------------------------------ kernel
 
-template <int KV, int Q, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams p) {
+// KV heads (waves) per work-group
+constexpr int kValuHeads = 4;
+
+template <int KV, int Q, int D, int BS, int G, int ST>
+__global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const DecodeParams p) {
   using O = Ops<KV, Q>;
   constexpr int CE = O::CE;
   constexpr int KVB = Elem<KV>::bytes;
@@ -178,18 +180,12 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   constexpr int NL = BS / TPL;   // rows per lane per block
   static_assert(D % CE == 0 && 64 % LPT == 0 && BS % TPL == 0, "unsupported tile shape");
 
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_acc[NW][G][D];
-
-  const int g = blockIdx.x;
-  const int part = blockIdx.y;
-  const int b = blockIdx.z;
-  const PartitionSpan span = partition_span<BS>(p, b, part);
-  if (span.skip) return;
+  const WaveTask task = wave_task<BS>(p);
+  if (task.idle) return;
+  const int g = task.g, b = task.b;
+  const PartitionSpan& span = task.span;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane % LPT;   // chunk of the row this lane owns
   const int tg = lane / LPT;  // row within a wave load
 
@@ -218,32 +214,33 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
   const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const float qk = p.qk_scale_log2;
 
-  // Issue the K and V loads of the block with id `blk`; false (nothing
-  // loaded) for an id outside the pool.
-  auto load_block = [&](int blk, Chunk (&kc)[NL], Chunk (&vc)[NL]) -> bool {
+  struct Buf {
+    Chunk k[NL], v[NL];
+  };
+
+  auto load = [&](int blk, Buf& r) -> bool {
     if (static_cast<unsigned>(blk) >= static_cast<unsigned>(p.num_blocks)) return false;
     const char* kp = kbase + static_cast<size_t>(blk) * blk_stride;
     const char* vp = vbase + static_cast<size_t>(blk) * blk_stride;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kc[i] = load_chunk(kp + i * TPL * row_stride);
+    for (int i = 0; i < NL; ++i) r.k[i] = load_chunk(kp + i * TPL * row_stride);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vc[i] = load_chunk(vp + i * TPL * row_stride);
+    for (int i = 0; i < NL; ++i) r.v[i] = load_chunk(vp + i * TPL * row_stride);
     return true;
   };
 
-  // Fold logical block j (its rows already loaded) into the running state.
-  auto consume = [&](int j, const Chunk (&kc)[NL], const Chunk (&vc)[NL]) {
+  auto consume = [&](int j, const Buf& r) {
     // valid rows of this block (only the last block of a sequence is partial)
     const int valid = min(BS, span.L - j * BS);
     float s[NL][G];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[i][h] = group_sum<LPT>(O::dot(qr[h], kc[i])) * qk;
+      for (int h = 0; h < G; ++h) s[i][h] = group_sum<LPT>(O::dot(qr[h], r.k[i])) * qk;
     }
     float vf[NL][CE];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) O::to_f32(vc[i], vf[i]);
+    for (int i = 0; i < NL; ++i) O::to_f32(r.v[i], vf[i]);
     if (valid < BS) {
       // rows past the end are excluded outright: their K and V may hold
       // anything (NaN included), so they get weight 0 and a zeroed V row.
@@ -278,26 +275,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
     }
   };
 
-  // Two register sets in ping-pong: the loads of iteration i+1 are in flight
-  // while iteration i is consumed.
-  const int nmine = wave_block_count<NW>(span, wave);
-  for (int base = 0; base < nmine; base += 64) {
-    const int cnt = min(64, nmine - base);
-    const int ids = prefetch_block_ids<NW>(table, span, wave, base, cnt, lane);
-    const int j0 = span.jbeg + wave + base * NW;
-    Chunk ka[NL], va[NL], kb[NL], vb[NL];
-    bool oka = load_block(block_id_at(ids, 0), ka, va);
-    bool okb = false;
-    for (int i = 0; i < cnt; i += 2) {
-      if (i + 1 < cnt) okb = load_block(block_id_at(ids, i + 1), kb, vb);
-      if (oka) consume(j0 + i * NW, ka, va);
-      if (i + 1 >= cnt) break;
-      if (i + 2 < cnt) oka = load_block(block_id_at(ids, i + 2), ka, va);
-      if (okb) consume(j0 + (i + 1) * NW, kb, vb);
-    }
-  }
+  walk_blocks<ST, Buf>(table, span, lane, load, consume);
 
-  // merge the per-lane states of the TPL row groups that own the same chunk
+  // merge the per-lane states of the TPL row groups that own the same chunk;
+  // the butterfly leaves the merged state in every lane
 #pragma unroll
   for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
@@ -316,30 +297,25 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(const DecodeParams
 
   if (tg == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < CE; ++e) sm_acc[wave][h][c * CE + e] = acc[h][e];
-      if (c == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
-      }
-    }
+    for (int h = 0; h < G; ++h)
+      store_partition<CE>(p, b, g, G, h, task.part, span.single, c * CE, m[h], l[h], acc[h]);
   }
-  __syncthreads();
-  merge_waves_and_store<G, D, NW>(p, sm_m, sm_l, sm_acc, b, g, part, span.single);
 }
 
 // ------------------------------------------------------------------ dispatch
 
 namespace {
 
-constexpr int kWaves = 4;
+// register sets in the load pipeline (blocks in flight per wave, plus one);
+// fp32 caches take one, their rows already fill the register file
+template <int KV>
+constexpr int kStages = KV == PA_F32 ? 1 : 2;
 
 template <int KV, int Q, int D, int BS, int G>
 hipError_t launch(const DecodeParams& p, hipStream_t s) {
-  dim3 grid(p.Hkv, p.num_partitions, p.B);
-  hipLaunchKernelGGL((decode_valu_kernel<KV, Q, D, BS, G, kWaves>), grid, dim3(kWaves * 64), 0, s,
-                     p);
+  const int nw = heads_per_group(p.Hkv, kValuHeads);
+  dim3 grid((p.Hkv + nw - 1) / nw, p.B, p.num_partitions);
+  hipLaunchKernelGGL((decode_valu_kernel<KV, Q, D, BS, G, kStages<KV>>), grid, dim3(nw * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -29,8 +29,9 @@ struct DecodeParams {
   int32_t out_dtype;
 };
 
-// Default tokens per split-K partition.
-constexpr int32_t kDefaultPartition = 512;
+// Waves the default split-K partition size aims for (a few rounds of the
+// 256 compute units of a gfx950 part).
+constexpr int64_t kTargetWaves = 8192;
 
 // Grid limit on the partition axis (grid y).
 constexpr int32_t kMaxPartitions = 65535;

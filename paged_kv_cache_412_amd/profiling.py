@@ -1,0 +1,208 @@
+"""rocprofv3 runs of bench.py and the summaries kept under ``profiles/``.
+
+Three steps, run from the repository root:
+
+``python -m paged_kv_cache_412_amd.profiling trace --workload W --out DIR``
+    (GPU) ``rocprofv3 --kernel-trace --stats -f csv`` around a short bench.py
+    run of workload W.
+``python -m paged_kv_cache_412_amd.profiling pmc --workload W --out DIR``
+    (GPU) four ``rocprofv3 --pmc`` passes, one counter each: FETCH_SIZE and
+    WRITE_SIZE around the same bench.py run, and around
+    ``bench.py --copy-calibration`` (a plain 1 GiB device copy).
+``python -m paged_kv_cache_412_amd.profiling summarize --workload W --dir DIR``
+    (any machine) reads those CSVs and writes
+    ``profiles/<kernel>_<workload>.md`` (per-kernel durations; HBM bytes per
+    launch when the PMC passes are there) and
+    ``profiles/traffic_<kernel>_<workload>.json`` (what bench.py reports as
+    ``roofline.traffic`` while the kernel sources are unchanged).
+
+FETCH_SIZE and WRITE_SIZE count KiB per dispatch.  Each is scaled by the
+factor that makes it read exactly 1 GiB for the calibration copy, so the
+figure is in bytes of HBM traffic as a plain copy would count them.
+Every rocprofv3 call runs as a child process with the program itself after
+``--`` and a hard time limit.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+ROCPROF = "rocprofv3"
+STEPS, WARMUP = 10, 3
+PMC_STEPS, PMC_WARMUP = 3, 1
+
+
+def _bench_cmd(workload: str, steps: int, warmup: int, extra=()) -> list:
+    return [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--steps",
+            str(steps), "--warmup", str(warmup), "--no-cpu-baseline", *extra]
+
+
+def _run(cmd: list, limit: int) -> None:
+    print("[profiling] " + " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, timeout=limit)
+    if r.returncode != 0:
+        raise SystemExit(f"command failed with status {r.returncode}")
+
+
+def trace(workload: str, out: str) -> None:
+    cmd = [ROCPROF, "--kernel-trace", "--stats", "-f", "csv", "-d", out, "-o", f"trace_{workload}",
+           "--", *_bench_cmd(workload, STEPS, WARMUP)]
+    _run(cmd, 300)
+
+
+def pmc(workload: str, out: str) -> None:
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        _run([ROCPROF, "--pmc", counter, "-f", "csv", "-d", out, "-o", f"pmc_{counter}_{workload}",
+              "--", *_bench_cmd(workload, PMC_STEPS, PMC_WARMUP)], 180)
+        _run([ROCPROF, "--pmc", counter, "-f", "csv", "-d", out, "-o", f"pmc_{counter}_calibration",
+              "--", *_bench_cmd(workload, 1, 0, ("--copy-calibration",))], 180)
+
+
+def _find(d: str, pattern: str):
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    return hits[-1] if hits else None
+
+
+def _counter_per_dispatch(path: str, counter: str) -> dict:
+    """kernel name -> list of counter values, one per dispatch (summed over
+    the counter's instances within a dispatch)."""
+    per = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            key = (row["Kernel_Name"], row.get("Dispatch_Id") or row.get("Correlation_Id"))
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize(workload: str, d: str) -> None:
+    sys.path.insert(0, ROOT)
+    import bench  # noqa: E402  (kernel naming and source hash)
+    from paged_kv_cache_412_amd import workloads
+
+    cfg = workloads.CONFIGS[workload]
+    kernel = bench.decode_kernel_name(cfg)
+    stats = _find(d, f"trace_{workload}_kernel_stats.csv")
+    if stats is None:
+        raise SystemExit(f"no kernel stats for {workload} under {d}")
+    with open(stats, newline="") as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"# {kernel} -- {workload}", "",
+             "Kernel durations from `rocprofv3 --kernel-trace --stats` around a short bench.py run.",
+             "", "Commands (repository root, MI355X):", "", "```",
+             f"python -m paged_kv_cache_412_amd.profiling trace --workload {workload} --out gpurun_out/prof",
+             "  # = " + " ".join([ROCPROF, "--kernel-trace", "--stats", "-f", "csv", "-d", "gpurun_out/prof",
+                                   "-o", f"trace_{workload}", "--", "python3", "bench.py", "--workload",
+                                   workload, "--steps", str(STEPS), "--warmup", str(WARMUP),
+                                   "--no-cpu-baseline"]),
+             f"python -m paged_kv_cache_412_amd.profiling summarize --workload {workload} --dir gpurun_out/prof",
+             "```", "", "| kernel | calls | average us | total us | % |", "|---|---|---|---|---|"]
+    avg_us = None
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = _short(r["Name"])
+        if not name.startswith("pa::"):
+            continue
+        a = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{name}` | {r['Calls']} | {a:.2f} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+        if name.startswith(f"pa::{kernel}") and avg_us is None:
+            avg_us = a
+    kvb = bench_kv_bytes(cfg)
+    if avg_us:
+        lines += ["", f"Algorithmic KV bytes per launch: {kvb} (valid tokens' K and V); at the "
+                      f"average duration of `{kernel}` that is {kvb / (avg_us * 1e-6) / 1e9:.1f} GB/s, "
+                      f"{100 * kvb / (avg_us * 1e-6) / 8e12:.1f} % of 8 TB/s."]
+    rec = {"kernel": kernel, "workload": workload, "kernel_hash": bench.kernel_hash(),
+           "avg_launch_us": avg_us, "algorithmic_bytes": kvb}
+    fetch = _find(d, f"pmc_FETCH_SIZE_{workload}_counter_collection.csv")
+    write = _find(d, f"pmc_WRITE_SIZE_{workload}_counter_collection.csv")
+    cfetch = _find(d, "pmc_FETCH_SIZE_calibration_counter_collection.csv")
+    cwrite = _find(d, "pmc_WRITE_SIZE_calibration_counter_collection.csv")
+    if fetch and write and cfetch and cwrite:
+        def kernel_avg(path, counter):
+            vals = [v for n, vs in _counter_per_dispatch(path, counter).items() if kernel in n
+                    for v in vs]
+            return sum(vals) / len(vals), len(vals)
+
+        def calib(path, counter):
+            per = _counter_per_dispatch(path, counter)
+            name, vals = max(per.items(), key=lambda kv: max(kv[1]))
+            return max(vals), _short(name)
+
+        f_kib, nf = kernel_avg(fetch, "FETCH_SIZE")
+        w_kib, nw = kernel_avg(write, "WRITE_SIZE")
+        cf_kib, cname = calib(cfetch, "FETCH_SIZE")
+        cw_kib, _ = calib(cwrite, "WRITE_SIZE")
+        ref = bench.CALIBRATION_BYTES
+        kf, kw = ref / (cf_kib * 1024), ref / (cw_kib * 1024)
+        hbm = f_kib * 1024 * kf + w_kib * 1024 * kw
+        rec.update({"fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+                    "calibration_kernel": cname, "calibration_fetch_kib": cf_kib,
+                    "calibration_write_kib": cw_kib, "fetch_factor": kf, "write_factor": kw,
+                    "hbm_bytes_per_launch": hbm, "dispatches": [nf, nw]})
+        lines += ["", "## HBM traffic (rocprofv3 --pmc, one counter per pass)", "", "```",
+                  f"python -m paged_kv_cache_412_amd.profiling pmc --workload {workload} --out gpurun_out/prof",
+                  "  # = rocprofv3 --pmc FETCH_SIZE -f csv ... -- python3 bench.py --workload "
+                  f"{workload} --steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline",
+                  "  #   rocprofv3 --pmc FETCH_SIZE -f csv ... -- python3 bench.py --copy-calibration",
+                  "  #   and the same two with WRITE_SIZE", "```", "",
+                  "| quantity | value |", "|---|---|",
+                  f"| FETCH_SIZE per `{kernel}` dispatch (KiB, mean of {nf}) | {f_kib:.0f} |",
+                  f"| WRITE_SIZE per dispatch (KiB, mean of {nw}) | {w_kib:.0f} |",
+                  f"| calibration: 1 GiB copy (`{cname}`) FETCH / WRITE (KiB) | {cf_kib:.0f} / {cw_kib:.0f} |",
+                  f"| scale factors fetch / write | {kf:.4f} / {kw:.4f} |",
+                  f"| HBM bytes per launch (scaled) | {hbm:.4g} |",
+                  f"| algorithmic KV bytes per launch | {kvb:.4g} |",
+                  f"| traffic / algorithmic | {hbm / kvb:.3f} |"]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"{kernel}_{workload}.md"), "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json"), "w", encoding="utf-8") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print("\n".join(lines))
+
+
+def bench_kv_bytes(cfg) -> int:
+    """Valid tokens' K and V bytes of the workload (its seeded lengths, no GPU)."""
+    import numpy as np
+
+    from paged_kv_cache_412_amd import workloads
+    lens = workloads.seq_lengths(cfg)
+    return int(np.sum(lens)) * 2 * cfg.Hkv * cfg.D * workloads.ELEM_BYTES[cfg.kv_dtype]
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("step", choices=["trace", "pmc", "summarize"])
+    ap.add_argument("--workload", default="llama13b")
+    ap.add_argument("--out", default="gpurun_out/prof")
+    ap.add_argument("--dir", default="gpurun_out/prof")
+    a = ap.parse_args(argv)
+    if a.step == "trace":
+        trace(a.workload, a.out)
+    elif a.step == "pmc":
+        pmc(a.workload, a.out)
+    else:
+        summarize(a.workload, a.dir)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -166,6 +166,17 @@ def _lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
     return rng.integers(lo, hi, size=cfg.B, endpoint=True).astype(np.int64)
 
 
+def seq_lengths(cfg: Config) -> np.ndarray:
+    """The lengths (new token included) ``make`` gives the sequences of
+    ``cfg``: the first draws of the config's generator."""
+    rng = np.random.default_rng(cfg.seed)
+    if cfg.shared:
+        sh = cfg.shared
+        stems = rng.integers(sh["stem"][0], sh["stem"][1], size=sh["prompts"], endpoint=True)
+        return np.repeat(sh["prefix"] + stems.astype(np.int64) + 1, sh["samples"])
+    return _lengths(cfg, rng)
+
+
 def make(cfg: Config, device="cpu", poison: bool = True, q_sigma: float = 1.0) -> Workload:
     """Build the seeded pre-step state of ``cfg`` on ``device``."""
     if cfg.shared:

@@ -21,6 +21,7 @@ def L():
 def test_header_declares_the_path_entry_points():
     names = set(binding.declared_functions())
     for n in ("pa_decode", "pa_decode_partition", "pa_decode_reduce", "pa_decode_workspace_size",
+              "pa_decode_partition_size",
               "pa_decode_check", "pa_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
               "pa_status_str", "pa_abi_version"):
         assert n in names
@@ -85,11 +86,32 @@ def test_decode_check_rejects(L, kw, status):
 
 
 def test_workspace_size_formula(L):
-    a = valid_args(max_blocks_per_seq=64)                    # 1024 tokens -> 2 partitions
+    a = valid_args(max_blocks_per_seq=64, partition_size=512)   # 1024 tokens -> 2 partitions
     assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 2 * (64 + 2)
     a = valid_args(max_blocks_per_seq=64, partition_size=256)   # 4 partitions
     assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 4 * (64 + 2)
-    assert L.pa_decode_workspace_size(ctypes.byref(valid_args())) == 0   # one partition
+    a = valid_args(max_blocks_per_seq=64)       # small batch: the default falls to 256 tokens
+    assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 4 * (64 + 2)
+    a = valid_args(max_blocks_per_seq=15)       # 240 tokens fit one default partition
+    assert L.pa_decode_workspace_size(ctypes.byref(a)) == 0
+
+
+@pytest.mark.parametrize("B,Hkv,bs,max_blocks,part", [
+    (256, 8, 16, 256, 1024),     # 70B-shaped layer: 2048 rows x 4 partitions
+    (64, 40, 16, 128, 512),      # 13B-shaped layer: 2560 rows x 2 partitions is too few
+    (16, 8, 16, 2048, 512),      # long context: 128 rows x 64 partitions
+    (16, 8, 32, 1024, 512),
+    (1, 1, 16, 64, 256),         # tiny: nothing reaches the target
+])
+def test_default_partition_choice(L, B, Hkv, bs, max_blocks, part):
+    a = valid_args(B=B, Hq=Hkv, Hkv=Hkv, D=128, block_size=bs, max_blocks_per_seq=max_blocks)
+    P = -(-(max_blocks * bs) // part)
+    want = 0 if P == 1 else 4 * B * Hkv * P * (128 + 2)
+    assert L.pa_decode_workspace_size(ctypes.byref(a)) == want
+    assert L.pa_decode_partition_size(ctypes.byref(a)) == part
+    a.partition_size = 64
+    assert L.pa_decode_partition_size(ctypes.byref(a)) == 64
+    assert L.pa_decode_partition_size(ctypes.byref(valid_args(Hq=6, Hkv=4))) == 0
     assert L.pa_decode_workspace_size(ctypes.byref(valid_args(Hq=6, Hkv=4))) == 0
     assert L.pa_decode_workspace_size(None) == 0
 
