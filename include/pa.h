@@ -102,9 +102,9 @@ typedef struct pa_decode_args {
  *   (F16,FP8_E4M3)}; out_dtype = q_dtype or PA_F32. */
 
 /* Default partition size (partition_size == 0): the largest of 1024 and 512
- * tokens for which B * Hkv * ceil(max_blocks_per_seq*block_size / size) is at
- * least 8192, else 256.  It depends only on these host-side sizes, never on
- * the device contents.
+ * tokens for which n = ceil(max_blocks_per_seq*block_size / size) is at least
+ * 4 and B * Hkv * n at least 4096, else 256.  It depends only on these
+ * host-side sizes, never on the device contents.
  *
  * Bytes of workspace pa_decode needs: 4*B*Hq*P*(D+2) with
  * P = ceil(max_blocks_per_seq*block_size / partition_size), or 0 when one

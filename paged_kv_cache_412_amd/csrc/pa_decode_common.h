@@ -91,30 +91,35 @@ __device__ __forceinline__ WaveTask wave_task(const DecodeParams& p) {
 // the loads of the next ST-1 blocks are in flight while a block is consumed.
 // Block ids come 64 at a time, one per lane, from a single vector load, and
 // each iteration takes its id with v_readlane, so no scalar load sits between
-// two blocks.  `load(blk, buf)` issues the loads of block id blk into buf and
-// returns false (nothing loaded) for an id outside the pool; `consume(j, buf)`
-// folds logical block j into the running state.
+// two blocks.
+//
+// `load(blk, buf)` issues the loads of block id blk into buf, through a
+// buffer resource that is empty when blk < 0: ids outside the pool and the
+// look-ahead past the partition's end load nothing but still issue the same
+// instructions.  Every path through the loop therefore has the same loads in
+// flight, and the compiler's wait counts stay exact (a load issued on one path
+// only would force it to wait for all loads, the look-ahead included).
+// `consume(j, ok, buf)` folds logical block j into the running state; ok is
+// false for an id outside the pool, whose block then counts no valid token.
 template <int ST, typename Buf, typename Load, typename Consume>
-__device__ __forceinline__ void walk_blocks(const int32_t* table, const PartitionSpan& s, int lane,
-                                            Load&& load, Consume&& consume) {
+__device__ __forceinline__ void walk_blocks(const int32_t* table, const PartitionSpan& s,
+                                            int num_blocks, int lane, Load&& load,
+                                            Consume&& consume) {
   for (int base = s.jbeg; base < s.jend; base += 64) {
     const int cnt = min(64, s.jend - base);
-    const int ids = lane < cnt ? table[base + lane] : -1;
+    int ids = lane < cnt ? table[base + lane] : -1;
+    if (static_cast<unsigned>(ids) >= static_cast<unsigned>(num_blocks)) ids = -1;
     Buf buf[ST];
-    bool ok[ST];
 #pragma unroll
-    for (int u = 0; u < ST; ++u) ok[u] = false;
-#pragma unroll
-    for (int u = 0; u < ST - 1; ++u) ok[u] = u < cnt && load(__builtin_amdgcn_readlane(ids, u), buf[u]);
+    for (int u = 0; u < ST - 1; ++u) load(__builtin_amdgcn_readlane(ids, u), buf[u]);
     for (int i = 0; i < cnt; i += ST) {
 #pragma unroll
       for (int u = 0; u < ST; ++u) {
         const int ii = i + u;
         if (ii >= cnt) break;
         const int nx = ii + ST - 1;
-        const int slot = (u + ST - 1) % ST;
-        if (nx < cnt) ok[slot] = load(__builtin_amdgcn_readlane(ids, nx), buf[slot]);
-        if (ok[u]) consume(base + ii, buf[u]);
+        load(nx < 64 ? __builtin_amdgcn_readlane(ids, nx) : -1, buf[(u + ST - 1) % ST]);
+        consume(base + ii, __builtin_amdgcn_readlane(ids, ii) >= 0, buf[u]);
       }
     }
   }

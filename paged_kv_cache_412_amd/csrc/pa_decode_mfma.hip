@@ -107,24 +107,6 @@ struct Mfma<PA_F16> {
   }
 };
 
-// Non-temporal load of N dwords (N = 1, 2 or 4) at a 4N-byte aligned address.
-template <int N>
-__device__ __forceinline__ void load_dwords(const char* p, uint32_t* out) {
-  if constexpr (N == 4) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    out[0] = v[0];
-    out[1] = v[1];
-    out[2] = v[2];
-    out[3] = v[3];
-  } else if constexpr (N == 2) {
-    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-    out[0] = v[0];
-    out[1] = v[1];
-  } else {
-    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-  }
-}
-
 // Half `sel` (0 = low, 1 = high) of dwords a and b, packed as (a_half, b_half).
 __device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int sel) {
   return sel ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
@@ -187,15 +169,16 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   float m_run = kMaxInit;  // running max of query lo (log2 units), same in all four groups
   float l_part = 0.f;      // this lane's share of the running sum of query lo
 
-  const size_t row_stride = static_cast<size_t>(p.Hkv) * D * KVB;
-  const size_t blk_stride = row_stride * BS;
-  const size_t head_off = static_cast<size_t>(g) * D * KVB;
-  // K: token row lo of each tile; e4m3 lanes start at their contiguous run
-  const size_t k_off = head_off + lo * row_stride + (FP8 ? static_cast<size_t>(grp) * (D / 4) : 0);
+  const uint32_t row_stride = static_cast<uint32_t>(p.Hkv) * D * KVB;
+  const uint32_t blk_bytes = row_stride * BS;
+  const int head_off = g * D * KVB;
+  // K: token row lo of each tile; e4m3 lanes start at their contiguous run,
+  // 16-bit lanes at chunk grp (chunk 4s+grp is 64*s bytes further)
+  const int k_off = head_off + lo * row_stride + (FP8 ? grp * (D / 4) : grp * 16);
   // V: token rows 4*grp + e of each tile, elements [EPL*lo, EPL*lo + EPL)
-  const size_t v_off = head_off + (4 * grp) * row_stride + static_cast<size_t>(EPL * lo) * KVB;
-  const char* kbase = static_cast<const char*>(p.k_cache) + k_off;
-  const char* vbase = static_cast<const char*>(p.v_cache) + v_off;
+  const int v_off = head_off + 4 * grp * row_stride + EPL * lo * KVB;
+  const char* kpool = static_cast<const char*>(p.k_cache);
+  const char* vpool = static_cast<const char*>(p.v_cache);
   const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const float qk = p.qk_scale_log2;
 
@@ -204,32 +187,37 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
     uint32_t v[TT][4][VR];
   };
 
-  auto load = [&](int blk, Raw& r) -> bool {
-    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(p.num_blocks)) return false;
-    const char* kp = kbase + static_cast<size_t>(blk) * blk_stride;
-    const char* vp = vbase + static_cast<size_t>(blk) * blk_stride;
+  // Loads of block id blk (nothing is read for blk < 0).
+  auto load = [&](int blk, Raw& r) {
+    const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
+    const uint32_t n = blk < 0 ? 0u : blk_bytes;
+    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + off, n);
+    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + off, n);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      const char* kt = kp + static_cast<size_t>(tt) * 16 * row_stride;
+      const int ts = tt * 16 * row_stride;
       if constexpr (FP8) {
-#pragma unroll
-        for (int i = 0; i < KR; i += KLD) load_dwords<KLD>(kt + i * 4, &r.k[tt][i]);
+        buffer_load<KLD, 0>(kr, k_off, ts, &r.k[tt][0]);
+        if constexpr (KR > KLD) buffer_load<KLD, 16>(kr, k_off, ts, &r.k[tt][KLD]);
       } else {
-#pragma unroll
-        for (int s = 0; s < SS; ++s) load_dwords<4>(kt + chunk_of(s) * 16, &r.k[tt][4 * s]);
+        buffer_load<4, 0>(kr, k_off, ts, &r.k[tt][0]);
+        buffer_load<4, 64>(kr, k_off, ts, &r.k[tt][4]);
+        if constexpr (SS > 2) {
+          buffer_load<4, 128>(kr, k_off, ts, &r.k[tt][8]);
+          buffer_load<4, 192>(kr, k_off, ts, &r.k[tt][12]);
+        }
       }
     }
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        load_dwords<VR>(vp + (static_cast<size_t>(tt) * 16 + e) * row_stride, r.v[tt][e]);
+      for (int e = 0; e < 4; ++e) buffer_load<VR>(vr, v_off, (tt * 16 + e) * row_stride, r.v[tt][e]);
     }
-    return true;
   };
 
-  auto consume = [&](int j, Raw& r) {
-    const int valid = min(BS, span.L - j * BS);
+  auto consume = [&](int j, bool ok, Raw& r) {
+    // valid rows of this block; a block id outside the pool counts none
+    const int valid = ok ? min(BS, span.L - j * BS) : 0;
     float sc[TT][4];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -313,7 +301,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
     }
   };
 
-  walk_blocks<ST, Raw>(table, span, lane, load, consume);
+  walk_blocks<ST, Raw>(table, span, p.num_blocks, lane, load, consume);
 
   // l of query lo summed over the four lane groups; every lane then fetches
   // m and l of the queries whose accumulators it holds (4*grp + i)

@@ -206,11 +206,12 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
     for (int e = 0; e < CE; ++e) acc[h][e] = 0.f;
   }
 
-  const size_t row_stride = static_cast<size_t>(p.Hkv) * D * KVB;  // bytes between token rows
-  const size_t blk_stride = row_stride * BS;
-  const size_t lane_off = static_cast<size_t>(g) * D * KVB + c * 16 + tg * row_stride;
-  const char* kbase = static_cast<const char*>(p.k_cache) + lane_off;
-  const char* vbase = static_cast<const char*>(p.v_cache) + lane_off;
+  const uint32_t row_stride = static_cast<uint32_t>(p.Hkv) * D * KVB;  // bytes between token rows
+  const uint32_t blk_bytes = row_stride * BS;
+  // this lane's chunk of row tg of a block, relative to the block's start
+  const int lane_off = static_cast<int>(g * D * KVB + c * 16 + tg * row_stride);
+  const char* kpool = static_cast<const char*>(p.k_cache);
+  const char* vpool = static_cast<const char*>(p.v_cache);
   const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const float qk = p.qk_scale_log2;
 
@@ -218,20 +219,22 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
     Chunk k[NL], v[NL];
   };
 
-  auto load = [&](int blk, Buf& r) -> bool {
-    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(p.num_blocks)) return false;
-    const char* kp = kbase + static_cast<size_t>(blk) * blk_stride;
-    const char* vp = vbase + static_cast<size_t>(blk) * blk_stride;
+  // Loads of block id blk (nothing is read for blk < 0).
+  auto load = [&](int blk, Buf& r) {
+    const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
+    const uint32_t n = blk < 0 ? 0u : blk_bytes;
+    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + off, n);
+    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + off, n);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) r.k[i] = load_chunk(kp + i * TPL * row_stride);
+    for (int i = 0; i < NL; ++i) buffer_load<4>(kr, lane_off, i * TPL * row_stride, r.k[i].w);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) r.v[i] = load_chunk(vp + i * TPL * row_stride);
-    return true;
+    for (int i = 0; i < NL; ++i) buffer_load<4>(vr, lane_off, i * TPL * row_stride, r.v[i].w);
   };
 
-  auto consume = [&](int j, const Buf& r) {
-    // valid rows of this block (only the last block of a sequence is partial)
-    const int valid = min(BS, span.L - j * BS);
+  auto consume = [&](int j, bool ok, const Buf& r) {
+    // valid rows of this block (only the last block of a sequence is partial;
+    // a block id outside the pool counts none)
+    const int valid = ok ? min(BS, span.L - j * BS) : 0;
     float s[NL][G];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
     }
   };
 
-  walk_blocks<ST, Buf>(table, span, lane, load, consume);
+  walk_blocks<ST, Buf>(table, span, p.num_blocks, lane, load, consume);
 
   // merge the per-lane states of the TPL row groups that own the same chunk;
   // the butterfly leaves the merged state in every lane

@@ -36,6 +36,48 @@ __device__ __forceinline__ Chunk load_chunk(const void* p) {
   return c;
 }
 
+// ---------------------------------------------------------------- buffer loads
+
+// Buffer resource (V#) over `bytes` bytes at `base`: raw buffer loads through
+// it return zeros, without touching memory, for offsets at or past `bytes`.
+// A resource with bytes = 0 therefore turns every load of a block that must
+// not be read into a no-op, so the loop can issue the same loads on every path.
+// Dword 3 (0x00020000: 32-bit data format) is the raw-buffer setting for gfx9
+// parts, gfx950 included.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Cache-policy bits of a buffer load: non-temporal (the pools are read once
+// per decode step; L2 and the MALL are left to the block tables and queries).
+constexpr int kLoadNT = 2;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// N dwords (1, 2 or 4) at byte voff + soff + IMM of the resource.
+template <int N, int IMM = 0>
+__device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                            uint32_t* out) {
+  if constexpr (N == 4) {
+    const u32x4_t v = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff + IMM, soff, kLoadNT));
+    out[0] = v[0];
+    out[1] = v[1];
+    out[2] = v[2];
+    out[3] = v[3];
+  } else if constexpr (N == 2) {
+    const u32x2_t v = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff + IMM, soff, kLoadNT));
+    out[0] = v[0];
+    out[1] = v[1];
+  } else {
+    out[0] = __builtin_bit_cast(uint32_t,
+                                __builtin_amdgcn_raw_buffer_load_b32(r, voff + IMM, soff, kLoadNT));
+  }
+}
+
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 

@@ -29,9 +29,11 @@ struct DecodeParams {
   int32_t out_dtype;
 };
 
-// Waves the default split-K partition size aims for (a few rounds of the
-// 256 compute units of a gfx950 part).
-constexpr int64_t kTargetWaves = 8192;
+// The default split-K partition size aims for at least kTargetWaves waves (a
+// few rounds of the 256 compute units of a gfx950 part) and at least
+// kMinPartitions partitions of the longest sequence the table can hold.
+constexpr int64_t kTargetWaves = 4096;
+constexpr int64_t kMinPartitions = 4;
 
 // Grid limit on the partition axis (grid y).
 constexpr int32_t kMaxPartitions = 65535;

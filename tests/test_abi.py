@@ -98,9 +98,10 @@ def test_workspace_size_formula(L):
 
 @pytest.mark.parametrize("B,Hkv,bs,max_blocks,part", [
     (256, 8, 16, 256, 1024),     # 70B-shaped layer: 2048 rows x 4 partitions
-    (64, 40, 16, 128, 512),      # 13B-shaped layer: 2560 rows x 2 partitions is too few
-    (16, 8, 16, 2048, 512),      # long context: 128 rows x 64 partitions
-    (16, 8, 32, 1024, 512),
+    (64, 40, 16, 128, 512),      # 13B-shaped layer: 2 partitions of 1024 are too few
+    (16, 8, 16, 2048, 1024),     # long context: 128 rows x 32 partitions
+    (16, 8, 32, 1024, 1024),
+    (16, 8, 16, 1000, 512),      # 128 x 16 = 2048 waves at 1024 misses the target
     (1, 1, 16, 64, 256),         # tiny: nothing reaches the target
 ])
 def test_default_partition_choice(L, B, Hkv, bs, max_blocks, part):
