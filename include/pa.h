@@ -92,7 +92,9 @@ typedef struct pa_decode_args {
   pa_dtype q_dtype, kv_dtype, out_dtype;
   int32_t partition_size;      /* tokens per split-K partition, a multiple of         */
                                /* block_size; 0 = library default (below)             */
-  void* workspace;             /* device scratch for split-K partials                 */
+  void* workspace;             /* device scratch for split-K partials, 16-byte        */
+                               /* aligned: fp32 acc [P][B*Hq][D], then m and l        */
+                               /* [P][B*Hq] each                                      */
   size_t workspace_bytes;      /* >= pa_decode_workspace_size(args)                   */
 } pa_decode_args;
 

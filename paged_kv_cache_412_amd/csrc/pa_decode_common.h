@@ -1,24 +1,25 @@
 // pa_decode_common.h -- pieces shared by the two decode-partition kernels
 // (the VALU kernel for small query groups and the MFMA kernel for grouped
-// query attention): the work-group -> (KV heads, partition, sequence)
-// mapping, the per-wave block-id prefetch, the load pipeline, and the store
-// of a finished partition.
+// query attention): the work schedule, the per-wave block walk with its load
+// pipeline, and the store of a finished segment.
 //
-// Both kernels compute, for one KV head g of one sequence b and one split-K
-// partition of the sequence's blocks, the online-softmax state of the G query
-// heads that share g (grouped-query attention, P1 = Ultralytics glossary page
+// Both kernels compute, for one KV head g of one sequence b and one segment
+// of the sequence's blocks, the online-softmax state of the G query heads
+// that share g (grouped-query attention, P1 = Ultralytics glossary page
 // "PagedAttention", section "İlgili Teknikler"): the running maximum m of the
 // scores (log2 units), the running sum l of 2^(s - m) and the unnormalised
-// V-weighted sum acc.  A partition covering the whole sequence writes
-// out = v_scale * acc / l directly; otherwise (m, l, v_scale * acc) go to the
-// workspace for the reduce kernel.
+// V-weighted sum acc.  A segment covering the whole sequence writes
+// out = v_scale * acc / l directly; otherwise (m, l, v_scale * acc) go to a
+// partials row for the reduce kernel.
 //
-// Work decomposition.  One wave64 per (KV head, partition, sequence); a
-// work-group holds the waves of up to NW consecutive KV heads of the same
-// partition (NW = 4 for the VALU kernel, 8 for the MFMA kernel).  All waves of a work-group walk the same blocks in the same
+// Work decomposition.  A work-group holds one wave64 per KV head of a group
+// of up to NW consecutive KV heads (NW = 4 for the VALU kernel, 8 for the
+// MFMA kernel).  All waves of a work-group walk the same blocks in the same
 // order, and a token row of a block stores every KV head contiguously, so
 // together they read each block as one contiguous sweep (DRAM pages stay
-// open) rather than D-element slices scattered over many rows.
+// open) rather than D-element slices scattered over many rows.  Which blocks
+// a work-group walks is the schedule's business (pa_internal.h): one
+// partition of one sequence, or an equal share of all sequences' blocks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,76 +33,103 @@ namespace pa {
 // (never NaN) while a wave has seen no valid token; real scores are far above.
 constexpr float kMaxInit = -1.0e30f;
 
-// Waves per work-group for Hkv KV heads: the smallest power of two covering
-// them, at most max_nw.
-inline int heads_per_group(int hkv, int max_nw) {
-  int nw = 1;
-  while (nw < hkv && nw < max_nw) nw <<= 1;
-  return nw;
-}
 
+// One segment of one sequence: blocks [jbeg, jend) of sequence b, which
+// holds L tokens.
 struct PartitionSpan {
   int L;        // sequence length, clamped to the table's capacity
-  int jbeg;     // first logical block of the partition
+  int jbeg;     // first logical block of the segment
   int jend;     // one past its last logical block
-  bool single;  // one partition covers the sequence: write `out` directly
-  bool skip;    // partition lies past the end of the sequence
 };
 
-template <int BS>
-__device__ __forceinline__ PartitionSpan partition_span(const DecodeParams& p, int b, int part) {
-  PartitionSpan s;
-  const int max_tokens = p.max_blocks_per_seq * BS;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
-  const int PB = p.partition_size / BS;
-  const int nblk = (L + BS - 1) / BS;
-  s.L = L;
-  s.jbeg = part * PB;
-  s.jend = min(s.jbeg + PB, nblk);
-  s.single = L <= p.partition_size;
-  s.skip = part > 0 && s.jbeg >= nblk;
-  return s;
+__device__ __forceinline__ int clamped_len(const DecodeParams& p, int b) {
+  const int max_tokens = p.max_blocks_per_seq * p.block_size;
+  const int L = p.seq_lens[b];
+  return L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
 }
 
-// Grid: x = group of NW KV heads (fastest), y = sequence, z = partition;
-// block = NW wave64s, wave w serving KV head x*NW + w.  With the partition
-// slowest, every sequence's first partitions (always full) are dispatched
-// before the later, shorter or empty ones, which then fill the tail.
-struct WaveTask {
-  int g, part, b;
-  bool idle;  // KV head beyond Hkv (last group) or partition past the end
-  PartitionSpan span;
+// Where a finished segment goes: complete -> out rows out_row + h (h < G);
+// otherwise -> partials rows part_row + h.
+struct SegmentDest {
+  bool complete;
+  size_t out_row;   // b*Hq + g*G
+  size_t part_row;  // partials row of query 0
 };
 
-template <int BS>
-__device__ __forceinline__ WaveTask wave_task(const DecodeParams& p) {
-  WaveTask t;
-  const int nw = blockDim.x >> 6;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  t.g = blockIdx.x * nw + wave;
-  t.b = blockIdx.y;
-  t.part = blockIdx.z;
-  t.span = partition_span<BS>(p, t.b, t.part);
-  t.idle = t.g >= p.Hkv || t.span.skip;
-  return t;
+// Calls fn(b, span, dest) for every segment this wave works on, for KV head
+// g = head_group * NW + wave.  Fixed schedule: work-group (hg, b, part) has
+// one segment, partition `part` of sequence b.  Balanced schedule:
+// work-group (hg, w) walks the sequences that overlap blocks
+// [w*F/groups, (w+1)*F/groups) of the concatenated block list.
+template <typename Fn>
+__device__ __forceinline__ void for_each_segment(const DecodeParams& p, int hg, int wave, int G,
+                                                 Fn&& fn) {
+  const int g = hg * p.heads_per_wg + wave;
+  if (!p.balanced) {
+    const int b = blockIdx.y;
+    const int part = blockIdx.z;
+    PartitionSpan s;
+    s.L = clamped_len(p, b);
+    const int PB = p.partition_size / p.block_size;
+    const int nblk = (s.L + p.block_size - 1) / p.block_size;
+    s.jbeg = part * PB;
+    s.jend = min(s.jbeg + PB, nblk);
+    if (part > 0 && s.jbeg >= nblk) return;  // partition past the end of this sequence
+    SegmentDest d;
+    d.complete = s.L <= p.partition_size;
+    d.out_row = static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G;
+    d.part_row = ws_row(p, d.out_row, part);
+    fn(b, s, d);
+    return;
+  }
+  const int w = blockIdx.y;
+  const int64_t F = p.prefix[p.B];
+  const int n = balanced_groups(p, F);
+  if (w >= n) return;  // fewer blocks than work-groups: the rest idle
+  const int64_t x0 = balanced_start(F, w, n);
+  const int64_t x1 = balanced_start(F, w + 1, n);
+  // the sequence holding block x0: the largest b with prefix[b] <= x0
+  int lo = 0, hi = p.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.prefix[mid] <= x0) lo = mid;
+    else hi = mid;
+  }
+  int which = 0;
+  for (int b = lo; b < p.B; ++b) {
+    const int64_t pb = p.prefix[b];
+    if (pb >= x1) break;
+    const int64_t pn = p.prefix[b + 1];
+    if (pn <= x0 || pn == pb) continue;  // before the range, or no blocks
+    PartitionSpan s;
+    s.L = clamped_len(p, b);
+    s.jbeg = static_cast<int>((x0 > pb ? x0 : pb) - pb);
+    s.jend = static_cast<int>((x1 < pn ? x1 : pn) - pb);
+    SegmentDest d;
+    d.complete = s.jbeg == 0 && pn <= x1;
+    d.out_row = static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G;
+    d.part_row = balanced_row(p, hg, w, which, wave, 0);
+    fn(b, s, d);
+    which = 1;
+  }
 }
 
-// Walk blocks jbeg..jend-1 of a partition with ST register sets in rotation:
-// the loads of the next ST-1 blocks are in flight while a block is consumed.
-// Block ids come 64 at a time, one per lane, from a single vector load, and
-// each iteration takes its id with v_readlane, so no scalar load sits between
-// two blocks.
+// Walk blocks jbeg..jend-1 of a partition in units of UB consecutive blocks,
+// with ST register sets in rotation: the loads of the next ST-1 units are in
+// flight while a unit is consumed.  Block ids come 64 at a time, one per lane,
+// from a single vector load, and each unit takes its ids with v_readlane, so
+// no scalar load sits between two units.
 //
-// `load(blk, buf)` issues the loads of block id blk into buf, through a
-// buffer resource that is empty when blk < 0: ids outside the pool and the
-// look-ahead past the partition's end load nothing but still issue the same
-// instructions.  Every path through the loop therefore has the same loads in
-// flight, and the compiler's wait counts stay exact (a load issued on one path
-// only would force it to wait for all loads, the look-ahead included).
-// `consume(j, ok, buf)` folds logical block j into the running state; ok is
-// false for an id outside the pool, whose block then counts no valid token.
-template <int ST, typename Buf, typename Load, typename Consume>
+// `load(ids, buf)` issues the loads of the unit's UB block ids into buf,
+// through buffer resources that are empty for ids < 0: ids outside the pool
+// and the look-ahead past the partition's end load nothing but still issue
+// the same instructions.  Every path through the loop therefore has the same
+// loads in flight, and the compiler's wait counts stay exact (a load issued on
+// one path only would force it to wait for all loads, the look-ahead
+// included).  `consume(j0, ok, buf)` folds logical blocks j0..j0+UB-1 into the
+// running state; bit u of ok is clear for a block that counts no valid token
+// (an id outside the pool, or past the partition's end).
+template <int ST, int UB, typename Buf, typename Load, typename Consume>
 __device__ __forceinline__ void walk_blocks(const int32_t* table, const PartitionSpan& s,
                                             int num_blocks, int lane, Load&& load,
                                             Consume&& consume) {
@@ -109,30 +137,59 @@ __device__ __forceinline__ void walk_blocks(const int32_t* table, const Partitio
     const int cnt = min(64, s.jend - base);
     int ids = lane < cnt ? table[base + lane] : -1;
     if (static_cast<unsigned>(ids) >= static_cast<unsigned>(num_blocks)) ids = -1;
+    const int units = (cnt + UB - 1) / UB;
+    // ids of unit k (k uniform; 64 is a multiple of UB, so a unit never
+    // straddles two 64-block chunks)
+    auto unit_ids = [&](int k, int (&out)[UB]) {
+#pragma unroll
+      for (int u = 0; u < UB; ++u) out[u] = k < 64 / UB ? __builtin_amdgcn_readlane(ids, k * UB + u) : -1;
+    };
     Buf buf[ST];
 #pragma unroll
-    for (int u = 0; u < ST - 1; ++u) load(__builtin_amdgcn_readlane(ids, u), buf[u]);
-    for (int i = 0; i < cnt; i += ST) {
+    for (int u = 0; u < ST - 1; ++u) {
+      int id[UB];
+      unit_ids(u, id);
+      load(id, buf[u]);
+    }
+    for (int i = 0; i < units; i += ST) {
 #pragma unroll
       for (int u = 0; u < ST; ++u) {
         const int ii = i + u;
-        if (ii >= cnt) break;
-        const int nx = ii + ST - 1;
-        load(nx < 64 ? __builtin_amdgcn_readlane(ids, nx) : -1, buf[(u + ST - 1) % ST]);
-        consume(base + ii, __builtin_amdgcn_readlane(ids, ii) >= 0, buf[u]);
+        if (ii >= units) break;
+        int nid[UB], cid[UB];
+        unit_ids(ii + ST - 1, nid);
+        load(nid, buf[(u + ST - 1) % ST]);
+        unit_ids(ii, cid);
+        unsigned ok = 0;
+#pragma unroll
+        for (int b = 0; b < UB; ++b) ok |= (cid[b] >= 0 ? 1u : 0u) << b;
+        consume(base + ii * UB, ok, buf[u]);
       }
     }
   }
 }
 
-// Store N consecutive output elements (out_dtype F32, F16 or BF16) starting at
-// element i; i is a multiple of N, N*elem a multiple of 4 bytes.
+// Vector stores.  Every lane's run of N outputs goes out in 16-byte (or, for
+// 8-byte runs, 8-byte) stores: element-wise stores would cost the address unit
+// one pass per lane and per element, and the address unit is the bottleneck
+// of these kernels while the K/V loads stream.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// N fp32 values to a 16-byte aligned destination (N a multiple of 4).
+template <int N>
+__device__ __forceinline__ void store_f32_n(float* dst, const float* v) {
+  static_assert(N % 4 == 0, "16-byte stores");
+#pragma unroll
+  for (int k = 0; k < N; k += 4)
+    *reinterpret_cast<f32x4_t*>(dst + k) = f32x4_t{v[k], v[k + 1], v[k + 2], v[k + 3]};
+}
+
+// N consecutive output elements (out_dtype F32, F16 or BF16) starting at
+// element i; the destination is aligned to the run's size (or 16 bytes).
 template <int N>
 __device__ __forceinline__ void store_out_n(void* base, size_t i, const float* v, int out_dtype) {
   if (out_dtype == PA_F32) {
-    float* o = static_cast<float*>(base) + i;
-#pragma unroll
-    for (int k = 0; k < N; ++k) o[k] = v[k];
+    store_f32_n<N>(static_cast<float*>(base) + i, v);
   } else {
     uint32_t w[N / 2];
 #pragma unroll
@@ -147,33 +204,37 @@ __device__ __forceinline__ void store_out_n(void* base, size_t i, const float* v
       }
       w[k] = lo | (hi << 16);
     }
-    uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + i);
+    uint16_t* o = static_cast<uint16_t*>(base) + i;
+    if constexpr (N / 2 >= 4) {
 #pragma unroll
-    for (int k = 0; k < N / 2; ++k) o[k] = w[k];
+      for (int k = 0; k < N / 2; k += 4)
+        *reinterpret_cast<u32x4_t*>(o + 2 * k) = u32x4_t{w[k], w[k + 1], w[k + 2], w[k + 3]};
+    } else {
+      static_assert(N / 2 == 2, "8-byte run");
+      *reinterpret_cast<u32x2_t*>(o) = u32x2_t{w[0], w[1]};
+    }
   }
 }
 
-// Finish N elements [d0, d0+N) of query head h (of the group of KV head g)
-// for one partition: out (single partition) or the workspace partials.
-// m, l: the head's final running max and sum; acc: its unnormalised sums.
+// Finish N elements [d0, d0+N) of query h of a segment: out (the segment
+// covers its sequence) or its partials row.  m, l: the query's final running
+// max and sum; acc: its unnormalised sums.
 template <int N>
-__device__ __forceinline__ void store_partition(const DecodeParams& p, int b, int g, int G, int h,
-                                                int part, bool single, int d0, float m, float l,
-                                                const float* acc) {
-  const size_t hq = static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G + h;
+__device__ __forceinline__ void store_segment(const DecodeParams& p, const SegmentDest& dst, int h,
+                                              int d0, float m, float l, const float* acc) {
   float v[N];
-  if (single) {
+  if (dst.complete) {
 #pragma unroll
     for (int k = 0; k < N; ++k) v[k] = l > 0.f ? (acc[k] / l) * p.v_scale : 0.f;
-    store_out_n<N>(p.out, hq * p.D + d0, v, p.out_dtype);
+    store_out_n<N>(p.out, (dst.out_row + h) * p.D + d0, v, p.out_dtype);
   } else {
-    const size_t pi = hq * p.num_partitions + part;
-    float* o = p.ws_acc + pi * p.D + d0;
+    const size_t r = dst.part_row + h;
 #pragma unroll
-    for (int k = 0; k < N; ++k) o[k] = acc[k] * p.v_scale;
+    for (int k = 0; k < N; ++k) v[k] = acc[k] * p.v_scale;
+    store_f32_n<N>(p.ws_acc + r * p.D + d0, v);
     if (d0 == 0) {
-      p.ws_m[pi] = m;
-      p.ws_l[pi] = l;
+      p.ws_m[r] = m;
+      p.ws_l[r] = l;
     }
   }
 }

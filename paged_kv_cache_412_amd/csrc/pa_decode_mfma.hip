@@ -122,7 +122,9 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   constexpr int KVB = FP8 ? 1 : 2;
   constexpr int SS = D / 32;                    // score MFMAs per tile (32 head-dim values each)
   constexpr int EPL = D / 16;                   // V elements per lane per row = PV MFMAs per tile
-  constexpr int TT = BS / 16;                   // 16-token tiles per block
+  constexpr int TPB = BS / 16;                  // 16-token tiles per block
+  constexpr int UB = BS == 16 ? 2 : 1;          // blocks per pipeline unit (32 tokens)
+  constexpr int TT = UB * TPB;                  // 16-token tiles per unit
   constexpr int KW = D / 8;                     // dwords of 16-bit K per lane per tile
   constexpr int KR = FP8 ? D / 16 : D / 8;      // dwords of stored K per lane per tile
   constexpr int VW = EPL / 2;                   // dwords of 16-bit V per lane per row
@@ -132,12 +134,11 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BS % 16 == 0, "block size");
 
-  const WaveTask task = wave_task<BS>(p);
-  if (task.idle) return;
-  const int g = task.g, b = task.b;
-  const PartitionSpan& span = task.span;
-
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = blockIdx.x;
+  const int g = hg * p.heads_per_wg + wave;
+  if (g >= p.Hkv) return;  // last head group of a head count that is not a multiple
   const int lo = lane & 15;
   const int grp = lane >> 4;
 
@@ -146,28 +147,6 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   // contiguous bytes of every one of the tile's 16 rows.  e4m3: chunk
   // SS*grp+s, so a lane's K bytes for the tile are one contiguous run.
   auto chunk_of = [&](int s) { return FP8 ? SS * grp + s : 4 * s + grp; };
-
-  // Q^T operand: query lo of the group, zero rows beyond G.
-  uint32_t qw[KW];
-  if (lo < G) {
-    const char* qrow =
-        static_cast<const char*>(p.q) + ((static_cast<size_t>(b) * p.Hq + g * G + lo) * D) * 2;
-#pragma unroll
-    for (int s = 0; s < SS; ++s) {
-      const Chunk c = *reinterpret_cast<const Chunk*>(qrow + chunk_of(s) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qw[4 * s + i] = c.w[i];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < KW; ++i) qw[i] = 0u;
-  }
-
-  f32x4 O[EPL];
-#pragma unroll
-  for (int mm = 0; mm < EPL; ++mm) O[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kMaxInit;  // running max of query lo (log2 units), same in all four groups
-  float l_part = 0.f;      // this lane's share of the running sum of query lo
 
   const uint32_t row_stride = static_cast<uint32_t>(p.Hkv) * D * KVB;
   const uint32_t blk_bytes = row_stride * BS;
@@ -179,7 +158,6 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   const int v_off = head_off + 4 * grp * row_stride + EPL * lo * KVB;
   const char* kpool = static_cast<const char*>(p.k_cache);
   const char* vpool = static_cast<const char*>(p.v_cache);
-  const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const float qk = p.qk_scale_log2;
 
   struct Raw {
@@ -187,183 +165,243 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
     uint32_t v[TT][4][VR];
   };
 
-  // Loads of block id blk (nothing is read for blk < 0).
-  auto load = [&](int blk, Raw& r) {
-    const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
-    const uint32_t n = blk < 0 ? 0u : blk_bytes;
-    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + off, n);
-    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + off, n);
+  // Loads of the unit's blocks (nothing is read for an id < 0).
+  auto load = [&](const int (&id)[UB], Raw& r) {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int ts = tt * 16 * row_stride;
-      if constexpr (FP8) {
-        buffer_load<KLD, 0>(kr, k_off, ts, &r.k[tt][0]);
-        if constexpr (KR > KLD) buffer_load<KLD, 16>(kr, k_off, ts, &r.k[tt][KLD]);
-      } else {
-        buffer_load<4, 0>(kr, k_off, ts, &r.k[tt][0]);
-        buffer_load<4, 64>(kr, k_off, ts, &r.k[tt][4]);
-        if constexpr (SS > 2) {
-          buffer_load<4, 128>(kr, k_off, ts, &r.k[tt][8]);
-          buffer_load<4, 192>(kr, k_off, ts, &r.k[tt][12]);
-        }
-      }
-    }
+    for (int ub = 0; ub < UB; ++ub) {
+      const int blk = id[ub];
+      const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
+      const uint32_t n = blk < 0 ? 0u : blk_bytes;
+      const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + off, n);
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) buffer_load<VR>(vr, v_off, (tt * 16 + e) * row_stride, r.v[tt][e]);
-    }
-  };
-
-  auto consume = [&](int j, bool ok, Raw& r) {
-    // valid rows of this block; a block id outside the pool counts none
-    const int valid = ok ? min(BS, span.L - j * BS) : 0;
-    float sc[TT][4];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      uint32_t kw[KW];
-      if constexpr (FP8) {
-#pragma unroll
-        for (int i = 0; i < KR; ++i) M::widen4(r.k[tt][i], kw[2 * i], kw[2 * i + 1]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < KW; ++i) kw[i] = r.k[tt][i];
-      }
-      f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < SS; ++s) S = M::qk(&kw[4 * s], &qw[4 * s], S);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // rows past the end may hold anything (NaN included): excluded outright
-        const int t = tt * 16 + 4 * grp + i;
-        sc[tt][i] = t < valid ? S[i] * qk : -__builtin_inff();
-      }
-    }
-    float bm = sc[0][0];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[tt][i]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float mn = fmaxf(m_run, bm);
-    if (__ballot(mn > m_run)) {
-      const float alpha = fast_exp2(m_run - mn);
-      l_part *= alpha;
-      float a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = __shfl(alpha, 4 * grp + i, 64);
-#pragma unroll
-      for (int mm = 0; mm < EPL; ++mm) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[mm][i] *= a[i];
-      }
-      m_run = mn;
-    }
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      float pw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pw[i] = fast_exp2(sc[tt][i] - m_run);
-        l_part += pw[i];
-      }
-      const uint32_t pa0 = M::pack2(pw[0], pw[1]);
-      const uint32_t pa1 = M::pack2(pw[2], pw[3]);
-      if (valid < BS) {
-        // zero the V rows past the end so that 0 * NaN cannot reach the sum
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (tt * 16 + 4 * grp + e >= valid) {
-#pragma unroll
-            for (int i = 0; i < VR; ++i) r.v[tt][e][i] = 0u;
+      for (int tb = 0; tb < TPB; ++tb) {
+        const int tt = ub * TPB + tb;
+        const int ts = tb * 16 * row_stride;
+        if constexpr (FP8) {
+          buffer_load<KLD, 0>(kr, k_off, ts, &r.k[tt][0]);
+          if constexpr (KR > KLD) buffer_load<KLD, 16>(kr, k_off, ts, &r.k[tt][KLD]);
+        } else {
+          buffer_load<4, 0>(kr, k_off, ts, &r.k[tt][0]);
+          buffer_load<4, 64>(kr, k_off, ts, &r.k[tt][4]);
+          if constexpr (SS > 2) {
+            buffer_load<4, 128>(kr, k_off, ts, &r.k[tt][8]);
+            buffer_load<4, 192>(kr, k_off, ts, &r.k[tt][12]);
           }
         }
       }
-      uint32_t vw[4][VW];
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (FP8) {
+    for (int ub = 0; ub < UB; ++ub) {
+      const int blk = id[ub];
+      const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
+      const uint32_t n = blk < 0 ? 0u : blk_bytes;
+      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + off, n);
 #pragma unroll
-          for (int i = 0; i < VR; ++i) M::widen4(r.v[tt][e][i], vw[e][2 * i], vw[e][2 * i + 1]);
-        } else {
+      for (int tb = 0; tb < TPB; ++tb) {
 #pragma unroll
-          for (int i = 0; i < VW; ++i) vw[e][i] = r.v[tt][e][i];
-        }
-      }
-#pragma unroll
-      for (int mm = 0; mm < EPL; ++mm) {
-        const uint32_t b0 = pick_halves(vw[0][mm >> 1], vw[1][mm >> 1], mm & 1);
-        const uint32_t b1 = pick_halves(vw[2][mm >> 1], vw[3][mm >> 1], mm & 1);
-        O[mm] = M::pv(pa0, pa1, b0, b1, O[mm]);
+        for (int e = 0; e < 4; ++e)
+          buffer_load<VR>(vr, v_off, (tb * 16 + e) * row_stride, r.v[ub * TPB + tb][e]);
       }
     }
   };
 
-  walk_blocks<ST, Raw>(table, span, p.num_blocks, lane, load, consume);
-
-  // l of query lo summed over the four lane groups; every lane then fetches
-  // m and l of the queries whose accumulators it holds (4*grp + i)
-  float lt = l_part + __shfl_xor(l_part, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  for_each_segment(p, hg, wave, G, [&](int b, const PartitionSpan& span, const SegmentDest& dst) {
+    // Q^T operand: query lo of the group, zero rows beyond G.
+    uint32_t qw[KW];
+    if (lo < G) {
+      const char* qrow =
+          static_cast<const char*>(p.q) + ((static_cast<size_t>(b) * p.Hq + g * G + lo) * D) * 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = 4 * grp + i;
-    const float lq = __shfl(lt, q, 64);
-    const float mq = __shfl(m_run, q, 64);
-    if (q < G) {
-      float o[EPL];
+      for (int s = 0; s < SS; ++s) {
+        const Chunk c = *reinterpret_cast<const Chunk*>(qrow + chunk_of(s) * 16);
 #pragma unroll
-      for (int mm = 0; mm < EPL; ++mm) o[mm] = O[mm][i];
-      store_partition<EPL>(p, b, g, G, q, task.part, span.single, EPL * lo, mq, lq, o);
+        for (int i = 0; i < 4; ++i) qw[4 * s + i] = c.w[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KW; ++i) qw[i] = 0u;
     }
-  }
+
+    f32x4 O[EPL];
+#pragma unroll
+    for (int mm = 0; mm < EPL; ++mm) O[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kMaxInit;  // running max of query lo (log2 units), same in all four groups
+    float l_part = 0.f;      // this lane's share of the running sum of query lo
+
+    auto consume = [&](int j0, unsigned ok, Raw& r) {
+      // valid rows of each 16-token tile; a block that is not ok counts none
+      int valid[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int ub = tt / TPB;
+        const int first = (j0 + ub) * BS + (tt % TPB) * 16;
+        valid[tt] = (ok >> ub) & 1u ? min(16, max(0, span.L - first)) : 0;
+      }
+      float sc[TT][4];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        uint32_t kw[KW];
+        if constexpr (FP8) {
+#pragma unroll
+          for (int i = 0; i < KR; ++i) M::widen4(r.k[tt][i], kw[2 * i], kw[2 * i + 1]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < KW; ++i) kw[i] = r.k[tt][i];
+        }
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < SS; ++s) S = M::qk(&kw[4 * s], &qw[4 * s], S);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // rows past the end may hold anything (NaN included): excluded outright
+          sc[tt][i] = 4 * grp + i < valid[tt] ? S[i] * qk : -__builtin_inff();
+        }
+      }
+      float bm = sc[0][0];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bm = fmaxf(bm, sc[tt][i]);
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float mn = fmaxf(m_run, bm);
+      if (__ballot(mn > m_run)) {
+        const float alpha = fast_exp2(m_run - mn);
+        l_part *= alpha;
+        float a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = __shfl(alpha, 4 * grp + i, 64);
+#pragma unroll
+        for (int mm = 0; mm < EPL; ++mm) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[mm][i] *= a[i];
+        }
+        m_run = mn;
+      }
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        float pw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pw[i] = fast_exp2(sc[tt][i] - m_run);
+          l_part += pw[i];
+        }
+        const uint32_t pa0 = M::pack2(pw[0], pw[1]);
+        const uint32_t pa1 = M::pack2(pw[2], pw[3]);
+        if (valid[tt] < 16) {
+          // zero the V rows past the end so that 0 * NaN cannot reach the sum
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (4 * grp + e >= valid[tt]) {
+#pragma unroll
+              for (int i = 0; i < VR; ++i) r.v[tt][e][i] = 0u;
+            }
+          }
+        }
+        uint32_t vw[4][VW];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < VR; ++i) M::widen4(r.v[tt][e][i], vw[e][2 * i], vw[e][2 * i + 1]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < VW; ++i) vw[e][i] = r.v[tt][e][i];
+          }
+        }
+#pragma unroll
+        for (int mm = 0; mm < EPL; ++mm) {
+          const uint32_t b0 = pick_halves(vw[0][mm >> 1], vw[1][mm >> 1], mm & 1);
+          const uint32_t b1 = pick_halves(vw[2][mm >> 1], vw[3][mm >> 1], mm & 1);
+          O[mm] = M::pv(pa0, pa1, b0, b1, O[mm]);
+        }
+      }
+    };
+
+    const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+    walk_blocks<ST, UB, Raw>(table, span, p.num_blocks, lane, load, consume);
+
+    // l of query lo summed over the four lane groups; every lane then fetches
+    // m and l of the queries whose accumulators it holds (4*grp + i)
+    float lt = l_part + __shfl_xor(l_part, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 4 * grp + i;
+      const float lq = __shfl(lt, q, 64);
+      const float mq = __shfl(m_run, q, 64);
+      if (q < G) {
+        float o[EPL];
+#pragma unroll
+        for (int mm = 0; mm < EPL; ++mm) o[mm] = O[mm][i];
+        store_segment<EPL>(p, dst, q, EPL * lo, mq, lq, o);
+      }
+    }
+  });
 }
 
 // ------------------------------------------------------------------ dispatch
 
 namespace {
 
-// register sets in the load pipeline (blocks in flight per wave, plus one)
+// register sets in the load pipeline (units in flight per wave, plus one)
 constexpr int kStages = 2;
 
-template <int KV, int Q, int D, int BS, int G>
-hipError_t launch(const DecodeParams& p, hipStream_t s) {
-  const int nw = heads_per_group(p.Hkv, kMfmaHeads);
-  dim3 grid((p.Hkv + nw - 1) / nw, p.B, p.num_partitions);
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, D, BS, G, kStages>), grid, dim3(nw * 64), 0, s, p);
-  return hipGetLastError();
-}
+template <int KV_, int Q_, int D_, int BS_, int G_>
+struct Tag {
+  static constexpr int KV = KV_, Q = Q_, D = D_, BS = BS_, G = G_;
+  static const void* kernel() {
+    return reinterpret_cast<const void*>(&decode_mfma_kernel<KV, Q, D, BS, G, kStages>);
+  }
+  static hipError_t launch(const DecodeParams& p, hipStream_t s) {
+    const dim3 grid = p.balanced ? dim3(p.head_groups, p.groups, 1)
+                                 : dim3(p.head_groups, p.B, p.num_partitions);
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, D, BS, G, kStages>), grid,
+                       dim3(p.heads_per_wg * 64), 0, s, p);
+    return hipGetLastError();
+  }
+};
 
-template <int KV, int Q, int D, int BS>
-hipError_t by_group(const DecodeParams& p, hipStream_t s, bool* ok) {
+template <int KV, int Q, int D, int BS, typename F>
+bool by_group(const DecodeParams& p, F&& f) {
   switch (p.Hq / p.Hkv) {
-    case 4: return launch<KV, Q, D, BS, 4>(p, s);
-    case 8: return launch<KV, Q, D, BS, 8>(p, s);
-    default: *ok = false; return hipSuccess;
+    case 4: f(Tag<KV, Q, D, BS, 4>{}); return true;
+    case 8: f(Tag<KV, Q, D, BS, 8>{}); return true;
+    default: return false;
   }
 }
 
-template <int KV, int Q, int D>
-hipError_t by_block(const DecodeParams& p, hipStream_t s, bool* ok) {
+template <int KV, int Q, int D, typename F>
+bool by_block(const DecodeParams& p, F&& f) {
   switch (p.block_size) {
-    case 16: return by_group<KV, Q, D, 16>(p, s, ok);
-    case 32: return by_group<KV, Q, D, 32>(p, s, ok);
-    default: *ok = false; return hipSuccess;
+    case 16: return by_group<KV, Q, D, 16>(p, f);
+    case 32: return by_group<KV, Q, D, 32>(p, f);
+    default: return false;
   }
 }
 
-template <int KV, int Q>
-hipError_t by_dim(const DecodeParams& p, hipStream_t s, bool* ok) {
+template <int KV, int Q, typename F>
+bool by_dim(const DecodeParams& p, F&& f) {
   switch (p.D) {
-    case 64: return by_block<KV, Q, 64>(p, s, ok);
-    case 128: return by_block<KV, Q, 128>(p, s, ok);
-    default: *ok = false; return hipSuccess;
+    case 64: return by_block<KV, Q, 64>(p, f);
+    case 128: return by_block<KV, Q, 128>(p, f);
+    default: return false;
   }
+}
+
+template <typename F>
+bool dispatch(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype, F&& f) {
+  if (kv_dtype == PA_F16 && q_dtype == PA_F16) return by_dim<PA_F16, PA_F16>(p, f);
+  if (kv_dtype == PA_BF16 && q_dtype == PA_BF16) return by_dim<PA_BF16, PA_BF16>(p, f);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16) return by_dim<PA_FP8_E4M3, PA_BF16>(p, f);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16) return by_dim<PA_FP8_E4M3, PA_F16>(p, f);
+  return false;
 }
 
 }  // namespace
+
+int32_t decode_mfma_heads() { return kMfmaHeads; }
 
 bool decode_mfma_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t group) {
   if (group != 4 && group != 8) return false;
@@ -373,16 +411,15 @@ bool decode_mfma_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t group) {
 
 hipError_t launch_decode_mfma(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
                               hipStream_t stream, bool* supported) {
-  *supported = true;
-  if (kv_dtype == PA_F16 && q_dtype == PA_F16) return by_dim<PA_F16, PA_F16>(p, stream, supported);
-  if (kv_dtype == PA_BF16 && q_dtype == PA_BF16)
-    return by_dim<PA_BF16, PA_BF16>(p, stream, supported);
-  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16)
-    return by_dim<PA_FP8_E4M3, PA_BF16>(p, stream, supported);
-  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16)
-    return by_dim<PA_FP8_E4M3, PA_F16>(p, stream, supported);
-  *supported = false;
-  return hipSuccess;
+  hipError_t e = hipSuccess;
+  *supported = dispatch(p, q_dtype, kv_dtype, [&](auto t) { e = decltype(t)::launch(p, stream); });
+  return e;
+}
+
+int32_t decode_mfma_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype) {
+  const void* fn = nullptr;
+  if (!dispatch(p, q_dtype, kv_dtype, [&](auto t) { fn = decltype(t)::kernel(); })) return 0;
+  return groups_per_cu(fn, p.heads_per_wg * 64);
 }
 
 }  // namespace pa

@@ -180,31 +180,13 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
   constexpr int NL = BS / TPL;   // rows per lane per block
   static_assert(D % CE == 0 && 64 % LPT == 0 && BS % TPL == 0, "unsupported tile shape");
 
-  const WaveTask task = wave_task<BS>(p);
-  if (task.idle) return;
-  const int g = task.g, b = task.b;
-  const PartitionSpan& span = task.span;
-
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = blockIdx.x;
+  const int g = hg * p.heads_per_wg + wave;
+  if (g >= p.Hkv) return;  // last head group of a head count that is not a multiple
   const int c = lane % LPT;   // chunk of the row this lane owns
   const int tg = lane / LPT;  // row within a wave load
-
-  typename O::QReg qr[G];
-  {
-    const char* qrow =
-        static_cast<const char*>(p.q) + (static_cast<size_t>(b) * p.Hq + g * G) * D * QB;
-#pragma unroll
-    for (int h = 0; h < G; ++h) qr[h] = O::load_q(qrow + h * D * QB, c * CE);
-  }
-
-  float m[G], l[G], acc[G][CE];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kMaxInit;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < CE; ++e) acc[h][e] = 0.f;
-  }
 
   const uint32_t row_stride = static_cast<uint32_t>(p.Hkv) * D * KVB;  // bytes between token rows
   const uint32_t blk_bytes = row_stride * BS;
@@ -212,7 +194,6 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
   const int lane_off = static_cast<int>(g * D * KVB + c * 16 + tg * row_stride);
   const char* kpool = static_cast<const char*>(p.k_cache);
   const char* vpool = static_cast<const char*>(p.v_cache);
-  const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
   const float qk = p.qk_scale_log2;
 
   struct Buf {
@@ -220,7 +201,8 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
   };
 
   // Loads of block id blk (nothing is read for blk < 0).
-  auto load = [&](int blk, Buf& r) {
+  auto load = [&](const int (&id)[1], Buf& r) {
+    const int blk = id[0];
     const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
     const uint32_t n = blk < 0 ? 0u : blk_bytes;
     const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + off, n);
@@ -231,78 +213,98 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
     for (int i = 0; i < NL; ++i) buffer_load<4>(vr, lane_off, i * TPL * row_stride, r.v[i].w);
   };
 
-  auto consume = [&](int j, bool ok, const Buf& r) {
-    // valid rows of this block (only the last block of a sequence is partial;
-    // a block id outside the pool counts none)
-    const int valid = ok ? min(BS, span.L - j * BS) : 0;
-    float s[NL][G];
+  for_each_segment(p, hg, wave, G, [&](int b, const PartitionSpan& span, const SegmentDest& dst) {
+    typename O::QReg qr[G];
+    {
+      const char* qrow =
+          static_cast<const char*>(p.q) + (static_cast<size_t>(b) * p.Hq + g * G) * D * QB;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[i][h] = group_sum<LPT>(O::dot(qr[h], r.k[i])) * qk;
+      for (int h = 0; h < G; ++h) qr[h] = O::load_q(qrow + h * D * QB, c * CE);
     }
-    float vf[NL][CE];
+
+    float m[G], l[G], acc[G][CE];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) O::to_f32(r.v[i], vf[i]);
-    if (valid < BS) {
-      // rows past the end are excluded outright: their K and V may hold
-      // anything (NaN included), so they get weight 0 and a zeroed V row.
+    for (int h = 0; h < G; ++h) {
+      m[h] = kMaxInit;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) acc[h][e] = 0.f;
+    }
+
+    auto consume = [&](int j, unsigned ok, const Buf& r) {
+      // valid rows of this block (only the last block of a sequence is
+      // partial; a block id outside the pool counts none)
+      const int valid = ok ? min(BS, span.L - j * BS) : 0;
+      float s[NL][G];
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        if (i * TPL + tg >= valid) {
 #pragma unroll
-          for (int h = 0; h < G; ++h) s[i][h] = -__builtin_inff();
+        for (int h = 0; h < G; ++h) s[i][h] = group_sum<LPT>(O::dot(qr[h], r.k[i])) * qk;
+      }
+      float vf[NL][CE];
 #pragma unroll
-          for (int e = 0; e < CE; ++e) vf[i][e] = 0.f;
+      for (int i = 0; i < NL; ++i) O::to_f32(r.v[i], vf[i]);
+      if (valid < BS) {
+        // rows past the end are excluded outright: their K and V may hold
+        // anything (NaN included), so they get weight 0 and a zeroed V row.
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          if (i * TPL + tg >= valid) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) s[i][h] = -__builtin_inff();
+#pragma unroll
+            for (int e = 0; e < CE; ++e) vf[i][e] = 0.f;
+          }
         }
       }
-    }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = m[h];
+      for (int h = 0; h < G; ++h) {
+        float mx = m[h];
 #pragma unroll
-      for (int i = 0; i < NL; ++i) mx = fmaxf(mx, s[i][h]);
-      const float alpha = fast_exp2(m[h] - mx);
-      m[h] = mx;
-      float lh = l[h] * alpha;
+        for (int i = 0; i < NL; ++i) mx = fmaxf(mx, s[i][h]);
+        const float alpha = fast_exp2(m[h] - mx);
+        m[h] = mx;
+        float lh = l[h] * alpha;
 #pragma unroll
-      for (int e = 0; e < CE; ++e) acc[h][e] *= alpha;
+        for (int e = 0; e < CE; ++e) acc[h][e] *= alpha;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const float pw = fast_exp2(s[i][h] - mx);
-        lh += pw;
+        for (int i = 0; i < NL; ++i) {
+          const float pw = fast_exp2(s[i][h] - mx);
+          lh += pw;
 #pragma unroll
-        for (int e = 0; e < CE; ++e) acc[h][e] = __builtin_fmaf(pw, vf[i][e], acc[h][e]);
+          for (int e = 0; e < CE; ++e) acc[h][e] = __builtin_fmaf(pw, vf[i][e], acc[h][e]);
+        }
+        l[h] = lh;
       }
-      l[h] = lh;
+    };
+
+    const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+    walk_blocks<ST, 1, Buf>(table, span, p.num_blocks, lane, load, consume);
+
+    // merge the per-lane states of the TPL row groups that own the same
+    // chunk; the butterfly leaves the merged state in every lane
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mo = __shfl_xor(m[h], off, 64);
+        const float lo = __shfl_xor(l[h], off, 64);
+        const float M = fmaxf(m[h], mo);
+        const float a = fast_exp2(m[h] - M);
+        const float ao = fast_exp2(mo - M);
+        l[h] = l[h] * a + lo * ao;
+#pragma unroll
+        for (int e = 0; e < CE; ++e)
+          acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], off, 64) * ao;
+        m[h] = M;
+      }
     }
-  };
 
-  walk_blocks<ST, Buf>(table, span, p.num_blocks, lane, load, consume);
-
-  // merge the per-lane states of the TPL row groups that own the same chunk;
-  // the butterfly leaves the merged state in every lane
+    if (tg == 0) {
 #pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off, 64);
-      const float lo = __shfl_xor(l[h], off, 64);
-      const float M = fmaxf(m[h], mo);
-      const float a = fast_exp2(m[h] - M);
-      const float ao = fast_exp2(mo - M);
-      l[h] = l[h] * a + lo * ao;
-#pragma unroll
-      for (int e = 0; e < CE; ++e) acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], off, 64) * ao;
-      m[h] = M;
+      for (int h = 0; h < G; ++h) store_segment<CE>(p, dst, h, c * CE, m[h], l[h], acc[h]);
     }
-  }
-
-  if (tg == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      store_partition<CE>(p, b, g, G, h, task.part, span.single, c * CE, m[h], l[h], acc[h]);
-  }
+  });
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -314,64 +316,86 @@ namespace {
 template <int KV>
 constexpr int kStages = KV == PA_F32 ? 1 : 2;
 
-template <int KV, int Q, int D, int BS, int G>
-hipError_t launch(const DecodeParams& p, hipStream_t s) {
-  const int nw = heads_per_group(p.Hkv, kValuHeads);
-  dim3 grid((p.Hkv + nw - 1) / nw, p.B, p.num_partitions);
-  hipLaunchKernelGGL((decode_valu_kernel<KV, Q, D, BS, G, kStages<KV>>), grid, dim3(nw * 64), 0, s, p);
-  return hipGetLastError();
-}
+template <int KV_, int Q_, int D_, int BS_, int G_>
+struct Tag {
+  static constexpr int KV = KV_, Q = Q_, D = D_, BS = BS_, G = G_;
+  static const void* kernel() {
+    return reinterpret_cast<const void*>(&decode_valu_kernel<KV, Q, D, BS, G, kStages<KV>>);
+  }
+  static hipError_t launch(const DecodeParams& p, hipStream_t s) {
+    const dim3 grid = p.balanced ? dim3(p.head_groups, p.groups, 1)
+                                 : dim3(p.head_groups, p.B, p.num_partitions);
+    hipLaunchKernelGGL((decode_valu_kernel<KV, Q, D, BS, G, kStages<KV>>), grid,
+                       dim3(p.heads_per_wg * 64), 0, s, p);
+    return hipGetLastError();
+  }
+};
 
-template <int KV, int Q, int D, int BS>
-hipError_t by_group(const DecodeParams& p, hipStream_t s, bool* ok) {
+// Calls f(Tag<...>{}) for the instance serving p; false if none is built.
+template <int KV, int Q, int D, int BS, typename F>
+bool by_group(const DecodeParams& p, F&& f) {
   switch (p.Hq / p.Hkv) {
-    case 1: return launch<KV, Q, D, BS, 1>(p, s);
-    case 2: return launch<KV, Q, D, BS, 2>(p, s);
+    case 1: f(Tag<KV, Q, D, BS, 1>{}); return true;
+    case 2: f(Tag<KV, Q, D, BS, 2>{}); return true;
     case 4:
-      if constexpr (KV == PA_F32) return launch<KV, Q, D, BS, 4>(p, s);
-      break;
+      if constexpr (KV == PA_F32) {
+        f(Tag<KV, Q, D, BS, 4>{});
+        return true;
+      }
+      return false;
     case 8:
-      if constexpr (KV == PA_F32) return launch<KV, Q, D, BS, 8>(p, s);
-      break;
-    default: break;
+      if constexpr (KV == PA_F32) {
+        f(Tag<KV, Q, D, BS, 8>{});
+        return true;
+      }
+      return false;
+    default: return false;
   }
-  *ok = false;
-  return hipSuccess;
 }
 
-template <int KV, int Q, int D>
-hipError_t by_block(const DecodeParams& p, hipStream_t s, bool* ok) {
+template <int KV, int Q, int D, typename F>
+bool by_block(const DecodeParams& p, F&& f) {
   switch (p.block_size) {
-    case 16: return by_group<KV, Q, D, 16>(p, s, ok);
-    case 32: return by_group<KV, Q, D, 32>(p, s, ok);
-    default: *ok = false; return hipSuccess;
+    case 16: return by_group<KV, Q, D, 16>(p, f);
+    case 32: return by_group<KV, Q, D, 32>(p, f);
+    default: return false;
   }
 }
 
-template <int KV, int Q>
-hipError_t by_dim(const DecodeParams& p, hipStream_t s, bool* ok) {
+template <int KV, int Q, typename F>
+bool by_dim(const DecodeParams& p, F&& f) {
   switch (p.D) {
-    case 64: return by_block<KV, Q, 64>(p, s, ok);
-    case 128: return by_block<KV, Q, 128>(p, s, ok);
-    default: *ok = false; return hipSuccess;
+    case 64: return by_block<KV, Q, 64>(p, f);
+    case 128: return by_block<KV, Q, 128>(p, f);
+    default: return false;
   }
+}
+
+template <typename F>
+bool dispatch(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype, F&& f) {
+  if (kv_dtype == PA_F32 && q_dtype == PA_F32) return by_dim<PA_F32, PA_F32>(p, f);
+  if (kv_dtype == PA_F16 && q_dtype == PA_F16) return by_dim<PA_F16, PA_F16>(p, f);
+  if (kv_dtype == PA_BF16 && q_dtype == PA_BF16) return by_dim<PA_BF16, PA_BF16>(p, f);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16) return by_dim<PA_FP8_E4M3, PA_BF16>(p, f);
+  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16) return by_dim<PA_FP8_E4M3, PA_F16>(p, f);
+  return false;
 }
 
 }  // namespace
 
+int32_t decode_valu_heads() { return kValuHeads; }
+
 hipError_t launch_decode_valu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
                               hipStream_t stream, bool* supported) {
-  *supported = true;
-  if (kv_dtype == PA_F32 && q_dtype == PA_F32) return by_dim<PA_F32, PA_F32>(p, stream, supported);
-  if (kv_dtype == PA_F16 && q_dtype == PA_F16) return by_dim<PA_F16, PA_F16>(p, stream, supported);
-  if (kv_dtype == PA_BF16 && q_dtype == PA_BF16)
-    return by_dim<PA_BF16, PA_BF16>(p, stream, supported);
-  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16)
-    return by_dim<PA_FP8_E4M3, PA_BF16>(p, stream, supported);
-  if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16)
-    return by_dim<PA_FP8_E4M3, PA_F16>(p, stream, supported);
-  *supported = false;
-  return hipSuccess;
+  hipError_t e = hipSuccess;
+  *supported = dispatch(p, q_dtype, kv_dtype, [&](auto t) { e = decltype(t)::launch(p, stream); });
+  return e;
+}
+
+int32_t decode_valu_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype) {
+  const void* fn = nullptr;
+  if (!dispatch(p, q_dtype, kv_dtype, [&](auto t) { fn = decltype(t)::kernel(); })) return 0;
+  return groups_per_cu(fn, p.heads_per_wg * 64);
 }
 
 }  // namespace pa

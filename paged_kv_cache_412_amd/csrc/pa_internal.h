@@ -11,6 +11,18 @@
 namespace pa {
 
 // Everything a decode-partition or reduce launch needs, resolved on the host.
+//
+// Two schedules split the work of a decode step among work-groups of
+// heads_per_wg waves (one KV head each):
+//  * fixed partitions (partition_size > 0 in the call): work-group
+//    (head group, sequence, partition) covers partition_size tokens of one
+//    sequence; partials rows are ws_row(hq, partition).
+//  * balanced (partition_size == 0): a plan kernel writes the prefix sums
+//    prefix[b] of the sequences' block counts; work-group (head group, w) of
+//    `groups` per head group takes blocks [w*F/groups, (w+1)*F/groups) of the
+//    concatenation of all sequences (F = prefix[B]).  It writes the output of
+//    every sequence it covers whole and partials only for the (at most two)
+//    sequences it covers in part; rows are balanced_row(...).
 struct DecodeParams {
   void* out;
   const void* q;
@@ -18,16 +30,61 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* ws_m;    // [B][Hq][P] running max (log2 units)
-  float* ws_l;    // [B][Hq][P] running sum
-  float* ws_acc;  // [B][Hq][P][D] unnormalised V-weighted sums (v_scale applied)
+  float* ws_acc;  // partial rows x D: unnormalised V-weighted sums (v_scale applied)
+  float* ws_m;    // partial rows: running max (log2 units)
+  float* ws_l;    // partial rows: running sum
+  int32_t* prefix;  // balanced: [B+1] block-count prefix sums
   int32_t B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq;
-  int32_t partition_size;  // tokens
-  int32_t num_partitions;  // P: partitions of the longest possible sequence
+  int32_t partition_size;  // fixed: tokens per partition
+  int32_t num_partitions;  // fixed: partitions of the longest possible sequence
+  int32_t balanced;        // 1 = balanced schedule
+  int32_t heads_per_wg;    // waves (KV heads) per work-group
+  int32_t head_groups;     // ceil(Hkv / heads_per_wg)
+  int32_t groups;          // balanced: work-groups per head group
   float qk_scale_log2;     // scale * k_scale * log2(e)
   float v_scale;
   int32_t out_dtype;
 };
+
+// Row of the split-K partials of query head hq (= b*Hq + h) and partition
+// `part` (fixed schedule).  Partition-major: the work-groups that run
+// together (one partition of many sequences) write one contiguous region.
+__host__ __device__ inline size_t ws_row(const DecodeParams& p, size_t hq, int part) {
+  return static_cast<size_t>(part) * (static_cast<size_t>(p.B) * p.Hq) + hq;
+}
+
+// Row of the balanced schedule's partials: work-group w of head group hg,
+// slot `which` (0: the first sequence of its range, 1: the last), wave
+// (KV head within the group) and query q of the KV head's group of G.
+__host__ __device__ inline size_t balanced_row(const DecodeParams& p, int hg, int w, int which,
+                                               int wave, int q) {
+  const int G = p.Hq / p.Hkv;
+  return ((static_cast<size_t>(hg) * p.groups + w) * 2 + which) *
+             (static_cast<size_t>(p.heads_per_wg) * G) +
+         static_cast<size_t>(wave) * G + q;
+}
+
+// Work-groups per head group that take part: at most one per block, so that
+// every one of them owns at least one block (w*F/n < (w+1)*F/n for n <= F).
+__host__ __device__ inline int balanced_groups(const DecodeParams& p, int64_t F) {
+  return static_cast<int>(F < p.groups ? F : p.groups);
+}
+
+// First block (in the concatenation of all sequences' blocks) of balanced
+// work-group w out of n, for F blocks in all.
+__host__ __device__ inline int64_t balanced_start(int64_t F, int w, int n) {
+  return static_cast<int64_t>(w) * F / n;
+}
+
+// The balanced work-group whose range holds block x: the largest w with
+// balanced_start(F, w, n) <= x.
+__host__ __device__ inline int balanced_owner(int64_t F, int64_t x, int n) {
+  return static_cast<int>(((x + 1) * n - 1) / F);
+}
+
+// Balanced schedule: at most this many waves in one launch bounds the
+// workspace (16 waves on each of 256 compute units).
+constexpr int64_t kBalancedMaxWaves = 4096;
 
 // The default split-K partition size aims for at least kTargetWaves waves (a
 // few rounds of the 256 compute units of a gfx950 part) and at least
@@ -43,6 +100,21 @@ constexpr int kCopySliceChunks = 1024;
 
 hipError_t launch_decode_partition(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
                                    hipStream_t stream, bool* supported);
+// Waves per work-group of the partition kernel that serves these arguments.
+int32_t decode_heads_per_wg(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t Hq, int32_t Hkv);
+int32_t decode_mfma_heads();  // most KV heads per work-group of each kernel
+int32_t decode_valu_heads();
+// Work-groups of `threads` threads running kernel `fn` that one compute unit
+// of the current device holds at once, from the runtime's occupancy
+// calculator, cached per (device, kernel); 0 when the runtime cannot say.
+int32_t groups_per_cu(const void* fn, int threads);
+// Compute units of the current device (cached); 256 (gfx950) if unknown.
+int32_t compute_units();
+// Work-groups of that kernel one compute unit holds at once (0 if unknown).
+int32_t decode_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype);
+int32_t decode_mfma_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype);
+int32_t decode_valu_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype);
+hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
 // The two partition kernels: matrix cores for query groups of 4 or 8 over
 // 16-bit or e4m3 caches, vector ALUs for everything else.
 bool decode_mfma_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t group);

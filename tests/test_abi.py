@@ -50,6 +50,7 @@ def valid_args(**kw):
     a.scale, a.k_scale, a.v_scale = 0.125, 1.0, 1.0
     a.q_dtype = a.kv_dtype = a.out_dtype = binding.PA_F32
     a.partition_size = 0
+    a.workspace, a.workspace_bytes = FAKE, 1 << 40
     for k, v in kw.items():
         setattr(a, k, v)
     return a
@@ -77,7 +78,10 @@ def test_decode_check_accepts_valid(L):
     (dict(D=96), 3), (dict(block_size=8), 3), (dict(Hq=24, Hkv=8), 3), (dict(Hq=32, Hkv=2), 3),
     (dict(q_dtype=binding.PA_F16), 3), (dict(out_dtype=binding.PA_BF16), 3),
     (dict(kv_dtype=binding.PA_FP8_E4M3, q_dtype=binding.PA_F32), 3), (dict(q_dtype=7), 3),
-    (dict(max_blocks_per_seq=64), 4),                 # 1024 tokens > one 512-token partition
+    (dict(workspace=0), 4), (dict(workspace_bytes=64), 4),   # the balanced schedule needs one
+    (dict(workspace=FAKE + 4), 2),                    # workspace must be 16-byte aligned
+    (dict(partition_size=512, max_blocks_per_seq=64, workspace=0), 4),   # 2 partitions
+    (dict(B=40000, max_blocks_per_seq=60000), 2),     # block count of the batch beyond int32
     (dict(kv_dtype=binding.PA_FP8_E4M3, q_dtype=binding.PA_BF16, out_dtype=binding.PA_BF16,
           k_scale=0.0), 2),
 ])
@@ -85,36 +89,48 @@ def test_decode_check_rejects(L, kw, status):
     assert check(L, **kw) == status
 
 
-def test_workspace_size_formula(L):
+def test_workspace_size_formula_fixed_partitions(L):
     a = valid_args(max_blocks_per_seq=64, partition_size=512)   # 1024 tokens -> 2 partitions
     assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 2 * (64 + 2)
     a = valid_args(max_blocks_per_seq=64, partition_size=256)   # 4 partitions
     assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 4 * (64 + 2)
-    a = valid_args(max_blocks_per_seq=64)       # small batch: the default falls to 256 tokens
-    assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 4 * (64 + 2)
-    a = valid_args(max_blocks_per_seq=15)       # 240 tokens fit one default partition
+    a = valid_args(max_blocks_per_seq=15, partition_size=256)   # 240 tokens: one partition
     assert L.pa_decode_workspace_size(ctypes.byref(a)) == 0
-
-
-@pytest.mark.parametrize("B,Hkv,bs,max_blocks,part", [
-    (256, 8, 16, 256, 1024),     # 70B-shaped layer: 2048 rows x 4 partitions
-    (64, 40, 16, 128, 512),      # 13B-shaped layer: 2 partitions of 1024 are too few
-    (16, 8, 16, 2048, 1024),     # long context: 128 rows x 32 partitions
-    (16, 8, 32, 1024, 1024),
-    (16, 8, 16, 1000, 512),      # 128 x 16 = 2048 waves at 1024 misses the target
-    (1, 1, 16, 64, 256),         # tiny: nothing reaches the target
-])
-def test_default_partition_choice(L, B, Hkv, bs, max_blocks, part):
-    a = valid_args(B=B, Hq=Hkv, Hkv=Hkv, D=128, block_size=bs, max_blocks_per_seq=max_blocks)
-    P = -(-(max_blocks * bs) // part)
-    want = 0 if P == 1 else 4 * B * Hkv * P * (128 + 2)
-    assert L.pa_decode_workspace_size(ctypes.byref(a)) == want
-    assert L.pa_decode_partition_size(ctypes.byref(a)) == part
-    a.partition_size = 64
-    assert L.pa_decode_partition_size(ctypes.byref(a)) == 64
-    assert L.pa_decode_partition_size(ctypes.byref(valid_args(Hq=6, Hkv=4))) == 0
     assert L.pa_decode_workspace_size(ctypes.byref(valid_args(Hq=6, Hkv=4))) == 0
     assert L.pa_decode_workspace_size(None) == 0
+
+
+def balanced_bytes(B, Hq, Hkv, D, nw):
+    """The balanced schedule's workspace: int32 prefix sums of B + 1 entries
+    (padded to 256 bytes), then fp32 partial rows (acc, m, l) for at most 4096
+    waves: head groups x work-groups per head group x 2 slots x KV heads per
+    work-group x G queries."""
+    hg = -(-Hkv // nw)
+    groups_cap = max(1, 4096 // (hg * nw))
+    rows = hg * groups_cap * 2 * nw * (Hq // Hkv)
+    return -(-(4 * (B + 1)) // 256) * 256 + 4 * rows * (D + 2)
+
+
+@pytest.mark.parametrize("kw,nw", [
+    (dict(), 8),                                                    # 8 KV heads, VALU: 4 per group
+    (dict(B=64, Hq=40, Hkv=40, D=128, max_blocks_per_seq=128), 4),  # 13B-shaped layer
+    (dict(B=256, Hq=64, Hkv=8, D=128, q_dtype=binding.PA_BF16, kv_dtype=binding.PA_BF16,
+          out_dtype=binding.PA_BF16, max_blocks_per_seq=256), 8),   # 70B GQA: MFMA kernel
+    (dict(B=16, Hq=32, Hkv=8, D=128, q_dtype=binding.PA_BF16, kv_dtype=binding.PA_FP8_E4M3,
+          out_dtype=binding.PA_BF16, k_scale=0.1, v_scale=0.1, max_blocks_per_seq=2048), 8),
+    (dict(B=3, Hq=2, Hkv=2, D=64), 2),
+])
+def test_workspace_size_formula_balanced(L, kw, nw):
+    a = valid_args(**kw)
+    want = balanced_bytes(a.B, a.Hq, a.Hkv, a.D, min(nw, 4 if a.Hq // a.Hkv <= 2 else 8))
+    assert L.pa_decode_workspace_size(ctypes.byref(a)) == want
+    assert L.pa_decode_partition_size(ctypes.byref(a)) == 0      # balanced: no fixed partition
+
+
+def test_partition_size_query(L):
+    a = valid_args(partition_size=64)
+    assert L.pa_decode_partition_size(ctypes.byref(a)) == 64
+    assert L.pa_decode_partition_size(ctypes.byref(valid_args(Hq=6, Hkv=4))) == 0
 
 
 def test_decode_with_bad_args_enqueues_nothing(L):

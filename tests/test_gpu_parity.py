@@ -97,6 +97,58 @@ def test_edge_lengths(name):
     assert np.array_equal(out[0], np.zeros_like(out[0])), "L = 0 must give zeros"
 
 
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "long_fp8", "long_fp8_bs32"])
+@pytest.mark.parametrize("shape", ["one_long", "many_short"])
+def test_balanced_schedule_extremes(name, shape):
+    """The default (balanced) schedule: one long sequence split over every
+    work-group, and hundreds of short ones (empty ones included) that several
+    per work-group cover whole."""
+    base = SMALL[name]
+    if shape == "one_long":
+        cfg = replace(base, B=1, lens=(6001,), len_range=(), pool_blocks=0)
+    else:
+        lens = tuple(int(x) for x in np.random.default_rng(3).integers(0, 40, 300))
+        cfg = replace(base, B=300, lens=lens, len_range=(), pool_blocks=0)
+    wl, step, exp = run_step(cfg, out_dtype="f32")
+    err = check_step(wl, step, exp, out_dtype="f32")
+    print(f"[ok] {name} {shape} max abs err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama13b", "shared", "llama70b", "long_fp8"])
+@pytest.mark.parametrize("part", [0, 64])
+def test_workspace_contents_never_read_unwritten(name, part):
+    """A workspace full of NaN bytes: every partial the reduce reads must
+    have been written by this step's partition kernel (the balanced schedule
+    with fewer blocks than work-groups included)."""
+    cfg = SMALL[name]
+    if part % cfg.block_size:
+        part = cfg.block_size
+    print(f"\n[case] poisoned workspace {name} part={part}", flush=True)
+    wl = workloads.make(cfg, device="cuda")
+    pre = parity.snapshot(wl)
+    step = DecodeStep(wl, partition_size=part, out_dtype="f32")
+    if step.workspace is not None:
+        step.workspace.fill_(0xFF)
+    step.run()
+    torch.cuda.synchronize()
+    exp = parity.oracle_step(wl, pre)
+    check_step(wl, step, exp, out_dtype="f32")
+
+
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "long_fp8"])
+def test_balanced_matches_fixed_partitions(name):
+    """Both schedules against the oracle, and against each other within the
+    tolerance (their summation orders differ)."""
+    cfg = SMALL[name]
+    wl, step, exp = run_step(cfg, out_dtype="f32")
+    a = parity.gpu_out(step.out)
+    check_step(wl, step, exp, out_dtype="f32")
+    wl2, step2, exp2 = run_step(cfg, partition_size=128, out_dtype="f32")
+    check_step(wl2, step2, exp2, out_dtype="f32")
+    b = parity.gpu_out(step2.out)
+    assert np.max(np.abs(a - b)) <= 2 * parity.TOL[cfg.kv_dtype]
+
+
 @pytest.mark.parametrize("name", ["tiny", "llama13b", "llama70b"])
 def test_single_token_returns_v_exactly(name):
     base = SMALL[name]
