@@ -90,11 +90,9 @@ typedef struct pa_decode_args {
   float scale;                 /* softmax scale, e.g. 1/sqrt(D)                       */
   float k_scale, v_scale;      /* fp8 dequantisation scales; must be 1 otherwise      */
   pa_dtype q_dtype, kv_dtype, out_dtype;
-  int32_t partition_size;      /* tokens per split-K partition, a multiple of         */
-                               /* block_size; 0 = library default (below)             */
-  void* workspace;             /* device scratch for split-K partials, 16-byte        */
-                               /* aligned: fp32 acc [P][B*Hq][D], then m and l        */
-                               /* [P][B*Hq] each                                      */
+  int32_t partition_size;      /* > 0: fixed split-K partitions of this many tokens,  */
+                               /* a multiple of block_size; 0: balanced schedule      */
+  void* workspace;             /* device scratch (layout below), 16-byte aligned      */
   size_t workspace_bytes;      /* >= pa_decode_workspace_size(args)                   */
 } pa_decode_args;
 
@@ -103,20 +101,32 @@ typedef struct pa_decode_args {
  *   (q, kv) in {(F32,F32), (F16,F16), (BF16,BF16), (BF16,FP8_E4M3),
  *   (F16,FP8_E4M3)}; out_dtype = q_dtype or PA_F32. */
 
-/* Default partition size (partition_size == 0): the largest of 1024 and 512
- * tokens for which n = ceil(max_blocks_per_seq*block_size / size) is at least
- * 4 and B * Hkv * n at least 4096, else 256.  It depends only on these
- * host-side sizes, never on the device contents.
+/* Schedules.
+ *   partition_size > 0 (fixed): one work-group per (KV heads, sequence,
+ *     partition of partition_size tokens).  P = ceil(max_blocks_per_seq *
+ *     block_size / partition_size) may not exceed 65535.  Workspace: fp32
+ *     acc [P][B*Hq][D], then m [P][B*Hq] and l [P][B*Hq]; 4*B*Hq*P*(D+2)
+ *     bytes, or none when P == 1.
+ *   partition_size == 0 (balanced, the default): a plan kernel sums the
+ *     sequences' block counts on the device, then one round of work-groups
+ *     splits the concatenation of all sequences' blocks into equal ranges,
+ *     so the work per work-group does not depend on the length mix.
+ *     Workspace: int32 block prefix sums [B+1] padded to a multiple of 256
+ *     bytes, then fp32 partials for rows = HG * W * 2 * NW * G:
+ *     acc [rows][D], m [rows], l [rows].  NW = KV heads per work-group
+ *     (the smallest power of two >= min(Hkv, 8) when G is 4 or 8 with a
+ *     16-bit query over a 16-bit or e4m3 cache, else min(Hkv, 4) rounded up
+ *     the same way), HG = ceil(Hkv / NW), W = max(1, floor(4096 / (HG*NW))).
+ * Workspace sizes depend only on these host-side sizes, never on device
+ * contents.  Contents need not be initialised and are overwritten.
  *
- * Bytes of workspace pa_decode needs: 4*B*Hq*P*(D+2) with
- * P = ceil(max_blocks_per_seq*block_size / partition_size), or 0 when one
- * partition covers every sequence.  P may not exceed 65535.  Returns 0 for
- * invalid arguments. */
+ * Bytes of workspace pa_decode needs for these arguments; 0 for invalid
+ * arguments (and for a fixed schedule with P == 1). */
 size_t pa_decode_workspace_size(const pa_decode_args* a);
 
-/* Tokens per split-K partition pa_decode will use for these arguments
- * (partition_size, or the default above when it is 0); 0 for invalid
- * arguments.  Host only. */
+/* Tokens per fixed split-K partition pa_decode will use for these arguments
+ * (partition_size); 0 for the balanced schedule and for invalid arguments.
+ * Host only. */
 int32_t pa_decode_partition_size(const pa_decode_args* a);
 
 /* Validate decode arguments without touching the GPU. */
@@ -134,16 +144,17 @@ pa_status pa_decode_check(const pa_decode_args* a);
  * Equivalent to pa_decode_partition followed by pa_decode_reduce. */
 pa_status pa_decode(const pa_decode_args* a, void* stream);
 
-/* Split-K step 1: one work-group per (sequence, KV head, partition of
- * partition_size tokens) computes the partition's running max m, sum l and
- * unnormalised V-weighted sum with an online softmax.  Sequences that fit in
- * one partition are finished here (out written); others leave fp32 partials
- * in the workspace. */
+/* Split-K step 1 (with the plan kernel first under the balanced schedule):
+ * each work-group computes, for each piece of a sequence it covers, the
+ * piece's running max m, sum l and unnormalised V-weighted sum with an
+ * online softmax.  Sequences covered by one work-group are finished here
+ * (out written); others leave fp32 partials in the workspace. */
 pa_status pa_decode_partition(const pa_decode_args* a, void* stream);
 
-/* Split-K step 2: for sequences longer than one partition, combine the
- * partials: M = max_p m_p, out = sum_p e^(m_p-M) acc_p / sum_p e^(m_p-M) l_p.
- * Enqueues nothing when one partition covers every sequence. */
+/* Split-K step 2: for sequences split between work-groups, combine the
+ * partials: M = max_p m_p, out = sum_p e^(m_p-M) acc_p / sum_p e^(m_p-M) l_p;
+ * under the balanced schedule it also writes zeros for sequences with
+ * seq_lens 0.  Enqueues nothing for a fixed schedule with P == 1. */
 pa_status pa_decode_reduce(const pa_decode_args* a, void* stream);
 
 /* Slot of each sequence's new token (P1 "Sayfalama Nasıl Çalışır", code

@@ -86,12 +86,6 @@ __host__ __device__ inline int balanced_owner(int64_t F, int64_t x, int n) {
 // workspace (16 waves on each of 256 compute units).
 constexpr int64_t kBalancedMaxWaves = 4096;
 
-// The default split-K partition size aims for at least kTargetWaves waves (a
-// few rounds of the 256 compute units of a gfx950 part) and at least
-// kMinPartitions partitions of the longest sequence the table can hold.
-constexpr int64_t kTargetWaves = 4096;
-constexpr int64_t kMinPartitions = 4;
-
 // Grid limit on the partition axis (grid y).
 constexpr int32_t kMaxPartitions = 65535;
 
