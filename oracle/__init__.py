@@ -34,7 +34,9 @@ Modules:
 * :mod:`oracle.fp8` -- the OCP e4m3 ("fn") codec, written from the format's
   definition; the encoder rounds to nearest-even and saturates.
 * :mod:`oracle.paged` -- slot mapping, the cache write, the block copy, the
-  gather through the block table and float64 softmax attention.
+  gather through the block table and float64 softmax attention: decode (one
+  new token per sequence) and prefill (several new tokens per sequence,
+  causal).
 * :mod:`oracle.blocks` -- the host-side block bookkeeping the pages describe:
   FIFO free list, per-block reference counts, allocation of a new block only
   when the last one is full, and copy-on-write of shared blocks.

@@ -158,3 +158,66 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables: 
         for g in range(Hkv):
             out[b, g * G:(g + 1) * G] = attend(q[b, g * G:(g + 1) * G], kb[:, g, :], vb[:, g, :], scale)
     return out
+
+
+def prefill_positions(q_starts: np.ndarray, seq_lens: np.ndarray, b: int):
+    """Positions of sequence ``b``'s new tokens: the last n = q_starts[b+1] -
+    q_starts[b] of its seq_lens[b] tokens, i.e. L - n, ..., L - 1.
+
+    The tokens before them (L - n of them) are context already in the cache:
+    an earlier chunk of the same prompt, or prefix blocks shared with other
+    requests (P1 "Diziler Arasında Blokları Paylaşma", prompt caching).
+    """
+    n = int(q_starts[b + 1]) - int(q_starts[b])
+    L = int(seq_lens[b])
+    return np.arange(L - n, L, dtype=np.int64)
+
+
+def prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables: np.ndarray,
+            seq_lens: np.ndarray, q_starts: np.ndarray, block_size: int, scale: float,
+            seqs=None, widen_k=None, widen_v=None) -> np.ndarray:
+    """Paged prefill attention for a batch (several new tokens per sequence),
+    float64.
+
+    ``q [T, Hq, D]`` packs the new tokens of all sequences: sequence b owns
+    rows ``q_starts[b] .. q_starts[b+1]-1``.  Their keys and values are
+    already in the pools, so sequence b's context holds ``seq_lens[b]``
+    tokens, the new ones last (:func:`prefill_positions`).  A new token at
+    position p attends to tokens 0..p of its sequence and to nothing later:
+    the model caches the keys and values of previous tokens for the next
+    ones (P1 "Çözdüğü Bellek Sorunu"), so a token sees itself and its past
+    (the causal reading; the pages print no mask).  Keys and values are
+    gathered through the block table (P1 "Sayfalama Nasıl Çalışır") and
+    each new token is attended exactly as :func:`attend` attends a decode
+    query over the first p + 1 tokens (P1 "İlgili Teknikler": the
+    FlashAttention-style kernels of current engines read paged blocks).
+    Grouped-query heads map as in :func:`decode`.
+
+    ``seqs`` restricts the work to some sequence indices (other rows NaN);
+    ``widen_k`` / ``widen_v`` as in :func:`decode`.
+    """
+    T, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    B = len(seq_lens)
+    out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+    for b in (range(B) if seqs is None else seqs):
+        pos = prefill_positions(q_starts, seq_lens, b)
+        if pos.size == 0:
+            continue
+        if pos[0] < 0:
+            raise ValueError("a sequence has more new tokens than tokens")
+        L = int(seq_lens[b])
+        kb = gather(k_pool, block_tables[b], L, block_size)
+        vb = gather(v_pool, block_tables[b], L, block_size)
+        kb = np.asarray(kb, dtype=np.float64) if widen_k is None else widen_k(kb)
+        vb = np.asarray(vb, dtype=np.float64) if widen_v is None else widen_v(vb)
+        r0 = int(q_starts[b])
+        for i, p in enumerate(pos):
+            seen = int(p) + 1
+            for g in range(Hkv):
+                heads = slice(g * G, (g + 1) * G)
+                out[r0 + i, heads] = attend(q[r0 + i, heads], kb[:seen, g, :], vb[:seen, g, :], scale)
+    return out

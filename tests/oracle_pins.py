@@ -210,6 +210,132 @@ def check_sharing_invariance(decode, seed=5):
 
 
 # --------------------------------------------------------------------------
+# prefill: causal attention of several new tokens per sequence
+# --------------------------------------------------------------------------
+
+def random_prefill(rng, Hq, Hkv, D, bs, lens, news):
+    """Random pools and scattered tables (float64, poisoned outside the valid
+    tokens) plus packed queries for ``news[b]`` new tokens per sequence."""
+    B = len(lens)
+    _, kp, vp, tables, lens = random_paged(rng, B, Hq, Hkv, D, bs, lens)
+    starts = np.concatenate([[0], np.cumsum(news)]).astype(np.int64)
+    q = rng.standard_normal((int(starts[-1]), Hq, D))
+    return q, kp, vp, tables, lens, starts
+
+
+def check_prefill_vs_sdpa(prefill, seed=21, Hq=6, Hkv=2, D=8, bs=4, lens=(1, 9, 16, 23), ctx=None):
+    """fp64 torch scaled_dot_product_attention on contiguous K/V (explicit slot
+    indexing).  Whole prompts (no context) use ``is_causal=True``; prompts
+    with ``ctx[b]`` tokens of context use the mask torch.tril(ones, ctx[b]),
+    which lets new token i see tokens 0 .. ctx[b] + i."""
+    rng = np.random.default_rng(seed)
+    ctx = ctx or (0,) * len(lens)
+    news = [L - c for L, c in zip(lens, ctx)]
+    q, kp, vp, tables, lens, starts = random_prefill(rng, Hq, Hkv, D, bs, lens, news)
+    scale = 0.43
+    out = prefill(q, kp, vp, tables, lens, starts, bs, scale)
+    G = Hq // Hkv
+    ks, vs = contiguous(kp, tables, lens, bs), contiguous(vp, tables, lens, bs)
+    for b, L in enumerate(lens):
+        n = news[b]
+        if n == 0:
+            continue
+        K = torch.from_numpy(ks[b]).permute(1, 0, 2).repeat_interleave(G, dim=0)    # [Hq, L, D]
+        V = torch.from_numpy(vs[b]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        Q = torch.from_numpy(q[starts[b]:starts[b + 1]]).permute(1, 0, 2)             # [Hq, n, D]
+        if ctx[b] == 0:
+            ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=scale)
+        else:
+            mask = torch.tril(torch.ones(n, int(L), dtype=torch.bool), diagonal=ctx[b])
+            ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(out[starts[b]:starts[b + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def check_prefill_rows_are_decodes(prefill, decode, seed=22, Hq=4, Hkv=2, D=8, bs=4,
+                                   lens=(7, 12, 30), news=(7, 3, 11)):
+    """New token i of sequence b at position p gives what a decode step gives
+    for a query at the end of the sequence's first p + 1 tokens (the same
+    gathered keys and values, no mask), up to rounding order."""
+    rng = np.random.default_rng(seed)
+    q, kp, vp, tables, lens, starts = random_prefill(rng, Hq, Hkv, D, bs, lens, news)
+    scale = 0.29
+    out = prefill(q, kp, vp, tables, lens, starts, bs, scale)
+    for b in range(len(lens)):
+        for i in range(news[b]):
+            r = int(starts[b]) + i
+            p = int(lens[b]) - news[b] + i
+            ref = decode(q[r:r + 1], kp, vp, tables[b:b + 1], np.array([p + 1]), bs, scale)
+            np.testing.assert_allclose(out[r], ref[0], rtol=1e-13, atol=1e-13, err_msg=str((b, i)))
+
+
+def check_prefill_bruteforce(prefill, seed=23, Hq=4, Hkv=2, D=3, bs=3, lens=(4, 8), news=(4, 3)):
+    """Pure-Python loops with math.exp over explicit slot indices."""
+    rng = np.random.default_rng(seed)
+    q, kp, vp, tables, lens, starts = random_prefill(rng, Hq, Hkv, D, bs, lens, news)
+    scale = 0.77
+    out = prefill(q, kp, vp, tables, lens, starts, bs, scale)
+    G = Hq // Hkv
+    for b in range(len(lens)):
+        for i in range(news[b]):
+            r = int(starts[b]) + i
+            last = int(lens[b]) - news[b] + i        # the newest token this query may see
+            for h in range(Hq):
+                g = h // G
+                rows = [(int(tables[b, t // bs]), t % bs) for t in range(last + 1)]
+                sc = [scale * sum(float(q[r, h, d]) * float(kp[blk, off, g, d]) for d in range(D))
+                      for blk, off in rows]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                for d in range(D):
+                    ref = sum(wt * float(vp[blk, off, g, d]) for wt, (blk, off) in zip(w, rows)) / sum(w)
+                    assert abs(out[r, h, d] - ref) <= 1e-12 * max(1.0, abs(ref)), (b, i, h, d)
+
+
+def check_prefill_chunking(prefill, seed=24, Hq=4, Hkv=4, D=8, bs=4, lens=(19, 26)):
+    """A prompt processed in two chunks (the first with the shorter length,
+    the second with the full one) gives the rows of one whole pass, bit for
+    bit, whatever the split."""
+    rng = np.random.default_rng(seed)
+    news = tuple(lens)
+    q, kp, vp, tables, lens, starts = random_prefill(rng, Hq, Hkv, D, bs, lens, news)
+    whole = prefill(q, kp, vp, tables, lens, starts, bs, 0.5)
+    for cut in (1, 5, 12, 18):
+        first, second = [], []
+        for b in range(len(lens)):
+            a = np.arange(int(starts[b]), int(starts[b]) + cut)
+            first.append(a)
+            second.append(np.arange(int(starts[b]) + cut, int(starts[b + 1])))
+        s1 = np.concatenate([[0], np.cumsum([len(a) for a in first])])
+        s2 = np.concatenate([[0], np.cumsum([len(a) for a in second])])
+        o1 = prefill(q[np.concatenate(first)], kp, vp, tables, np.full(len(lens), cut), s1, bs, 0.5)
+        o2 = prefill(q[np.concatenate(second)], kp, vp, tables, lens, s2, bs, 0.5)
+        assert np.array_equal(o1, whole[np.concatenate(first)]), cut
+        assert np.array_equal(o2, whole[np.concatenate(second)]), cut
+
+
+def check_prefill_first_token(prefill, seed=25, bs=4, D=8):
+    """The first token of a prompt sees only itself, so its output is its own
+    value row exactly; a prompt of identical keys averages the value rows it
+    sees (closed forms)."""
+    rng = np.random.default_rng(seed)
+    q, kp, vp, tables, lens, starts = random_prefill(rng, 2, 2, D, bs, (6, 10), (6, 10))
+    out = prefill(q, kp, vp, tables, lens, starts, bs, 0.6)
+    for b in range(2):
+        r = int(starts[b])
+        for h in range(2):
+            assert np.array_equal(out[r, h], vp[tables[b, 0], 0, h]), (b, h)
+    q, kp, vp, tables, lens, starts = random_prefill(rng, 1, 1, D, bs, (9,), (5,))
+    for t in range(9):
+        kp[tables[0, t // bs], t % bs, 0] = kp[tables[0, 0], 0, 0]
+    out = prefill(q, kp, vp, tables, lens, starts, bs, 0.6)
+    rows = np.stack([vp[tables[0, t // bs], t % bs, 0] for t in range(9)])
+    for i in range(5):
+        p = 4 + i
+        np.testing.assert_allclose(out[i, 0], rows[:p + 1].mean(axis=0), rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
 # e4m3 codec
 # --------------------------------------------------------------------------
 

@@ -211,3 +211,39 @@ def test_out_of_blocks_raises():
     blocks.allocate_sequence(pool, 16, 16)
     with pytest.raises(blocks.OutOfBlocks):
         blocks.allocate_sequence(pool, 1, 16)
+
+
+# ---------------------------------------------------------------- prefill
+
+def test_prefill_whole_prompts_match_causal_sdpa():
+    pins.check_prefill_vs_sdpa(paged.prefill)
+    pins.check_prefill_vs_sdpa(paged.prefill, seed=31, Hq=8, Hkv=1, D=16, bs=16, lens=(40, 17, 3))
+
+
+def test_prefill_with_context_matches_masked_sdpa():
+    pins.check_prefill_vs_sdpa(paged.prefill, lens=(9, 16, 23, 5), ctx=(8, 3, 10, 0))
+    pins.check_prefill_vs_sdpa(paged.prefill, seed=32, Hq=4, Hkv=4, D=8, bs=2, lens=(33, 12),
+                               ctx=(20, 11))
+
+
+def test_prefill_rows_are_decode_steps():
+    pins.check_prefill_rows_are_decodes(paged.prefill, paged.decode)
+
+
+def test_prefill_bruteforce():
+    pins.check_prefill_bruteforce(paged.prefill)
+
+
+def test_prefill_chunking_and_closed_forms():
+    pins.check_prefill_chunking(paged.prefill)
+    pins.check_prefill_first_token(paged.prefill)
+
+
+@settings(max_examples=20, deadline=None)
+@given(seed=st.integers(0, 10_000), G=st.sampled_from([1, 2, 4]), Hkv=st.integers(1, 2),
+       bs=st.sampled_from([1, 4, 16]), lens=st.lists(st.integers(1, 30), min_size=1, max_size=3),
+       frac=st.floats(0.0, 1.0))
+def test_prefill_matches_sdpa_random_shapes(seed, G, Hkv, bs, lens, frac):
+    ctx = tuple(int(frac * (L - 1)) for L in lens)
+    pins.check_prefill_vs_sdpa(paged.prefill, seed=seed, Hq=G * Hkv, Hkv=Hkv, D=8, bs=bs,
+                               lens=tuple(lens), ctx=ctx)

@@ -202,3 +202,66 @@ def test_block_mutants_are_caught(monkeypatch, mutant):
     monkeypatch.setattr(blocks, "append_slot", mutant)
     with pytest.raises(AssertionError):
         test_oracle_blocks.test_shared_stem_copy_order()
+
+
+def prefill_with(positions=None, seen=None, gmap=None, rows=None):
+    """The oracle's prefill with one part swapped for a mutant: the new
+    tokens' positions, how many tokens a query at position p sees, the GQA
+    head map, or which q row a new token reads."""
+    positions = positions or paged.prefill_positions
+    seen = seen or (lambda p, L: p + 1)
+    gmap = gmap or (lambda h, G, Hkv: h // G)
+    rows = rows or (lambda r0, i, n: r0 + i)
+
+    def prefill(q, kp, vp, tables, lens, starts, bs, scale, seqs=None):
+        T, Hq, D = q.shape
+        Hkv = kp.shape[2]
+        G = Hq // Hkv
+        out = np.full((T, Hq, D), np.nan)
+        for b in range(len(lens)):
+            pos = positions(starts, lens, b)
+            L = int(lens[b])
+            kb = paged.gather(kp, tables[b], L, bs)
+            vb = paged.gather(vp, tables[b], L, bs)
+            n = len(pos)
+            for i, p in enumerate(pos):
+                k = max(1, min(L, seen(int(p), L)))
+                for h in range(Hq):
+                    g = gmap(h, G, Hkv)
+                    out[int(starts[b]) + i, h] = paged.attend(q[rows(int(starts[b]), i, n), h:h + 1],
+                                                              kb[:k, g], vb[:k, g], scale)[0]
+        return out
+    return prefill
+
+
+def positions_top_left(starts, lens, b):
+    return np.arange(int(starts[b + 1]) - int(starts[b]))
+
+
+PREFILL_MUTANTS = {
+    "excludes itself": prefill_with(seen=lambda p, L: p),
+    "sees one token ahead": prefill_with(seen=lambda p, L: p + 2),
+    "no causal mask": prefill_with(seen=lambda p, L: L),
+    "positions from the chunk start": prefill_with(positions=positions_top_left),
+    "gqa head modulo": prefill_with(gmap=lambda h, G, Hkv: h % Hkv),
+    "rows reversed within a sequence": prefill_with(rows=lambda r0, i, n: r0 + n - 1 - i),
+}
+
+
+def prefill_pins(prefill):
+    pins.check_prefill_vs_sdpa(prefill)
+    pins.check_prefill_vs_sdpa(prefill, lens=(9, 16, 23, 5), ctx=(8, 3, 10, 0))
+    pins.check_prefill_rows_are_decodes(prefill, paged.decode)
+    pins.check_prefill_bruteforce(prefill)
+    pins.check_prefill_first_token(prefill)
+
+
+def test_real_prefill_passes_the_same_pins():
+    prefill_pins(prefill_with())
+    prefill_pins(paged.prefill)
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_MUTANTS))
+def test_prefill_mutant_is_caught(name):
+    with pytest.raises(AssertionError):
+        prefill_pins(PREFILL_MUTANTS[name])
