@@ -1,6 +1,6 @@
 /*
- * pa.h -- C ABI of libpa, the paged KV-cache decode path for AMD Instinct
- * MI355X (gfx950).
+ * pa.h -- C ABI of libpa, the paged KV-cache attention path for AMD Instinct
+ * MI355X (gfx950): decode, prefill and the cache-side kernels.
  *
  * Sources (web pages on PagedAttention, cited by title and section):
  *   P1  Ultralytics glossary page "PagedAttention" (Turkish): introduction;
@@ -193,6 +193,72 @@ pa_status pa_reshape_and_cache(const void* k_new, const void* v_new, void* k_cac
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int32_t P,
                          int32_t num_blocks, int32_t block_size, int32_t Hkv, int32_t D,
                          pa_dtype kv_dtype, void* stream);
+
+/* Arguments of one prefill call over a batch (one layer): several new
+ * tokens per sequence, attended causally over the paged context. */
+typedef struct pa_prefill_args {
+  void* out;                   /* [T][Hq][D] out_dtype; rows of new tokens written    */
+  const void* q;               /* [T][Hq][D] q_dtype: the new tokens of all           */
+                               /* sequences, packed in sequence order                 */
+  const void* k_cache;         /* [num_blocks][block_size][Hkv][D] kv_dtype           */
+  const void* v_cache;         /* same shape and dtype as k_cache                     */
+  const int32_t* block_tables; /* [B][max_blocks_per_seq]                             */
+  const int32_t* seq_lens;     /* [B]: tokens in context, the new ones included       */
+  const int32_t* q_starts;     /* [B+1]: sequence b owns q rows                       */
+                               /* q_starts[b] .. q_starts[b+1]-1                      */
+  int32_t B, T;                /* sequences; rows of q and out                        */
+  int32_t max_q_len;           /* >= every q_starts[b+1] - q_starts[b] (host bound    */
+                               /* that sizes the grid)                                */
+  int32_t Hq, Hkv, D;
+  int32_t block_size, num_blocks, max_blocks_per_seq;
+  float scale;                 /* softmax scale, e.g. 1/sqrt(D)                       */
+  float k_scale, v_scale;      /* fp8 dequantisation scales; must be 1 otherwise      */
+  pa_dtype q_dtype, kv_dtype, out_dtype;
+} pa_prefill_args;
+
+/* Supported prefill combinations (others return PA_ERR_UNSUPPORTED):
+ *   D in {64, 128}; block_size in {16, 32}; G = Hq/Hkv in {1, 2, 4, 8};
+ *   (q, kv) in {(F16,F16), (BF16,BF16), (BF16,FP8_E4M3), (F16,FP8_E4M3)};
+ *   out_dtype = q_dtype or PA_F32.  No workspace. */
+
+/* Validate prefill arguments without touching the GPU. */
+pa_status pa_prefill_check(const pa_prefill_args* a);
+
+/* Paged prefill attention (P1 "Çözdüğü Bellek Sorunu": the cache keeps
+ * earlier tokens' K/V for later tokens; P1 "Sayfalama Nasıl Çalışır": keys
+ * and values are gathered block by block through the table; P1 "İlgili
+ * Teknikler": FlashAttention-style kernels over paged blocks, grouped-query
+ * attention).  The new tokens' K and V must already be in the pools
+ * (pa_prefill_slot_mapping, then pa_reshape_and_cache over the T rows).
+ * Sequence b has n_b = q_starts[b+1] - q_starts[b] new tokens, the last n_b
+ * of its L = seq_lens[b] tokens; the earlier L - n_b are cached context (an
+ * earlier chunk, or shared prefix blocks).  New token i sits at position
+ * p = L - n_b + i, and for q row r = q_starts[b] + i and query head h, with
+ * g = h / (Hq/Hkv):
+ *   s_t = scale * k_scale * sum_d q[r,h,d] * K[t,g,d]          for t <= p
+ *   out[r,h,:] = v_scale * sum_{t<=p} exp(s_t - max s) V[t,g,:] / sum_{t<=p} exp(s_t - max s)
+ * K[t,g,:] as in pa_decode.  fp32 accumulation; the weights enter the
+ * weighted sum rounded to the 16-bit operand type (e4m3 caches compute in
+ * q_dtype).  Device-side: n_b is clamped to [0, min(max_q_len, L,
+ * T - q_starts[b])] (rows past it are not written); rows no sequence owns
+ * are not written; L is clamped as in pa_decode; block ids outside the pool
+ * are read as zeros. */
+pa_status pa_prefill(const pa_prefill_args* a, void* stream);
+
+/* Slots of the new tokens of a prefill batch (P1 "Sayfalama Nasıl
+ * Çalışır", code sketch): q row r of sequence b (q_starts[b] <= r <
+ * q_starts[b+1]) is new token i = r - q_starts[b] at position
+ * p = seq_lens[b] - n_b + i, and
+ *   slots[r] = block_tables[b][p / block_size] * block_size + p % block_size,
+ * or -1 when p < 0, when p / block_size >= max_blocks_per_seq, when that
+ * table entry is negative, or when no sequence owns row r.  q_starts must be
+ * nondecreasing; T > 0 with B == 0 returns PA_ERR_SHAPE.  All arrays in
+ * device memory: block_tables int32
+ * [B][max_blocks_per_seq], seq_lens [B], q_starts [B+1], slots [T]. */
+pa_status pa_prefill_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
+                                  const int32_t* q_starts, int32_t B, int32_t T,
+                                  int32_t max_blocks_per_seq, int32_t block_size, int32_t* slots,
+                                  void* stream);
 
 /* Static description of a status code. */
 const char* pa_status_str(pa_status s);

@@ -52,6 +52,21 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class PrefillArgs(ctypes.Structure):
+    """Mirror of ``pa_prefill_args``."""
+
+    _fields_ = [
+        ("out", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p), ("block_tables", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("q_starts", ctypes.c_void_p), ("B", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("scale", ctypes.c_float), ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float), ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
+        ("out_dtype", ctypes.c_int),
+    ]
+
+
 _lib = None
 
 
@@ -88,6 +103,13 @@ def lib() -> ctypes.CDLL:
     L.pa_reshape_and_cache.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     L.pa_copy_blocks.restype = ctypes.c_int
+    pargp = ctypes.POINTER(PrefillArgs)
+    L.pa_prefill_check.argtypes = [pargp]
+    L.pa_prefill_check.restype = ctypes.c_int
+    L.pa_prefill.argtypes = [pargp, vp]
+    L.pa_prefill.restype = ctypes.c_int
+    L.pa_prefill_slot_mapping.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    L.pa_prefill_slot_mapping.restype = ctypes.c_int
     L.pa_status_str.argtypes = [ctypes.c_int]
     L.pa_status_str.restype = ctypes.c_char_p
     L.pa_abi_version.argtypes = []
@@ -247,3 +269,62 @@ def copy_blocks(k_cache, v_cache, block_mapping, kv_dtype=None, stream=None):
     _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
                                 block_mapping.shape[0], NB, bs, Hkv, D, _pa_dtype(k_cache, kv_dtype),
                                 _stream(stream)), "pa_copy_blocks")
+
+
+def prefill_args(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, max_q_len, scale,
+                 k_scale=1.0, v_scale=1.0, kv_dtype=None) -> PrefillArgs:
+    """Build ``pa_prefill_args`` from tensors (shapes per include/pa.h).
+    ``max_q_len`` is a host integer: the most new tokens of any sequence."""
+    for t, n, nd in ((out, "out", 3), (q, "q", 3), (k_cache, "k_cache", 4), (v_cache, "v_cache", 4)):
+        _require(t, n, ndim=nd)
+    _require(block_tables, "block_tables", torch.int32, 2)
+    _require(seq_lens, "seq_lens", torch.int32, 1)
+    _require(q_starts, "q_starts", torch.int32, 1)
+    T, Hq, D = q.shape
+    NB, bs, Hkv, Dk = k_cache.shape
+    B = seq_lens.shape[0]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or Dk != D or tuple(out.shape) != (T, Hq, D):
+        raise ValueError("inconsistent shapes")
+    if block_tables.shape[0] != B or q_starts.shape[0] != B + 1:
+        raise ValueError("block_tables / q_starts batch mismatch")
+    a = PrefillArgs()
+    a.out, a.q, a.k_cache, a.v_cache = _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    a.block_tables, a.seq_lens, a.q_starts = _ptr(block_tables), _ptr(seq_lens), _ptr(q_starts)
+    a.B, a.T, a.max_q_len = B, T, int(max_q_len)
+    a.Hq, a.Hkv, a.D = Hq, Hkv, D
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = bs, NB, block_tables.shape[1]
+    a.scale, a.k_scale, a.v_scale = float(scale), float(k_scale), float(v_scale)
+    a.q_dtype = _pa_dtype(q)
+    a.kv_dtype = _pa_dtype(k_cache, kv_dtype)
+    a.out_dtype = _pa_dtype(out)
+    return a
+
+
+def prefill_check(args: PrefillArgs) -> int:
+    return int(lib().pa_prefill_check(ctypes.byref(args)))
+
+
+def prefill_run(args: PrefillArgs, stream=None) -> None:
+    _check(lib().pa_prefill(ctypes.byref(args), _stream(stream)), "pa_prefill")
+
+
+def prefill(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, max_q_len, scale,
+            k_scale=1.0, v_scale=1.0, kv_dtype=None, stream=None):
+    """pa_prefill on tensors."""
+    prefill_run(prefill_args(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, max_q_len,
+                             scale, k_scale, v_scale, kv_dtype), stream)
+    return out
+
+
+def prefill_slot_mapping(block_tables, seq_lens, q_starts, block_size, slots, stream=None):
+    _require(block_tables, "block_tables", torch.int32, 2)
+    _require(seq_lens, "seq_lens", torch.int32, 1)
+    _require(q_starts, "q_starts", torch.int32, 1)
+    _require(slots, "slots", torch.int32, 1)
+    B = seq_lens.shape[0]
+    if block_tables.shape[0] != B or q_starts.shape[0] != B + 1:
+        raise ValueError("batch mismatch")
+    _check(lib().pa_prefill_slot_mapping(_ptr(block_tables), _ptr(seq_lens), _ptr(q_starts), B,
+                                         slots.shape[0], block_tables.shape[1], int(block_size),
+                                         _ptr(slots), _stream(stream)), "pa_prefill_slot_mapping")
+    return slots

@@ -41,76 +41,9 @@
 #include "pa_decode_common.h"
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_mfma.h"
 
 namespace pa {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-
-// MFMA operand type (the query dtype): contractions, packing of fp32 weights
-// and widening of e4m3 codes.
-template <int MT>
-struct Mfma;
-
-template <>
-struct Mfma<PA_BF16> {
-  __device__ static f32x4 qk(const uint32_t* a, const uint32_t* b, f32x4 c) {
-    const u32x4 av = {a[0], a[1], a[2], a[3]};
-    const u32x4 bv = {b[0], b[1], b[2], b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                   __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
-  }
-  __device__ static f32x4 pv(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
-    const u32x2 av = {a0, a1};
-    const u32x2 bv = {b0, b1};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, av),
-                                                     __builtin_bit_cast(s16x4, bv), c, 0, 0, 0);
-  }
-  // two fp32 -> bf16 pair, round to nearest even
-  __device__ static uint32_t pack2(float x, float y) {
-    const bf16x2 v = {static_cast<__bf16>(x), static_cast<__bf16>(y)};
-    return __builtin_bit_cast(uint32_t, v);
-  }
-  // four e4m3 codes -> two dwords of bf16 pairs (exact)
-  __device__ static void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-  }
-};
-
-template <>
-struct Mfma<PA_F16> {
-  __device__ static f32x4 qk(const uint32_t* a, const uint32_t* b, f32x4 c) {
-    const u32x4 av = {a[0], a[1], a[2], a[3]};
-    const u32x4 bv = {b[0], b[1], b[2], b[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
-                                                  __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
-  }
-  __device__ static f32x4 pv(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
-    const u32x2 av = {a0, a1};
-    const u32x2 bv = {b0, b1};
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
-                                                 __builtin_bit_cast(f16x4, bv), c, 0, 0, 0);
-  }
-  __device__ static uint32_t pack2(float x, float y) {
-    const f16x2 v = {static_cast<_Float16>(x), static_cast<_Float16>(y)};
-    return __builtin_bit_cast(uint32_t, v);
-  }
-  __device__ static void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
-  }
-};
-
-// Half `sel` (0 = low, 1 = high) of dwords a and b, packed as (a_half, b_half).
-__device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int sel) {
-  return sel ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-}
 
 // KV heads (waves) per work-group
 constexpr int kMfmaHeads = 8;

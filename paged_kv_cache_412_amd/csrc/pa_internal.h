@@ -89,6 +89,37 @@ constexpr int64_t kBalancedMaxWaves = 4096;
 // Grid limit on the partition axis (grid y).
 constexpr int32_t kMaxPartitions = 65535;
 
+// Everything a prefill launch needs, resolved on the host.  Work-group
+// (sequence b, KV head, query tile) covers kPrefillRows rows of (new token,
+// query head of the KV head's group) pairs: 128 / G consecutive new tokens
+// of sequence b with all G query heads each.
+struct PrefillParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* q_starts;  // [B+1]
+  int32_t B, T, max_q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq;
+  int32_t q_tiles;          // query tiles per (sequence, KV head): ceil(max_q_len*G / 128)
+  int32_t total_groups;     // B * Hkv * q_tiles (the 1-D grid)
+  float qk_scale_log2;      // scale * k_scale * log2(e)
+  float v_scale;
+  int32_t out_dtype;
+};
+
+constexpr int kPrefillRows = 128;  // (token, head) rows per work-group: 4 waves x 32
+
+bool prefill_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t D, int32_t block_size,
+                    int32_t group);
+hipError_t launch_prefill(const PrefillParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
+                          hipStream_t stream, bool* supported);
+hipError_t launch_prefill_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
+                                       const int32_t* q_starts, int32_t B, int32_t T,
+                                       int32_t max_blocks, int32_t block_size, int32_t* slots,
+                                       hipStream_t stream);
+
 // Block copy: 16-byte chunks handled by one work-group (16 KiB).
 constexpr int kCopySliceChunks = 1024;
 

@@ -1,0 +1,423 @@
+// pa_prefill.hip -- paged prefill attention on the matrix cores (gfx950):
+// several new tokens per sequence, each attending causally to its
+// sequence's cached context and to the new tokens up to itself, with every
+// key and value read through the block table from the same paged pools the
+// decode step reads.
+//
+// P1 = Ultralytics glossary page "PagedAttention".  The cache holds earlier
+// tokens' K/V so later tokens can use them ("Çözdüğü Bellek Sorunu"); the
+// attention kernel gathers them block by block through the table ("Sayfalama
+// Nasıl Çalışır"); current engines run FlashAttention-style kernels over the
+// paged blocks, so the score matrix never reaches device memory ("İlgili
+// Teknikler"); grouped-query attention shares a KV head among G query heads
+// (same section).
+//
+// Work split.  A work-group of four waves owns 128 rows of (new token, query
+// head) pairs of one KV head: 128 / G consecutive new tokens of one sequence
+// with all G heads of the group, so every K/V tile it loads serves all of
+// them.  Wave w owns rows [32w, 32w + 32) as two 16-column MFMA tiles.  The
+// keys run in tiles of 32 (two 16-token blocks, or one 32-token block): the
+// work-group copies each tile's K and V rows from the pool into LDS (double
+// buffered, the next tile's global loads in flight during the current
+// tile's matrix work), and every wave reads its MFMA operands from there.
+//
+// Contractions (lane l, lo = l % 16, grp = l / 16; layouts in pa_mfma.h):
+//   S^T = K Q^T, one 16x16x32 MFMA per 32 head-dim values: A = 16 key rows
+//     (lane: key lo, head-dim run grp*D/4 + [0, D/4)), B = Q^T (lane: query
+//     row lo, the same run).  Lane l ends up with the scores of query row lo
+//     for keys 4*grp + r of each 16-key half.
+//   O^T += V^T P^T, one 16x16x32 MFMA per 16 head-dim rows: B = P^T straight
+//     from the score registers (slots e < 4: keys 4*grp + e of the first
+//     half, e >= 4: the same of the second half); A = V^T, where MFMA number
+//     mm maps row lo to head-dim d = (D/16)*lo + mm, so each lane reads one
+//     contiguous D/16-element run of each of its eight key rows and the 16
+//     lanes of a group read each row whole.  Lane l then holds output
+//     columns d = (D/16)*(4*grp + r) + mm of query row lo: D/4 contiguous
+//     values, stored with 16-byte writes.
+// Softmax runs in log2 units on the score layout.  The weights enter the
+// weighted sum rounded to the 16-bit operand type, and the running sum adds
+// up exactly those rounded weights, so the output is a weighted mean of V
+// rows (a dominant key returns its value row).  Each query's running
+// maximum may lag the true maximum by at most 8 (a factor 256): the
+// accumulators are rescaled only when a tile raises some maximum further
+// than that, which after the first tiles is rare.  The result does not
+// depend on the lag (sum 2^(s-m) v / sum 2^(s-m) is the same for any m),
+// and weights stay below 2^8, far inside the 16-bit operand range.
+
+#include <hip/hip_runtime.h>
+
+#include "pa_decode_common.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_mfma.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = kPrefillRows / 32;  // 32 rows per wave
+constexpr int kKeys = 32;                  // keys per LDS tile
+constexpr float kSlack = 8.f;              // allowed lag of the running max (log2 units)
+
+// XCD-aware order: the hardware deals consecutive work-groups round-robin to
+// the 8 XCDs, each with its own L2.  Map hardware index i to a logical index
+// so that each XCD receives one contiguous run of logical work-groups: the
+// query tiles of one (sequence, KV head), which read the same K/V, then share
+// an L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_logical(int i, int n) {
+  constexpr int X = 8;
+  const int q = n / X, r = n % X;
+  const int x = i % X, k = i / X;
+  return x * q + min(x, r) + k;
+}
+
+template <int KV, int Q, int D, int BS, int G>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillParams p) {
+  using M = Mfma<Q>;
+  constexpr int KVB = Elem<KV>::bytes;
+  constexpr int EPL = D / 16;              // head-dim values per lane and key row (PV)
+  constexpr int KK = D / 32;               // score MFMAs per 16-key half
+  constexpr int TOK = kPrefillRows / G;    // new tokens per work-group
+  constexpr int PITCH = D * 2 + 16;        // LDS bytes per key row (16-bit values + pad)
+  constexpr int TILE = kKeys * PITCH;
+  constexpr int CPR = D * KVB / 16;        // 16-byte global chunks per key row
+  constexpr int RPP = (kWaves * 64 / CPR) < kKeys ? (kWaves * 64 / CPR) : kKeys;
+  constexpr int PASSES = kKeys / RPP;      // staging loads per thread, K and V each
+  static_assert(kKeys % RPP == 0, "tile shape");
+  static_assert(G >= 1 && G <= 16 && (G & (G - 1)) == 0, "group size");
+  static_assert(EPL % 2 == 0, "head dim");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE];  // [buffer][K, V]
+
+  const int lid = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lo = lid & 15, grp = lid >> 4;
+
+  // ---- which (sequence, KV head, query tile); heavy (late) tiles first
+  const int logical = xcd_logical(blockIdx.x, p.total_groups);
+  const int qt = p.q_tiles - 1 - logical % p.q_tiles;
+  const int bh = logical / p.q_tiles;
+  const int kvh = bh % p.Hkv;
+  const int b = bh / p.Hkv;
+
+  const int qs = p.q_starts[b];
+  const int L = min(max(p.seq_lens[b], 0), p.max_blocks_per_seq * BS);
+  int n = min(p.q_starts[b + 1] - qs, p.max_q_len);
+  n = min(n, L);
+  n = (qs < 0 || qs > p.T) ? 0 : min(n, p.T - qs);  // rows stay inside q and out
+  const int t0 = qt * TOK;
+  if (t0 >= n) return;  // whole work-group, before any barrier
+  const int ntok = min(TOK, n - t0);
+  const int ctx = L - n;                   // cached tokens before the new ones
+  const int n_keys = ctx + t0 + ntok;      // keys the tile's last token sees
+  const int tiles = (n_keys + kKeys - 1) / kKeys;
+
+  // ---- this lane's two query rows (row -> token row / G, head row % G)
+  int pos[2];
+  bool valid[2];
+  size_t orow[2];
+  u32x4 qv[2][KK];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = wave * 32 + nt * 16 + lo;
+    const int tok = row / G;
+    valid[nt] = tok < ntok;
+    const int tk = min(tok, ntok - 1);  // rows past the tile repeat its last token
+    pos[nt] = ctx + t0 + tk;
+    orow[nt] = (static_cast<size_t>(qs + t0 + tk) * p.Hq + static_cast<size_t>(kvh) * G + row % G) * D;
+    const uint8_t* qp = static_cast<const uint8_t*>(p.q) + (orow[nt] + grp * (D / 4)) * 2;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qv[nt][kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk);
+  }
+  const int wtok0 = wave * 32 / G;
+  const bool wave_active = wtok0 < ntok;
+  const int pmin = ctx + t0 + wtok0;
+  const int pmax = ctx + t0 + min((wave * 32 + 31) / G, ntok - 1);
+
+  // ---- staging: thread -> (key row within the pass, 16-byte chunk)
+  const int64_t row_stride = static_cast<int64_t>(p.Hkv) * D * KVB;
+  const uint8_t* kbase = static_cast<const uint8_t*>(p.k_cache) + static_cast<int64_t>(kvh) * D * KVB;
+  const uint8_t* vbase = static_cast<const uint8_t*>(p.v_cache) + static_cast<int64_t>(kvh) * D * KVB;
+  const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+  const int srow = threadIdx.x / CPR, schunk = threadIdx.x % CPR;
+  const bool stager = srow < RPP;
+  u32x4 kst[PASSES], vst[PASSES];
+
+  auto fetch = [&](int j) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int key = j * kKeys + ps * RPP + srow;
+      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+      if (stager && key < n_keys) {
+        const int blk = table[key / BS];
+        if (blk >= 0 && blk < p.num_blocks) {
+          const int64_t off = (static_cast<int64_t>(blk) * BS + key % BS) * row_stride + schunk * 16;
+          kx = *reinterpret_cast<const u32x4*>(kbase + off);
+          vx = *reinterpret_cast<const u32x4*>(vbase + off);
+        }
+      }
+      kst[ps] = kx;
+      vst[ps] = vx;
+    }
+  };
+  auto stage = [&](int buf) {
+    if (!stager) return;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int r = ps * RPP + srow;
+      uint8_t* kd = &lds[buf][0][r * PITCH];
+      uint8_t* vd = &lds[buf][1][r * PITCH];
+      if constexpr (KVB == 2) {
+        *reinterpret_cast<u32x4*>(kd + schunk * 16) = kst[ps];
+        *reinterpret_cast<u32x4*>(vd + schunk * 16) = vst[ps];
+      } else {  // 16 e4m3 codes -> 16 operand values (exact), 32 bytes
+        uint32_t w[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          M::widen4(kst[ps][i], w[2 * i], w[2 * i + 1]);
+          M::widen4(vst[ps][i], w[8 + 2 * i], w[8 + 2 * i + 1]);
+        }
+        *reinterpret_cast<u32x4*>(kd + schunk * 32) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(kd + schunk * 32 + 16) = u32x4{w[4], w[5], w[6], w[7]};
+        *reinterpret_cast<u32x4*>(vd + schunk * 32) = u32x4{w[8], w[9], w[10], w[11]};
+        *reinterpret_cast<u32x4*>(vd + schunk * 32 + 16) = u32x4{w[12], w[13], w[14], w[15]};
+      }
+    }
+  };
+
+  const float c = p.qk_scale_log2;
+  const float ninf = -__builtin_huge_valf();
+  float m[2] = {kMaxInit, kMaxInit};  // running max of query row lo (log2 units)
+  float l[2] = {0.f, 0.f};            // this lane's share of the running sum
+  f32x4 o[2][EPL];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mm = 0; mm < EPL; ++mm) o[nt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  fetch(0);
+  stage(0);
+  __syncthreads();
+
+  for (int j = 0; j < tiles; ++j) {
+    const int k0 = j * kKeys;
+    if (j + 1 < tiles) fetch(j + 1);
+    if (wave_active && k0 <= pmax) {
+      const uint8_t* Kt = lds[j & 1][0];
+      const uint8_t* Vt = lds[j & 1][1];
+      // scores
+      f32x4 s[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 a =
+              *reinterpret_cast<const u32x4*>(Kt + (16 * kt + lo) * PITCH + grp * (D / 2) + 16 * kk);
+          s[kt][0] = M::mma32(a, qv[0][kk], s[kt][0]);
+          s[kt][1] = M::mma32(a, qv[1][kk], s[kt][1]);
+        }
+      }
+      // scale; mask keys after each query's position (only near the diagonal)
+      const bool diag = k0 + kKeys - 1 > pmin;
+      float mx[2] = {ninf, ninf};
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = s[kt][nt][r] * c;
+            if (diag && k0 + 16 * kt + 4 * grp + r > pos[nt]) x = ninf;
+            s[kt][nt][r] = x;
+            mx[nt] = fmaxf(mx[nt], x);
+          }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        mx[nt] = fmaxf(mx[nt], __shfl_xor(mx[nt], 16, 64));
+        mx[nt] = fmaxf(mx[nt], __shfl_xor(mx[nt], 32, 64));
+      }
+      if (__ballot(mx[0] > m[0] + kSlack || mx[1] > m[1] + kSlack)) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const float mn = fmaxf(m[nt], mx[nt]);
+          const float alpha = fast_exp2(m[nt] - mn);
+          m[nt] = mn;
+          l[nt] *= alpha;
+#pragma unroll
+          for (int mm = 0; mm < EPL; ++mm) o[nt][mm] *= alpha;
+        }
+      }
+      // weights, packed as the B operand of the weighted sum
+      u32x4 pb[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float w[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[kt][r] = fast_exp2(s[kt][nt][r] - m[nt]);
+        pb[nt] = u32x4{M::pack2(w[0][0], w[0][1]), M::pack2(w[0][2], w[0][3]),
+                       M::pack2(w[1][0], w[1][1]), M::pack2(w[1][2], w[1][3])};
+        // the sum takes the weights as rounded for the matrix cores, so the
+        // result is an exact weighted mean of V rows under those weights
+        l[nt] += (M::pair_sum(pb[nt][0]) + M::pair_sum(pb[nt][1])) +
+                 (M::pair_sum(pb[nt][2]) + M::pair_sum(pb[nt][3]));
+      }
+      // value rows: keys 4*grp + e (e < 4) and 16 + 4*grp + e - 4 (e >= 4)
+      uint32_t vr[8][EPL / 2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = (e < 4 ? 0 : 16) + 4 * grp + (e & 3);
+        const uint8_t* src = Vt + key * PITCH + EPL * lo * 2;
+        if constexpr (EPL == 8) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+          vr[e][0] = x[0];
+          vr[e][1] = x[1];
+          vr[e][2] = x[2];
+          vr[e][3] = x[3];
+        } else {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+          vr[e][0] = x[0];
+          vr[e][1] = x[1];
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < EPL; ++mm) {
+        const u32x4 a = {pick_halves(vr[0][mm / 2], vr[1][mm / 2], mm & 1),
+                         pick_halves(vr[2][mm / 2], vr[3][mm / 2], mm & 1),
+                         pick_halves(vr[4][mm / 2], vr[5][mm / 2], mm & 1),
+                         pick_halves(vr[6][mm / 2], vr[7][mm / 2], mm & 1)};
+        o[0][mm] = M::mma32(a, pb[0], o[0][mm]);
+        o[1][mm] = M::mma32(a, pb[1], o[1][mm]);
+      }
+    }
+    if (j + 1 < tiles) stage((j + 1) & 1);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float lt = l[nt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (!valid[nt]) continue;
+    // lt > 0: the running max never exceeds the largest score seen, whose
+    // weight 2^(s - m) is therefore about 1 or more
+    const float inv = p.v_scale / lt;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v[EPL];
+#pragma unroll
+      for (int mm = 0; mm < EPL; ++mm) v[mm] = o[nt][mm][r] * inv;
+      store_out_n<EPL>(p.out, orow[nt] + EPL * (4 * grp + r), v, p.out_dtype);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+template <int KV_, int Q_, int D_, int BS_, int G_>
+struct Tag {
+  static hipError_t launch(const PrefillParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((prefill_kernel<KV_, Q_, D_, BS_, G_>), dim3(p.total_groups),
+                       dim3(kWaves * 64), 0, s, p);
+    return hipGetLastError();
+  }
+};
+
+template <int KV, int Q, int D, int BS, typename F>
+bool by_group(int32_t G, F&& f) {
+  switch (G) {
+    case 1: f(Tag<KV, Q, D, BS, 1>{}); return true;
+    case 2: f(Tag<KV, Q, D, BS, 2>{}); return true;
+    case 4: f(Tag<KV, Q, D, BS, 4>{}); return true;
+    case 8: f(Tag<KV, Q, D, BS, 8>{}); return true;
+    default: return false;
+  }
+}
+
+template <int KV, int Q, int D, typename F>
+bool by_block(int32_t bs, int32_t G, F&& f) {
+  switch (bs) {
+    case 16: return by_group<KV, Q, D, 16>(G, f);
+    case 32: return by_group<KV, Q, D, 32>(G, f);
+    default: return false;
+  }
+}
+
+template <int KV, int Q, typename F>
+bool by_dim(int32_t D, int32_t bs, int32_t G, F&& f) {
+  switch (D) {
+    case 64: return by_block<KV, Q, 64>(bs, G, f);
+    case 128: return by_block<KV, Q, 128>(bs, G, f);
+    default: return false;
+  }
+}
+
+template <typename F>
+bool dispatch(pa_dtype q, pa_dtype kv, int32_t D, int32_t bs, int32_t G, F&& f) {
+  if (kv == PA_F16 && q == PA_F16) return by_dim<PA_F16, PA_F16>(D, bs, G, f);
+  if (kv == PA_BF16 && q == PA_BF16) return by_dim<PA_BF16, PA_BF16>(D, bs, G, f);
+  if (kv == PA_FP8_E4M3 && q == PA_BF16) return by_dim<PA_FP8_E4M3, PA_BF16>(D, bs, G, f);
+  if (kv == PA_FP8_E4M3 && q == PA_F16) return by_dim<PA_FP8_E4M3, PA_F16>(D, bs, G, f);
+  return false;
+}
+
+// ---------------------------------------------------------------- slot mapping
+
+// Slot of every new row: row r of sequence b (q_starts[b] <= r < q_starts[b+1])
+// is new token i = r - q_starts[b] at position seq_lens[b] - n_b + i.
+__global__ __launch_bounds__(256) void prefill_slot_mapping_kernel(
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ q_starts, int32_t B, int32_t T, int32_t max_blocks, int32_t bs,
+    int32_t* __restrict__ slots) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= T) return;
+  // last b with q_starts[b] <= r (binary search over the B + 1 starts)
+  int lo_b = 0, hi_b = B;  // invariant: answer in [lo_b, hi_b)
+  while (hi_b - lo_b > 1) {
+    const int mid = (lo_b + hi_b) >> 1;
+    if (q_starts[mid] <= r) lo_b = mid; else hi_b = mid;
+  }
+  const int b = lo_b;
+  int slot = -1;
+  const int s0 = q_starts[b], s1 = q_starts[b + 1];
+  if (s0 <= r && r < s1) {
+    const int64_t pos = static_cast<int64_t>(seq_lens[b]) - (s1 - s0) + (r - s0);
+    if (pos >= 0 && pos / bs < max_blocks) {
+      const int blk = tables[static_cast<size_t>(b) * max_blocks + pos / bs];
+      const int64_t s = static_cast<int64_t>(blk) * bs + pos % bs;
+      if (blk >= 0 && s <= INT32_MAX) slot = static_cast<int>(s);
+    }
+  }
+  slots[r] = slot;
+}
+
+}  // namespace
+
+bool prefill_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t D, int32_t block_size,
+                    int32_t group) {
+  return dispatch(q_dtype, kv_dtype, D, block_size, group, [](auto) {});
+}
+
+hipError_t launch_prefill(const PrefillParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,
+                          hipStream_t stream, bool* supported) {
+  hipError_t e = hipSuccess;
+  *supported = dispatch(q_dtype, kv_dtype, p.D, p.block_size, p.Hq / p.Hkv,
+                        [&](auto t) { e = decltype(t)::launch(p, stream); });
+  return e;
+}
+
+hipError_t launch_prefill_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
+                                       const int32_t* q_starts, int32_t B, int32_t T,
+                                       int32_t max_blocks, int32_t block_size, int32_t* slots,
+                                       hipStream_t stream) {
+  const int threads = 256;
+  hipLaunchKernelGGL(prefill_slot_mapping_kernel, dim3((T + threads - 1) / threads), dim3(threads),
+                     0, stream, block_tables, seq_lens, q_starts, B, T, max_blocks, block_size,
+                     slots);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -76,3 +76,53 @@ class DecodeStep:
         self.decode_partition(stream)
         self.decode_reduce(stream)
         return self.out
+
+
+class PrefillStep:
+    """One prefill call of the paged KV cache on the GPU, through the C ABI.
+
+    The sequences' tables already hold blocks for every new token (the host
+    block manager allocates them when the prompt is admitted).  A call:
+
+    1. ``pa_prefill_slot_mapping`` slot of every new token;
+    2. ``pa_reshape_and_cache``    write the new K/V rows to their slots;
+    3. ``pa_prefill``              causal paged attention of the new tokens.
+
+    All three are idempotent, so the prepared call can be replayed for timing.
+    """
+
+    def __init__(self, wl, out_dtype=None, device="cuda"):
+        cfg = wl.cfg
+        self.wl = wl
+        dev = torch.device(device)
+        width = max(1, max(len(r) for r in wl.tables))
+        self.tables_np = pad_tables(wl.tables, width)
+        self.block_tables = torch.from_numpy(self.tables_np).to(dev)
+        self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev)
+        self.q_starts = torch.from_numpy(wl.q_starts.astype(np.int32)).to(dev)
+        self.max_q_len = int(max(wl.news)) if len(wl.news) else 0
+        self.slots = torch.empty(wl.T, dtype=torch.int32, device=dev)
+        odt = out_dtype or cfg.out_dtype
+        self.out = torch.empty((wl.T, cfg.Hq, cfg.D), dtype=TORCH_DTYPE[odt], device=dev)
+        self.kv_dtype = cfg.kv_dtype
+        self.args = binding.prefill_args(self.out, wl.q, wl.k_pool, wl.v_pool, self.block_tables,
+                                         self.seq_lens, self.q_starts, self.max_q_len, wl.scale,
+                                         wl.k_scale, wl.v_scale, cfg.kv_dtype)
+
+    def slot_mapping(self, stream=None):
+        binding.prefill_slot_mapping(self.block_tables, self.seq_lens, self.q_starts,
+                                     self.wl.cfg.block_size, self.slots, stream)
+
+    def cache_write(self, stream=None):
+        wl = self.wl
+        binding.reshape_and_cache(wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, self.slots, wl.k_scale,
+                                  wl.v_scale, self.kv_dtype, stream)
+
+    def attention(self, stream=None):
+        binding.prefill_run(self.args, stream)
+
+    def run(self, stream=None):
+        self.slot_mapping(stream)
+        self.cache_write(stream)
+        self.attention(stream)
+        return self.out

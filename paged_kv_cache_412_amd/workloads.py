@@ -25,6 +25,16 @@ Workloads (shapes follow the pages' examples; P1 = Ultralytics glossary page
   8 KV heads, head dim 128, batch 16, lengths uniform in [16384, 32768],
   block size 16 or 32, bf16 queries and new rows.
 
+Prefill workloads (several new tokens per sequence, :func:`make_prefill`):
+
+* ``prefill13b`` -- the 13B layer shape, 16 whole prompts of 512..4096
+  tokens (no cached context), fp16.
+* ``prefill70b`` -- the 70B GQA shape, 16 chunks of 1,024 new tokens after
+  0..3072 cached tokens (chunked prefill, or a prompt behind a cached
+  prefix), bf16.
+* ``prefill_fp8`` -- GQA 32/8 with an e4m3 cache, 8 chunks of 2,048 new
+  tokens after 0..6144 cached tokens, bf16 queries.
+
 State handed to the step (the "pre-step" state): every sequence's cache holds
 its first L-1 tokens; the decode step appends token L-1 and then attends over
 all L tokens.  Tables hold ceil((L-1)/bs) blocks; the host block manager
@@ -74,6 +84,7 @@ class Config:
     slack: float = 0.10
     shared: dict = field(default_factory=dict)  # shared-prefix layout parameters
     partition_size: int = 512
+    prefill: dict = field(default_factory=dict)  # prefill: inclusive ranges "new", "ctx"
 
     @property
     def G(self) -> int:
@@ -99,6 +110,16 @@ CONFIGS = {
     "long_fp8_bs32": Config("long_fp8_bs32", 6, B=16, Hq=32, Hkv=8, D=128, block_size=32,
                             kv_dtype=E4M3, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
                             len_range=(16384, 32768)),
+    # prefill: several new tokens per sequence, causal over the paged context
+    "prefill13b": Config("prefill13b", 7, B=16, Hq=40, Hkv=40, D=128, block_size=16, kv_dtype=F16,
+                         q_dtype=F16, out_dtype=F16, src_dtype=F16,
+                         prefill=dict(new=(512, 4096), ctx=(0, 0))),
+    "prefill70b": Config("prefill70b", 8, B=16, Hq=64, Hkv=8, D=128, block_size=16, kv_dtype=BF16,
+                         q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
+                         prefill=dict(new=(1024, 1024), ctx=(0, 3072))),
+    "prefill_fp8": Config("prefill_fp8", 9, B=8, Hq=32, Hkv=8, D=128, block_size=16, kv_dtype=E4M3,
+                          q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
+                          prefill=dict(new=(2048, 2048), ctx=(0, 6144))),
 }
 
 
@@ -268,3 +289,99 @@ def pad_tables(tables: list, width: int) -> np.ndarray:
     for i, row in enumerate(tables):
         out[i, : len(row)] = row
     return out
+
+
+@dataclass
+class PrefillWorkload:
+    """State before one prefill call plus the new tokens' rows.
+
+    Sequence b holds ``ctx[b]`` cached tokens and receives ``news[b]`` new
+    ones, so ``seq_lens[b] = ctx[b] + news[b]``; its table already lists the
+    ceil(seq_lens[b] / bs) blocks of all of them (allocated FIFO from the
+    shuffled free list).  Device tensors: ``q [T,Hq,D]`` and ``k_new``/
+    ``v_new [T,Hkv,D]`` packed by sequence (``q_starts``), pools
+    ``[NB,bs,Hkv,D]`` holding the cached tokens.
+    """
+
+    cfg: Config
+    seq_lens: np.ndarray
+    news: np.ndarray
+    q_starts: np.ndarray
+    tables: list
+    num_blocks: int
+    q: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    scale: float = 0.0
+
+    @property
+    def T(self) -> int:
+        return int(self.q_starts[-1])
+
+    @property
+    def max_blocks(self) -> int:
+        bs = self.cfg.block_size
+        return max(1, max(-(-int(L) // bs) for L in self.seq_lens))
+
+
+def prefill_lengths(cfg: Config):
+    """(new tokens, cached tokens) per sequence: the first draws of the
+    config's generator, new counts first."""
+    rng = np.random.default_rng(cfg.seed)
+    lo, hi = cfg.prefill["new"]
+    news = rng.integers(lo, hi, size=cfg.B, endpoint=True).astype(np.int64)
+    lo, hi = cfg.prefill["ctx"]
+    ctx = rng.integers(lo, hi, size=cfg.B, endpoint=True).astype(np.int64)
+    return news, ctx, rng
+
+
+def make_prefill(cfg: Config, device="cpu", poison: bool = True, lengths=None) -> PrefillWorkload:
+    """Build the seeded pre-prefill state of ``cfg`` on ``device``.
+
+    Draw order: new counts, cached counts, free-list shuffle, then values
+    (K pool, V pool, new K rows, new V rows, q).  ``lengths`` = (news, ctx)
+    replaces the drawn counts (edge-case tests).  With ``poison`` the free
+    blocks, the new tokens' slots (the cache write fills them) and the slots
+    past each sequence's end are NaN (0x7F for e4m3)."""
+    news, ctx, rng = prefill_lengths(cfg)
+    if lengths is not None:
+        news = np.asarray(lengths[0], dtype=np.int64)
+        ctx = np.asarray(lengths[1], dtype=np.int64)
+        if len(news) != cfg.B or len(ctx) != cfg.B:
+            raise ValueError("lengths must give B entries each")
+    gen = torch.Generator(device=device).manual_seed(cfg.seed)
+    bs, Hkv, D, Hq = cfg.block_size, cfg.Hkv, cfg.D, cfg.Hq
+    lens = ctx + news
+    need = int(sum(_ceil_div(int(L), bs) for L in lens))
+    NB = cfg.pool_blocks or int(np.ceil(need * (1.0 + cfg.slack)))
+    free = [int(b) for b in rng.permutation(NB)]
+    tables = [[free.pop(0) for _ in range(_ceil_div(int(L), bs))] for L in lens]
+    k_pool, k_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device)
+    v_pool, v_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device)
+    if poison:
+        pv = _poison_value(cfg.kv_dtype)
+        used = np.zeros(NB, dtype=bool)
+        for row in tables:
+            used[row] = True
+        free_ids = torch.as_tensor(np.nonzero(~used)[0], device=device, dtype=torch.long)
+        k_pool.index_fill_(0, free_ids, pv)
+        v_pool.index_fill_(0, free_ids, pv)
+        for row, c in zip(tables, ctx):
+            c = int(c)
+            for j in range(c // bs, len(row)):   # blocks holding new tokens or nothing
+                first = c % bs if j == c // bs else 0
+                k_pool[row[j], first:] = pv
+                v_pool[row[j], first:] = pv
+    starts = np.concatenate([[0], np.cumsum(news)]).astype(np.int64)
+    T = int(starts[-1])
+    k_new, _ = _fill_values((T, Hkv, D), cfg.src_dtype, gen, device)
+    v_new, _ = _fill_values((T, Hkv, D), cfg.src_dtype, gen, device)
+    q, _ = _fill_values((T, Hq, D), cfg.q_dtype, gen, device)
+    return PrefillWorkload(cfg=cfg, seq_lens=lens, news=news, q_starts=starts, tables=tables,
+                           num_blocks=NB, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new,
+                           v_new=v_new, k_scale=k_scale, v_scale=v_scale,
+                           scale=1.0 / float(np.sqrt(D)))

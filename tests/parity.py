@@ -107,6 +107,57 @@ def oracle_step(wl, pre: PreStep, seqs=None) -> Expected:
     return Expected(tables, copies, slots, k, v, out)
 
 
+@dataclass
+class PrefillExpected:
+    slots: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    out: np.ndarray       # float64 [T, Hq, D], NaN rows for sequences not computed
+
+
+def prefill_row_tables(tables: np.ndarray, q_starts: np.ndarray) -> np.ndarray:
+    """The table row of the sequence owning each new row (for slot mapping)."""
+    owner = np.repeat(np.arange(len(q_starts) - 1), np.diff(q_starts))
+    return tables[owner]
+
+
+def prefill_table(wl) -> np.ndarray:
+    width = max(1, max(len(r) for r in wl.tables))
+    tab = np.full((len(wl.tables), width), -1, dtype=np.int64)
+    for i, r in enumerate(wl.tables):
+        tab[i, :len(r)] = r
+    return tab
+
+
+def prefill_slots(wl) -> np.ndarray:
+    """The oracle's slot of every new row: its sequence's table row at the
+    row's position."""
+    tab = prefill_table(wl)
+    positions = np.concatenate([paged.prefill_positions(wl.q_starts, wl.seq_lens, b)
+                                for b in range(len(wl.seq_lens))] or [np.zeros(0, np.int64)])
+    return paged.slot_mapping(prefill_row_tables(tab, wl.q_starts), positions, wl.cfg.block_size)
+
+
+def oracle_prefill(wl, pre: PreStep, seqs=None) -> PrefillExpected:
+    cfg = wl.cfg
+    bs = cfg.block_size
+    tab = prefill_table(wl)
+    slots = prefill_slots(wl)
+
+    def enc(rows, scale):
+        if cfg.src_dtype == cfg.kv_dtype:
+            return rows
+        return fp8.quantize(widen(rows, cfg.src_dtype), scale)
+
+    k = paged.write_cache(pre.k_pool, enc(pre.k_new, wl.k_scale), slots, bs)
+    v = paged.write_cache(pre.v_pool, enc(pre.v_new, wl.v_scale), slots, bs)
+    q = widen(pre.q, cfg.q_dtype)
+    out = paged.prefill(q, k, v, tab, wl.seq_lens, wl.q_starts, bs, wl.scale, seqs=seqs,
+                        widen_k=lambda x: widen(x, cfg.kv_dtype, wl.k_scale),
+                        widen_v=lambda x: widen(x, cfg.kv_dtype, wl.v_scale))
+    return PrefillExpected(slots, k, v, out)
+
+
 def gpu_out(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 

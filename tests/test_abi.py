@@ -23,6 +23,7 @@ def test_header_declares_the_path_entry_points():
     for n in ("pa_decode", "pa_decode_partition", "pa_decode_reduce", "pa_decode_workspace_size",
               "pa_decode_partition_size",
               "pa_decode_check", "pa_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
+              "pa_prefill", "pa_prefill_check", "pa_prefill_slot_mapping",
               "pa_status_str", "pa_abi_version"):
         assert n in names
 
@@ -153,3 +154,74 @@ def test_cache_and_copy_validation(L):
     assert L.pa_slot_mapping(vp, vp, 0, 4, 16, vp, None) == 0
     assert L.pa_slot_mapping(0, vp, 4, 4, 16, vp, None) == 1
     assert L.pa_slot_mapping(vp, vp, 4, 0, 16, vp, None) == 2
+
+
+# ---------------------------------------------------------------- prefill
+
+def valid_prefill(**kw):
+    a = binding.PrefillArgs()
+    a.out = a.q = a.k_cache = a.v_cache = a.block_tables = a.seq_lens = a.q_starts = FAKE
+    a.B, a.T, a.max_q_len = 4, 100, 40
+    a.Hq, a.Hkv, a.D = 8, 2, 128
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = 16, 64, 8
+    a.scale, a.k_scale, a.v_scale = 0.125, 1.0, 1.0
+    a.q_dtype = a.kv_dtype = a.out_dtype = binding.PA_BF16
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def pcheck(L, **kw):
+    return L.pa_prefill_check(ctypes.byref(valid_prefill(**kw)))
+
+
+def test_prefill_check_accepts_supported_combinations(L):
+    P = binding
+    for q, kv in ((P.PA_F16, P.PA_F16), (P.PA_BF16, P.PA_BF16), (P.PA_BF16, P.PA_FP8_E4M3),
+                  (P.PA_F16, P.PA_FP8_E4M3)):
+        for out in (q, P.PA_F32):
+            for D in (64, 128):
+                for bs in (16, 32):
+                    for Hq in (2, 4, 8, 16):
+                        assert pcheck(L, q_dtype=q, kv_dtype=kv, out_dtype=out, D=D, block_size=bs,
+                                      Hq=Hq) == 0, (q, kv, out, D, bs, Hq)
+
+
+def test_prefill_check_rejections(L):
+    P = binding
+    assert L.pa_prefill_check(None) == 1
+    assert pcheck(L, q=0) == 1
+    assert pcheck(L, q_starts=0) == 1
+    assert pcheck(L, out=FAKE + 8) == 2                                     # misaligned
+    assert pcheck(L, B=-1) == 2 and pcheck(L, T=-1) == 2 and pcheck(L, max_q_len=-1) == 2
+    assert pcheck(L, Hq=3) == 2                                             # Hq % Hkv
+    assert pcheck(L, Hq=6) == 3                                             # G = 3 not built
+    assert pcheck(L, Hq=32) == 3                                            # G = 16 not built
+    assert pcheck(L, D=96) == 3 and pcheck(L, block_size=8) == 3
+    assert pcheck(L, q_dtype=P.PA_F32, kv_dtype=P.PA_F32, out_dtype=P.PA_F32) == 3
+    assert pcheck(L, q_dtype=P.PA_F16, kv_dtype=P.PA_BF16) == 3
+    assert pcheck(L, out_dtype=P.PA_F16) == 3
+    assert pcheck(L, q_dtype=9) == 3
+    assert pcheck(L, scale=float("inf")) == 2
+    assert pcheck(L, k_scale=2.0) == 2                                      # 16-bit cache: scales 1
+    assert pcheck(L, kv_dtype=P.PA_FP8_E4M3, k_scale=0.0) == 2
+    assert pcheck(L, kv_dtype=P.PA_FP8_E4M3, v_scale=float("nan")) == 2
+    assert pcheck(L, kv_dtype=P.PA_FP8_E4M3, k_scale=0.02, v_scale=3.0) == 0
+    assert pcheck(L, max_blocks_per_seq=1 << 27, block_size=32) == 2       # tokens past int32
+    # grid: B * Hkv * ceil(max_q_len * G / 128) must fit in int32
+    assert pcheck(L, B=65535, Hkv=64, Hq=512, max_q_len=1 << 20) == 2
+    # nothing to do: no pointers needed
+    assert pcheck(L, T=0, q=0, out=0) == 0
+    assert pcheck(L, B=0, q=0, seq_lens=0) == 0
+
+
+def test_prefill_slot_mapping_rejections(L):
+    # every case returns before any launch
+    assert L.pa_prefill_slot_mapping(FAKE, FAKE, FAKE, -1, 4, 8, 16, FAKE, None) == 2
+    assert L.pa_prefill_slot_mapping(FAKE, FAKE, FAKE, 2, -1, 8, 16, FAKE, None) == 2
+    assert L.pa_prefill_slot_mapping(FAKE, FAKE, FAKE, 2, 4, 0, 16, FAKE, None) == 2
+    assert L.pa_prefill_slot_mapping(FAKE, FAKE, FAKE, 2, 4, 8, 0, FAKE, None) == 2
+    assert L.pa_prefill_slot_mapping(FAKE, FAKE, FAKE, 2, 4, 8, 16, None, None) == 1
+    assert L.pa_prefill_slot_mapping(None, FAKE, FAKE, 2, 4, 8, 16, FAKE, None) == 1
+    assert L.pa_prefill_slot_mapping(FAKE, FAKE, FAKE, 0, 4, 8, 16, FAKE, None) == 2
+    assert L.pa_prefill_slot_mapping(None, None, None, 0, 0, 8, 16, None, None) == 0
