@@ -132,34 +132,50 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
   const int pmin = ctx + t0 + wtok0;
   const int pmax = ctx + t0 + min((wave * 32 + 31) / G, ntok - 1);
 
-  // ---- staging: thread -> (key row within the pass, 16-byte chunk)
+  // ---- staging: thread -> (key row within the pass, 16-byte chunk).  The
+  // rows one wave stages in one pass lie in one block, so each wave reads
+  // them through one buffer resource over that block: absent blocks get a
+  // resource of 0 bytes and rows past the last key an offset past the end,
+  // and both read as zeros.  Every path thus issues the same loads, and the
+  // compiler's wait counts stay exact (loads retire in order).
+  constexpr int TB = kKeys / BS > 0 ? kKeys / BS : 1;  // blocks per key tile
+  constexpr int WROWS = 64 / CPR;                       // rows one wave stages per pass
+  static_assert(BS % WROWS == 0 || WROWS % BS == 0, "a wave's rows in one block");
+  static_assert(WROWS <= BS, "a wave's rows in one block");
   const int64_t row_stride = static_cast<int64_t>(p.Hkv) * D * KVB;
-  const uint8_t* kbase = static_cast<const uint8_t*>(p.k_cache) + static_cast<int64_t>(kvh) * D * KVB;
-  const uint8_t* vbase = static_cast<const uint8_t*>(p.v_cache) + static_cast<int64_t>(kvh) * D * KVB;
+  const uint32_t blk_bytes = static_cast<uint32_t>(row_stride * BS);
   const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+  const int nblk = (n_keys + BS - 1) / BS;  // table entries this work-group reads
+  const __amdgpu_buffer_rsrc_t trs = block_rsrc(table, static_cast<uint32_t>(nblk) * 4u);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int srow = threadIdx.x / CPR, schunk = threadIdx.x % CPR;
-  const bool stager = srow < RPP;
+  const bool wave_stages = wv * WROWS < RPP;  // uniform: whole waves stage or not
+  const int col = kvh * D * KVB + schunk * 16;
   u32x4 kst[PASSES], vst[PASSES];
-
-  auto fetch = [&](int j) {
+  // ids of the blocks of a tile, lane t < TB holding its t-th block
+  auto load_ids = [&](int j) {
+    return static_cast<int>(
+        __builtin_amdgcn_raw_buffer_load_b32(trs, (j * TB + (lid % TB)) * 4, 0, 0));
+  };
+  auto fetch = [&](int j, int ids) {
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
+      const int row0 = ps * RPP + wv * WROWS;          // first row this wave stages
+      const int blk = __builtin_amdgcn_readlane(ids, (row0 / BS) % TB);
+      const int key0 = j * kKeys + row0;
+      const bool ok = wave_stages && key0 < n_keys && blk >= 0 && blk < p.num_blocks;
+      const char* bbase = static_cast<const char*>(p.k_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
+      const char* vbase = static_cast<const char*>(p.v_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
+      const __amdgpu_buffer_rsrc_t kr = block_rsrc(bbase, ok ? blk_bytes : 0u);
+      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase, ok ? blk_bytes : 0u);
       const int key = j * kKeys + ps * RPP + srow;
-      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (stager && key < n_keys) {
-        const int blk = table[key / BS];
-        if (blk >= 0 && blk < p.num_blocks) {
-          const int64_t off = (static_cast<int64_t>(blk) * BS + key % BS) * row_stride + schunk * 16;
-          kx = *reinterpret_cast<const u32x4*>(kbase + off);
-          vx = *reinterpret_cast<const u32x4*>(vbase + off);
-        }
-      }
-      kst[ps] = kx;
-      vst[ps] = vx;
+      const int voff = key < n_keys ? static_cast<int>((key % BS) * row_stride) + col : 0x7fffff00;
+      kst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, voff, 0, 0));
+      vst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 0, 0));
     }
   };
   auto stage = [&](int buf) {
-    if (!stager) return;
+    if (!wave_stages) return;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int r = ps * RPP + srow;
@@ -193,13 +209,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
 #pragma unroll
     for (int mm = 0; mm < EPL; ++mm) o[nt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0);
+  int ids_next = load_ids(1);  // tile 1's blocks (consumed one iteration later)
+  fetch(0, load_ids(0));
   stage(0);
   __syncthreads();
 
   for (int j = 0; j < tiles; ++j) {
     const int k0 = j * kKeys;
-    if (j + 1 < tiles) fetch(j + 1);
+    // tile j+2's block ids, then tile j+1's rows: the same loads on every
+    // iteration (past the last tile they read zeros into a buffer no one reads)
+    const int ids = ids_next;
+    ids_next = load_ids(j + 2);
+    fetch(j + 1, ids);
     if (wave_active && k0 <= pmax) {
       const uint8_t* Kt = lds[j & 1][0];
       const uint8_t* Vt = lds[j & 1][1];
@@ -291,7 +312,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
         o[1][mm] = M::mma32(a, pb[1], o[1][mm]);
       }
     }
-    if (j + 1 < tiles) stage((j + 1) & 1);
+    stage((j + 1) & 1);
     __syncthreads();
   }
 
