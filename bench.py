@@ -34,6 +34,7 @@ KERNEL_SOURCES = ["paged_kv_cache_412_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_412_amd/csrc/pa_decode_mfma.hip",
                   "paged_kv_cache_412_amd/csrc/pa_decode_common.h",
                   "paged_kv_cache_412_amd/csrc/pa_device.h",
+                  "paged_kv_cache_412_amd/csrc/pa_mfma.h",
                   "paged_kv_cache_412_amd/csrc/pa_api.hip"]
 CALIBRATION_BYTES = 1 << 30  # size of the plain copy used to scale the PMC byte counters
 

@@ -33,6 +33,7 @@ struct Mfma;
 
 template <>
 struct Mfma<PA_BF16> {
+  static constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
   __device__ static f32x4 qk(const uint32_t* a, const uint32_t* b, f32x4 c) {
     const u32x4 av = {a[0], a[1], a[2], a[3]};
     const u32x4 bv = {b[0], b[1], b[2], b[3]};
@@ -65,6 +66,7 @@ struct Mfma<PA_BF16> {
 
 template <>
 struct Mfma<PA_F16> {
+  static constexpr uint32_t kOnePair = 0x3C003C00u;  // (1.0, 1.0) in f16
   __device__ static f32x4 qk(const uint32_t* a, const uint32_t* b, f32x4 c) {
     const u32x4 av = {a[0], a[1], a[2], a[3]};
     const u32x4 bv = {b[0], b[1], b[2], b[3]};
@@ -98,7 +100,8 @@ struct Mfma<PA_F16> {
 
 // Half `sel` (0 = low, 1 = high) of dwords a and b, packed as (a_half, b_half).
 __device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int sel) {
-  return sel ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+  // one v_perm_b32: bytes 0-3 index the second operand (a), 4-7 the first (b)
+  return __builtin_amdgcn_perm(b, a, sel ? 0x07060302u : 0x05040100u);
 }
 
 }  // namespace pa

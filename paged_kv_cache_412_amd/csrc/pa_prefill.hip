@@ -36,8 +36,9 @@
 //     values, stored with 16-byte writes.
 // Softmax runs in log2 units on the score layout.  The weights enter the
 // weighted sum rounded to the 16-bit operand type, and the running sum adds
-// up exactly those rounded weights, so the output is a weighted mean of V
-// rows (a dominant key returns its value row).  Each query's running
+// up exactly those rounded weights (one more MFMA per tile, against a row of
+// ones), so the output is a weighted mean of V rows (a dominant key returns
+// its value row).  Each query's running
 // maximum may lag the true maximum by at most 8 (a factor 256): the
 // accumulators are rescaled only when a tile raises some maximum further
 // than that, which after the first tiles is rare.  The result does not
@@ -57,6 +58,10 @@ namespace {
 constexpr int kWaves = kPrefillRows / 32;  // 32 rows per wave
 constexpr int kKeys = 32;                  // keys per LDS tile
 constexpr float kSlack = 8.f;              // allowed lag of the running max (log2 units)
+
+// Maximum of two scores without the quieting copies fmaxf costs in IEEE
+// mode (v_maximum3_f32 on gfx950).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // XCD-aware order: the hardware deals consecutive work-groups round-robin to
 // the 8 XCDs, each with its own L2.  Map hardware index i to a logical index
@@ -110,6 +115,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
   const int n_keys = ctx + t0 + ntok;      // keys the tile's last token sees
   const int tiles = (n_keys + kKeys - 1) / kKeys;
 
+  // Scores are scaled by c = scale * k_scale * log2(e) inside one fused
+  // multiply-add before the exponential.  A negative c is taken as |c| with
+  // the queries negated (exact for 16-bit values), so the running max can be
+  // taken over unscaled scores; c = 0 is taken as the smallest normal float
+  // (every weight still rounds to 1) so that masked scores stay -inf.
+  const float c_in = p.qk_scale_log2;
+  const uint32_t qflip = c_in < 0.f ? 0x80008000u : 0u;
+  const float c = fmaxf(fabsf(c_in), 1.17549435e-38f);
+
   // ---- this lane's two query rows (row -> token row / G, head row % G)
   int pos[2];
   bool valid[2];
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
     orow[nt] = (static_cast<size_t>(qs + t0 + tk) * p.Hq + static_cast<size_t>(kvh) * G + row % G) * D;
     const uint8_t* qp = static_cast<const uint8_t*>(p.q) + (orow[nt] + grp * (D / 4)) * 2;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qv[nt][kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk);
+    for (int kk = 0; kk < KK; ++kk) qv[nt][kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk) ^ qflip;
   }
   const int wtok0 = wave * 32 / G;
   const bool wave_active = wtok0 < ntok;
@@ -199,15 +213,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
     }
   };
 
-  const float c = p.qk_scale_log2;
   const float ninf = -__builtin_huge_valf();
   float m[2] = {kMaxInit, kMaxInit};  // running max of query row lo (log2 units)
-  float l[2] = {0.f, 0.f};            // this lane's share of the running sum
+  f32x4 l[2];                         // running sum of query row lo (four equal copies)
   f32x4 o[2][EPL];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < 2; ++nt) {
+    l[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mm = 0; mm < EPL; ++mm) o[nt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // A operand of all ones: ones x P^T sums the rounded weights of each query
+  // over the tile's 32 keys on the matrix cores (every row of the result)
+  const u32x4 ones = {M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair};
+  // byte addresses of the lanes l ^ 16 and l ^ 32 (the other groups' lanes of
+  // the same query column) for ds_bpermute
+  const int xor16 = (lid ^ 16) << 2, xor32 = (lid ^ 32) << 2;
 
   int ids_next = load_ids(1);  // tile 1's blocks (consumed one iteration later)
   fetch(0, load_ids(0));
@@ -238,24 +259,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
           s[kt][1] = M::mma32(a, qv[1][kk], s[kt][1]);
         }
       }
-      // scale; mask keys after each query's position (only near the diagonal)
-      const bool diag = k0 + kKeys - 1 > pmin;
-      float mx[2] = {ninf, ninf};
+      // mask keys after each query's position (only near the diagonal)
+      if (k0 + kKeys - 1 > pmin) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x = s[kt][nt][r] * c;
-            if (diag && k0 + 16 * kt + 4 * grp + r > pos[nt]) x = ninf;
-            s[kt][nt][r] = x;
-            mx[nt] = fmaxf(mx[nt], x);
-          }
+            for (int r = 0; r < 4; ++r)
+              if (k0 + 16 * kt + 4 * grp + r > pos[nt]) s[kt][nt][r] = ninf;
+      }
+      // tile max per query (unscaled, then scaled: c > 0).  IEEE maximum
+      // (v_maximum3_f32): the scores hold no signalling NaNs to quiet
+      float mx[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        mx[nt] = fmaxf(mx[nt], __shfl_xor(mx[nt], 16, 64));
-        mx[nt] = fmaxf(mx[nt], __shfl_xor(mx[nt], 32, 64));
+        float x = vmax(vmax(vmax(s[0][nt][0], s[0][nt][1]), s[0][nt][2]), s[0][nt][3]);
+        x = vmax(vmax(vmax(vmax(x, s[1][nt][0]), s[1][nt][1]), s[1][nt][2]), s[1][nt][3]);
+        x = vmax(x, u2f(__builtin_amdgcn_ds_bpermute(xor16, f2u(x))));
+        x = vmax(x, u2f(__builtin_amdgcn_ds_bpermute(xor32, f2u(x))));
+        mx[nt] = x * c;
       }
       if (__ballot(mx[0] > m[0] + kSlack || mx[1] > m[1] + kSlack)) {
 #pragma unroll
@@ -263,7 +286,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
           const float mn = fmaxf(m[nt], mx[nt]);
           const float alpha = fast_exp2(m[nt] - mn);
           m[nt] = mn;
-          l[nt] *= alpha;
+          l[nt] *= alpha;  // all four copies
 #pragma unroll
           for (int mm = 0; mm < EPL; ++mm) o[nt][mm] *= alpha;
         }
@@ -276,13 +299,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) w[kt][r] = fast_exp2(s[kt][nt][r] - m[nt]);
+          for (int r = 0; r < 4; ++r) w[kt][r] = fast_exp2(__builtin_fmaf(s[kt][nt][r], c, -m[nt]));
         pb[nt] = u32x4{M::pack2(w[0][0], w[0][1]), M::pack2(w[0][2], w[0][3]),
                        M::pack2(w[1][0], w[1][1]), M::pack2(w[1][2], w[1][3])};
         // the sum takes the weights as rounded for the matrix cores, so the
         // result is an exact weighted mean of V rows under those weights
-        l[nt] += (M::pair_sum(pb[nt][0]) + M::pair_sum(pb[nt][1])) +
-                 (M::pair_sum(pb[nt][2]) + M::pair_sum(pb[nt][3]));
+        l[nt] = M::mma32(ones, pb[nt], l[nt]);
       }
       // value rows: keys 4*grp + e (e < 4) and 16 + 4*grp + e - 4 (e >= 4)
       uint32_t vr[8][EPL / 2];
@@ -319,9 +341,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
   if (!wave_active) return;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    float lt = l[nt];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = l[nt][0];
     if (!valid[nt]) continue;
     // lt > 0: the running max never exceeds the largest score seen, whose
     // weight 2^(s - m) is therefore about 1 or more
