@@ -55,8 +55,10 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = kPrefillRows / 32;  // 32 rows per wave
-constexpr int kKeys = 32;                  // keys per LDS tile
+constexpr int kWaves = 4;                  // waves per work-group
+constexpr int kNT = kPrefillRows / (kWaves * 16);  // 16-column query tiles per wave
+constexpr int kKeys = kPrefillKeys;        // keys per LDS tile
+constexpr int kMinGroupsPerCU = kNT > 2 ? 1 : 2;
 constexpr float kSlack = 8.f;              // allowed lag of the running max (log2 units)
 
 // Maximum of two scores without the quieting copies fmaxf costs in IEEE
@@ -76,21 +78,36 @@ __device__ __forceinline__ int xcd_logical(int i, int n) {
 }
 
 template <int KV, int Q, int D, int BS, int G>
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(const PrefillParams p) {
   using M = Mfma<Q>;
   constexpr int KVB = Elem<KV>::bytes;
+  constexpr int NT = kNT;                  // 16-column query tiles per wave
+  constexpr int RW = 16 * NT;              // rows per wave
+  constexpr int KS = kKeys / 16;           // 16-key score tiles per key tile
+  constexpr int KP = kKeys / 32;           // 32-key weighted-sum steps per key tile
   constexpr int EPL = D / 16;              // head-dim values per lane and key row (PV)
-  constexpr int KK = D / 32;               // score MFMAs per 16-key half
+  constexpr int KK = D / 32;               // score MFMAs per 16-key tile
   constexpr int TOK = kPrefillRows / G;    // new tokens per work-group
-  constexpr int PITCH = D * 2 + 16;        // LDS bytes per key row (16-bit values + pad)
-  constexpr int TILE = kKeys * PITCH;
+  constexpr int CH = D / 8;                // 16-byte chunks per LDS row (16-bit values)
+  constexpr int ROWB = D * 2;              // LDS bytes per key row
+  constexpr int TILE = kKeys * ROWB;
   constexpr int CPR = D * KVB / 16;        // 16-byte global chunks per key row
   constexpr int RPP = (kWaves * 64 / CPR) < kKeys ? (kWaves * 64 / CPR) : kKeys;
   constexpr int PASSES = kKeys / RPP;      // staging loads per thread, K and V each
-  static_assert(kKeys % RPP == 0, "tile shape");
+  static_assert(kPrefillRows == kWaves * RW, "rows per work-group");
+  static_assert(kKeys % RPP == 0 && kKeys % 32 == 0, "tile shape");
   static_assert(G >= 1 && G <= 16 && (G & (G - 1)) == 0, "group size");
-  static_assert(EPL % 2 == 0, "head dim");
+  static_assert(EPL % 2 == 0 && (CH == 8 || CH == 16), "head dim");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE];  // [buffer][K, V]
+
+  // LDS placement of 16-byte chunk c of key row r: XOR-swizzled so that the
+  // 16 lanes that read one chunk column of 16 rows (K operands), the lanes
+  // that read one row whole (V operands) and the staging writes each touch
+  // distinct banks.
+  auto lds_off = [](int r, int c) {
+    const int sw = CH == 16 ? (r & 15) : ((r >> 1) & 7);
+    return r * ROWB + ((c ^ sw) << 4);
+  };
 
   const int lid = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -124,14 +141,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
   const uint32_t qflip = c_in < 0.f ? 0x80008000u : 0u;
   const float c = fmaxf(fabsf(c_in), 1.17549435e-38f);
 
-  // ---- this lane's two query rows (row -> token row / G, head row % G)
-  int pos[2];
-  bool valid[2];
-  size_t orow[2];
-  u32x4 qv[2][KK];
+  // ---- this lane's NT query rows (row -> token row / G, head row % G)
+  int pos[NT];
+  bool valid[NT];
+  size_t orow[NT];
+  u32x4 qv[NT][KK];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = wave * 32 + nt * 16 + lo;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = wave * RW + nt * 16 + lo;
     const int tok = row / G;
     valid[nt] = tok < ntok;
     const int tk = min(tok, ntok - 1);  // rows past the tile repeat its last token
@@ -141,10 +158,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qv[nt][kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk) ^ qflip;
   }
-  const int wtok0 = wave * 32 / G;
+  const int wtok0 = wave * RW / G;
   const bool wave_active = wtok0 < ntok;
   const int pmin = ctx + t0 + wtok0;
-  const int pmax = ctx + t0 + min((wave * 32 + 31) / G, ntok - 1);
+  const int pmax = ctx + t0 + min((wave * RW + RW - 1) / G, ntok - 1);
 
   // ---- staging: thread -> (key row within the pass, 16-byte chunk).  The
   // rows one wave stages in one pass lie in one block, so each wave reads
@@ -154,8 +171,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
   // compiler's wait counts stay exact (loads retire in order).
   constexpr int TB = kKeys / BS > 0 ? kKeys / BS : 1;  // blocks per key tile
   constexpr int WROWS = 64 / CPR;                       // rows one wave stages per pass
-  static_assert(BS % WROWS == 0 || WROWS % BS == 0, "a wave's rows in one block");
-  static_assert(WROWS <= BS, "a wave's rows in one block");
+  static_assert(WROWS <= BS && BS % WROWS == 0, "a wave's rows in one block");
   const int64_t row_stride = static_cast<int64_t>(p.Hkv) * D * KVB;
   const uint32_t blk_bytes = static_cast<uint32_t>(row_stride * BS);
   const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
@@ -178,10 +194,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
       const int blk = __builtin_amdgcn_readlane(ids, (row0 / BS) % TB);
       const int key0 = j * kKeys + row0;
       const bool ok = wave_stages && key0 < n_keys && blk >= 0 && blk < p.num_blocks;
-      const char* bbase = static_cast<const char*>(p.k_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
-      const char* vbase = static_cast<const char*>(p.v_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
-      const __amdgpu_buffer_rsrc_t kr = block_rsrc(bbase, ok ? blk_bytes : 0u);
-      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase, ok ? blk_bytes : 0u);
+      const char* kb = static_cast<const char*>(p.k_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
+      const char* vb = static_cast<const char*>(p.v_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
+      const __amdgpu_buffer_rsrc_t kr = block_rsrc(kb, ok ? blk_bytes : 0u);
+      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vb, ok ? blk_bytes : 0u);
       const int key = j * kKeys + ps * RPP + srow;
       const int voff = key < n_keys ? static_cast<int>((key % BS) * row_stride) + col : 0x7fffff00;
       kst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, voff, 0, 0));
@@ -193,38 +209,39 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int r = ps * RPP + srow;
-      uint8_t* kd = &lds[buf][0][r * PITCH];
-      uint8_t* vd = &lds[buf][1][r * PITCH];
+      uint8_t* kd = lds[buf][0];
+      uint8_t* vd = lds[buf][1];
       if constexpr (KVB == 2) {
-        *reinterpret_cast<u32x4*>(kd + schunk * 16) = kst[ps];
-        *reinterpret_cast<u32x4*>(vd + schunk * 16) = vst[ps];
-      } else {  // 16 e4m3 codes -> 16 operand values (exact), 32 bytes
+        *reinterpret_cast<u32x4*>(kd + lds_off(r, schunk)) = kst[ps];
+        *reinterpret_cast<u32x4*>(vd + lds_off(r, schunk)) = vst[ps];
+      } else {  // 16 e4m3 codes -> 16 operand values (exact), two chunks
         uint32_t w[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           M::widen4(kst[ps][i], w[2 * i], w[2 * i + 1]);
           M::widen4(vst[ps][i], w[8 + 2 * i], w[8 + 2 * i + 1]);
         }
-        *reinterpret_cast<u32x4*>(kd + schunk * 32) = u32x4{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<u32x4*>(kd + schunk * 32 + 16) = u32x4{w[4], w[5], w[6], w[7]};
-        *reinterpret_cast<u32x4*>(vd + schunk * 32) = u32x4{w[8], w[9], w[10], w[11]};
-        *reinterpret_cast<u32x4*>(vd + schunk * 32 + 16) = u32x4{w[12], w[13], w[14], w[15]};
+        *reinterpret_cast<u32x4*>(kd + lds_off(r, 2 * schunk)) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(kd + lds_off(r, 2 * schunk + 1)) = u32x4{w[4], w[5], w[6], w[7]};
+        *reinterpret_cast<u32x4*>(vd + lds_off(r, 2 * schunk)) = u32x4{w[8], w[9], w[10], w[11]};
+        *reinterpret_cast<u32x4*>(vd + lds_off(r, 2 * schunk + 1)) = u32x4{w[12], w[13], w[14], w[15]};
       }
     }
   };
 
   const float ninf = -__builtin_huge_valf();
-  float m[2] = {kMaxInit, kMaxInit};  // running max of query row lo (log2 units)
-  f32x4 l[2];                         // running sum of query row lo (four equal copies)
-  f32x4 o[2][EPL];
+  float m[NT];   // running max of query row lo (log2 units)
+  f32x4 l[NT];   // running sum of query row lo (four equal copies)
+  f32x4 o[NT][EPL];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = kMaxInit;
     l[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mm = 0; mm < EPL; ++mm) o[nt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // A operand of all ones: ones x P^T sums the rounded weights of each query
-  // over the tile's 32 keys on the matrix cores (every row of the result)
+  // over 32 keys on the matrix cores (every row of the result)
   const u32x4 ones = {M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair};
   // byte addresses of the lanes l ^ 16 and l ^ 32 (the other groups' lanes of
   // the same query column) for ds_bpermute
@@ -246,43 +263,47 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
       const uint8_t* Kt = lds[j & 1][0];
       const uint8_t* Vt = lds[j & 1][1];
       // scores
-      f32x4 s[2][2];
+      f32x4 s[KS][NT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[ks][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(Kt + (16 * kt + lo) * PITCH + grp * (D / 2) + 16 * kk);
-          s[kt][0] = M::mma32(a, qv[0][kk], s[kt][0]);
-          s[kt][1] = M::mma32(a, qv[1][kk], s[kt][1]);
+          const u32x4 a = *reinterpret_cast<const u32x4*>(Kt + lds_off(16 * ks + lo, grp * KK + kk));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) s[ks][nt] = M::mma32(a, qv[nt][kk], s[ks][nt]);
         }
       }
       // mask keys after each query's position (only near the diagonal)
       if (k0 + kKeys - 1 > pmin) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (k0 + 16 * kt + 4 * grp + r > pos[nt]) s[kt][nt][r] = ninf;
+              if (k0 + 16 * ks + 4 * grp + r > pos[nt]) s[ks][nt][r] = ninf;
       }
       // tile max per query (unscaled, then scaled: c > 0).  IEEE maximum
       // (v_maximum3_f32): the scores hold no signalling NaNs to quiet
-      float mx[2];
+      float mx[NT];
+      bool up = false;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float x = vmax(vmax(vmax(s[0][nt][0], s[0][nt][1]), s[0][nt][2]), s[0][nt][3]);
-        x = vmax(vmax(vmax(vmax(x, s[1][nt][0]), s[1][nt][1]), s[1][nt][2]), s[1][nt][3]);
+      for (int nt = 0; nt < NT; ++nt) {
+        float x = s[0][nt][0];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int r = (ks == 0 ? 1 : 0); r < 4; ++r) x = vmax(x, s[ks][nt][r]);
         x = vmax(x, u2f(__builtin_amdgcn_ds_bpermute(xor16, f2u(x))));
         x = vmax(x, u2f(__builtin_amdgcn_ds_bpermute(xor32, f2u(x))));
         mx[nt] = x * c;
+        up = up || mx[nt] > m[nt] + kSlack;
       }
-      if (__ballot(mx[0] > m[0] + kSlack || mx[1] > m[1] + kSlack)) {
+      if (__ballot(up)) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const float mn = fmaxf(m[nt], mx[nt]);
           const float alpha = fast_exp2(m[nt] - mn);
           m[nt] = mn;
@@ -291,47 +312,53 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
           for (int mm = 0; mm < EPL; ++mm) o[nt][mm] *= alpha;
         }
       }
-      // weights, packed as the B operand of the weighted sum
-      u32x4 pb[2];
+      // weighted sum, 32 keys at a time
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float w[2][4];
+      for (int kp = 0; kp < KP; ++kp) {
+        // weights, packed as the B operand: slots e < 4 are keys 4*grp + e of
+        // the first 16-key tile, e >= 4 the same of the second
+        u32x4 pb[NT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int nt = 0; nt < NT; ++nt) {
+          float w[2][4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) w[kt][r] = fast_exp2(__builtin_fmaf(s[kt][nt][r], c, -m[nt]));
-        pb[nt] = u32x4{M::pack2(w[0][0], w[0][1]), M::pack2(w[0][2], w[0][3]),
-                       M::pack2(w[1][0], w[1][1]), M::pack2(w[1][2], w[1][3])};
-        // the sum takes the weights as rounded for the matrix cores, so the
-        // result is an exact weighted mean of V rows under those weights
-        l[nt] = M::mma32(ones, pb[nt], l[nt]);
-      }
-      // value rows: keys 4*grp + e (e < 4) and 16 + 4*grp + e - 4 (e >= 4)
-      uint32_t vr[8][EPL / 2];
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = (e < 4 ? 0 : 16) + 4 * grp + (e & 3);
-        const uint8_t* src = Vt + key * PITCH + EPL * lo * 2;
-        if constexpr (EPL == 8) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(src);
-          vr[e][0] = x[0];
-          vr[e][1] = x[1];
-          vr[e][2] = x[2];
-          vr[e][3] = x[3];
-        } else {
-          const u32x2 x = *reinterpret_cast<const u32x2*>(src);
-          vr[e][0] = x[0];
-          vr[e][1] = x[1];
+            for (int r = 0; r < 4; ++r)
+              w[h][r] = fast_exp2(__builtin_fmaf(s[2 * kp + h][nt][r], c, -m[nt]));
+          pb[nt] = u32x4{M::pack2(w[0][0], w[0][1]), M::pack2(w[0][2], w[0][3]),
+                         M::pack2(w[1][0], w[1][1]), M::pack2(w[1][2], w[1][3])};
+          // the sum takes the weights as rounded for the matrix cores, so the
+          // result is an exact weighted mean of V rows under those weights
+          l[nt] = M::mma32(ones, pb[nt], l[nt]);
         }
-      }
+        // value rows: keys 32*kp + 4*grp + e (e < 4) and 32*kp + 16 + 4*grp + e - 4
+        uint32_t vr[8][EPL / 2];
 #pragma unroll
-      for (int mm = 0; mm < EPL; ++mm) {
-        const u32x4 a = {pick_halves(vr[0][mm / 2], vr[1][mm / 2], mm & 1),
-                         pick_halves(vr[2][mm / 2], vr[3][mm / 2], mm & 1),
-                         pick_halves(vr[4][mm / 2], vr[5][mm / 2], mm & 1),
-                         pick_halves(vr[6][mm / 2], vr[7][mm / 2], mm & 1)};
-        o[0][mm] = M::mma32(a, pb[0], o[0][mm]);
-        o[1][mm] = M::mma32(a, pb[1], o[1][mm]);
+        for (int e = 0; e < 8; ++e) {
+          const int key = 32 * kp + (e < 4 ? 0 : 16) + 4 * grp + (e & 3);
+          if constexpr (EPL == 8) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(Vt + lds_off(key, lo));
+            vr[e][0] = x[0];
+            vr[e][1] = x[1];
+            vr[e][2] = x[2];
+            vr[e][3] = x[3];
+          } else {
+            const u32x2 x =
+                *reinterpret_cast<const u32x2*>(Vt + lds_off(key, lo >> 1) + ((lo & 1) << 3));
+            vr[e][0] = x[0];
+            vr[e][1] = x[1];
+          }
+        }
+#pragma unroll
+        for (int mm = 0; mm < EPL; ++mm) {
+          const u32x4 a = {pick_halves(vr[0][mm / 2], vr[1][mm / 2], mm & 1),
+                           pick_halves(vr[2][mm / 2], vr[3][mm / 2], mm & 1),
+                           pick_halves(vr[4][mm / 2], vr[5][mm / 2], mm & 1),
+                           pick_halves(vr[6][mm / 2], vr[7][mm / 2], mm & 1)};
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[nt][mm] = M::mma32(a, pb[nt], o[nt][mm]);
+        }
       }
     }
     stage((j + 1) & 1);
@@ -340,7 +367,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(const PrefillPa
 
   if (!wave_active) return;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const float lt = l[nt][0];
     if (!valid[nt]) continue;
     // lt > 0: the running max never exceeds the largest score seen, whose
