@@ -2,7 +2,11 @@
 
 One step = the whole hot path over one batch: slot mapping, copy-on-write
 block copies (when the workload shares blocks), the cache write of one new
-token per sequence, the split-K decode partitions and their reduce.  Inputs
+token per sequence, the split-K decode partitions and their reduce.  With a
+prefill workload (``--workload prefill13b | prefill70b | prefill_fp8``) a
+step is the prefill path instead: slot mapping of every new token, the cache
+write, and causal paged attention, reported in algorithmic TFLOP/s against
+the matrix-core peak.  Inputs
 are seeded synthetic data already resident in HBM; the timed region holds
 exactly ``--steps`` steps between a synchronise and two HIP events.
 
@@ -29,19 +33,27 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 METRIC = "paged decode attention: effective KV GB/s and % of HBM peak; seqs/s per layer"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["paged_kv_cache_412_amd/csrc/pa_decode.hip",
-                  "paged_kv_cache_412_amd/csrc/pa_decode_valu.hip",
-                  "paged_kv_cache_412_amd/csrc/pa_decode_mfma.hip",
-                  "paged_kv_cache_412_amd/csrc/pa_decode_common.h",
-                  "paged_kv_cache_412_amd/csrc/pa_device.h",
-                  "paged_kv_cache_412_amd/csrc/pa_mfma.h",
-                  "paged_kv_cache_412_amd/csrc/pa_api.hip"]
+_COMMON_SOURCES = ["paged_kv_cache_412_amd/csrc/pa_device.h",
+                   "paged_kv_cache_412_amd/csrc/pa_mfma.h",
+                   "paged_kv_cache_412_amd/csrc/pa_decode_common.h",
+                   "paged_kv_cache_412_amd/csrc/pa_internal.h",
+                   "paged_kv_cache_412_amd/csrc/pa_api.hip"]
+# sources a kernel's measured counters depend on (the counters are dropped
+# when any of them changes)
+KERNEL_SOURCES = {
+    "decode": ["paged_kv_cache_412_amd/csrc/pa_decode.hip",
+               "paged_kv_cache_412_amd/csrc/pa_decode_valu.hip",
+               "paged_kv_cache_412_amd/csrc/pa_decode_mfma.hip"] + _COMMON_SOURCES,
+    "prefill": ["paged_kv_cache_412_amd/csrc/pa_prefill.hip"] + _COMMON_SOURCES,
+}
 CALIBRATION_BYTES = 1 << 30  # size of the plain copy used to scale the PMC byte counters
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense 16-bit matrix peak
 
 
-def kernel_hash() -> str:
+def kernel_hash(kernel: str) -> str:
+    family = "prefill" if kernel.startswith("prefill") else "decode"
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -54,10 +66,35 @@ def kv_bytes(wl) -> int:
 
 
 def decode_kernel_name(cfg) -> str:
-    """The partition kernel the library dispatches for this workload: the
-    matrix-core kernel for query groups of 4 or 8 over 16-bit or e4m3 caches,
+    """The dominant kernel the library dispatches for this workload: the
+    prefill kernel for prefill workloads; for decode, the matrix-core
+    partition kernel for query groups of 4 or 8 over 16-bit or e4m3 caches,
     the vector-ALU kernel otherwise."""
+    if cfg.prefill:
+        return "prefill_kernel"
     return "decode_mfma_kernel" if cfg.G in (4, 8) and cfg.kv_dtype != "f32" else "decode_valu_kernel"
+
+
+def prefill_flops(wl) -> int:
+    """Algorithmic flops of one prefill call: 4*D per (query head, visible
+    key) pair -- 2*D for the score, 2*D for the weighted sum -- over the
+    causal pairs: new token i of sequence b sees ctx_b + i + 1 keys."""
+    c = wl.cfg
+    pairs = 0
+    for n, L in zip(wl.news, wl.seq_lens):
+        n, L = int(n), int(L)
+        ctx = L - n
+        pairs += n * ctx + n * (n + 1) // 2
+    return 4 * c.D * c.Hq * pairs
+
+
+def prefill_bytes(wl) -> int:
+    """Bytes a prefill call must move at least: every sequence's L_b tokens
+    of K and V (all KV heads) read once, q read once, out written once."""
+    from paged_kv_cache_412_amd.workloads import ELEM_BYTES
+    c = wl.cfg
+    kv = int(np.sum(wl.seq_lens)) * 2 * c.Hkv * c.D * ELEM_BYTES[c.kv_dtype]
+    return kv + wl.T * c.Hq * c.D * (ELEM_BYTES[c.q_dtype] + ELEM_BYTES[c.out_dtype])
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -68,7 +105,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path, encoding="utf-8") as f:
         rec = json.load(f)
-    if rec.get("kernel_hash") != kernel_hash():
+    if rec.get("kernel_hash") != kernel_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -120,6 +157,119 @@ def cpu_baseline(wl, step, budget_s: float):
             "seconds": round(dt, 3), "seq_layers_per_s": round(len(done) / dt, 3)}
 
 
+def cpu_baseline_prefill(wl, step, budget_s: float):
+    """The oracle as it stands over a bounded sample of new tokens: each
+    sampled token's attention as a one-row prefill over its sequence's first
+    p + 1 tokens, all query heads."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+    from tests import parity
+
+    cfg = wl.cfg
+    k = parity.storage(wl.k_pool)
+    v = parity.storage(wl.v_pool)
+    q = parity.widen(parity.storage(wl.q), cfg.q_dtype)
+    tab = step.tables_np.astype(np.int64)
+    rows = np.random.default_rng(0).permutation(wl.T)
+    owner = np.searchsorted(wl.q_starts, rows, side="right") - 1
+    done, flops = 0, 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for r, b in zip(rows, owner):
+            pos = int(wl.seq_lens[b]) - int(wl.news[b]) + int(r - wl.q_starts[b])
+            paged.prefill(q[r:r + 1], k, v, tab[b:b + 1], np.array([pos + 1]), np.array([0, 1]),
+                          cfg.block_size, wl.scale,
+                          widen_k=lambda x: parity.widen(x, cfg.kv_dtype, wl.k_scale),
+                          widen_v=lambda x: parity.widen(x, cfg.kv_dtype, wl.v_scale))
+            done += 1
+            flops += 4 * cfg.D * cfg.Hq * (pos + 1)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {wl.T} new tokens (all {cfg.Hq} heads), {dt:.1f} s, "
+                      f"fp64 NumPy, BLAS limited to 1 thread",
+            "seconds": round(dt, 3)}
+
+
+def bench_prefill(args, cfg):
+    """Prefill workloads: one step = slot mapping, cache write and causal
+    paged attention of every sequence's new tokens."""
+    import torch
+
+    from paged_kv_cache_412_amd import workloads
+    from paged_kv_cache_412_amd.step import PrefillStep
+
+    print(f"[bench] building prefill workload {cfg.name}", file=sys.stderr, flush=True)
+    wl = workloads.make_prefill(cfg, device="cuda")
+    step = PrefillStep(wl)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    stages = ["slot_mapping", "cache_write", "attention"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, s in enumerate(stages):
+            getattr(step, s)()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, s in enumerate(stages)}
+    flops = prefill_flops(wl)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    attn_ms = stage_ms["attention"]
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS["bf16" if cfg.q_dtype == "bf16" else "f16"]
+    kernel = decode_kernel_name(cfg)
+    out = {
+        "metric": "paged prefill attention: algorithmic TFLOP/s and % of the MFMA peak; tokens/s per layer",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.q_dtype,
+        "accum_dtype": "f32",
+        "data": "synthetic (seeded N(0,1) queries, new rows and caches, scattered block tables)",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
+                   "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype,
+                   "new_tokens": f"U[{cfg.prefill['new'][0]},{cfg.prefill['new'][1]}]",
+                   "cached_tokens": f"U[{cfg.prefill['ctx'][0]},{cfg.prefill['ctx'][1]}]",
+                   "total_new_tokens": wl.T, "pool_blocks": wl.num_blocks},
+        "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
+        "flops_per_step": flops,
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(kernel, cfg.name),
+                     "algorithmic_bytes": prefill_bytes(wl), "avg_launch_ms": round(attn_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_prefill(wl, step, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +300,8 @@ def main(argv=None):
         return copy_calibration()
     binding.lib()
     cfg = workloads.CONFIGS[args.workload]
+    if cfg.prefill:
+        return bench_prefill(args, cfg)
     print(f"[bench] building workload {cfg.name}", file=sys.stderr, flush=True)
     wl = workloads.make(cfg, device="cuda")
     step = DecodeStep(wl, partition_size=args.partition_size)

@@ -88,7 +88,7 @@ def _counter_per_dispatch(path: str, counter: str) -> dict:
 
 
 def _short(name: str) -> str:
-    return name.split("(")[0].replace("void ", "")
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
 
 def summarize(workload: str, d: str) -> None:
@@ -124,11 +124,18 @@ def summarize(workload: str, d: str) -> None:
         if name.startswith(f"pa::{kernel}") and avg_us is None:
             avg_us = a
     kvb = bench_kv_bytes(cfg)
-    if avg_us:
+    if avg_us and cfg.prefill:
+        fl = bench_prefill_flops(cfg)
+        lines += ["", f"Algorithmic flops per launch: {fl} (4*D per query head and visible key); at the "
+                      f"average duration of `{kernel}` that is {fl / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s, "
+                      f"{100 * fl / (avg_us * 1e-6) / 2.5e15:.1f} % of the 2.5 PFLOP/s 16-bit matrix peak. "
+                      f"Bytes a launch must move at least (every sequence's K and V read once, "
+                      f"q read once, out written once): {kvb}."]
+    elif avg_us:
         lines += ["", f"Algorithmic KV bytes per launch: {kvb} (valid tokens' K and V); at the "
                       f"average duration of `{kernel}` that is {kvb / (avg_us * 1e-6) / 1e9:.1f} GB/s, "
                       f"{100 * kvb / (avg_us * 1e-6) / 8e12:.1f} % of 8 TB/s."]
-    rec = {"kernel": kernel, "workload": workload, "kernel_hash": bench.kernel_hash(),
+    rec = {"kernel": kernel, "workload": workload, "kernel_hash": bench.kernel_hash(kernel),
            "avg_launch_us": avg_us, "algorithmic_bytes": kvb}
     fetch = _find(d, f"pmc_FETCH_SIZE_{workload}_counter_collection.csv")
     write = _find(d, f"pmc_WRITE_SIZE_{workload}_counter_collection.csv")
@@ -168,7 +175,7 @@ def summarize(workload: str, d: str) -> None:
                   f"| calibration: 1 GiB copy (`{cname}`) FETCH / WRITE (KiB) | {cf_kib:.0f} / {cw_kib:.0f} |",
                   f"| scale factors fetch / write | {kf:.4f} / {kw:.4f} |",
                   f"| HBM bytes per launch (scaled) | {hbm:.4g} |",
-                  f"| algorithmic KV bytes per launch | {kvb:.4g} |",
+                  f"| algorithmic bytes per launch | {kvb:.4g} |",
                   f"| traffic / algorithmic | {hbm / kvb:.3f} |"]
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{kernel}_{workload}.md"), "w", encoding="utf-8") as f:
@@ -180,12 +187,29 @@ def summarize(workload: str, d: str) -> None:
 
 
 def bench_kv_bytes(cfg) -> int:
-    """Valid tokens' K and V bytes of the workload (its seeded lengths, no GPU)."""
+    """Algorithmic bytes of the workload's dominant kernel (its seeded
+    lengths, no GPU): for decode the valid tokens' K and V; for prefill
+    those plus q read once and out written once."""
     import numpy as np
 
     from paged_kv_cache_412_amd import workloads
-    lens = workloads.seq_lengths(cfg)
+    if cfg.prefill:
+        news, ctx, _ = workloads.prefill_lengths(cfg)
+        lens = news + ctx
+        qo = int(np.sum(news)) * cfg.Hq * cfg.D * (workloads.ELEM_BYTES[cfg.q_dtype] +
+                                                   workloads.ELEM_BYTES[cfg.out_dtype])
+        return int(np.sum(lens)) * 2 * cfg.Hkv * cfg.D * workloads.ELEM_BYTES[cfg.kv_dtype] + qo
+    else:
+        lens = workloads.seq_lengths(cfg)
     return int(np.sum(lens)) * 2 * cfg.Hkv * cfg.D * workloads.ELEM_BYTES[cfg.kv_dtype]
+
+
+def bench_prefill_flops(cfg) -> int:
+    """Algorithmic flops of the prefill workload (its seeded lengths, no GPU)."""
+    from paged_kv_cache_412_amd import workloads
+    news, ctx, _ = workloads.prefill_lengths(cfg)
+    pairs = sum(int(n) * int(c) + int(n) * (int(n) + 1) // 2 for n, c in zip(news, ctx))
+    return 4 * cfg.D * cfg.Hq * pairs
 
 
 def main(argv=None) -> int:
