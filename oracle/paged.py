@@ -85,6 +85,26 @@ def copy_blocks(pool: np.ndarray, pairs: np.ndarray) -> np.ndarray:
     return out
 
 
+def swap_blocks(src_pool: np.ndarray, dst_pool: np.ndarray, pairs: np.ndarray) -> np.ndarray:
+    """Return a copy of ``dst_pool`` with whole block ``src`` of ``src_pool``
+    copied over block ``dst`` for every ``(src, dst)`` row of ``pairs``.
+
+    P3 article A names page-granular eviction: single pages move between GPU
+    memory and CPU memory instead of whole sequences.  Moving a page out is
+    this copy from the device pool to a host pool, moving it back in is the
+    copy the other way; every byte of the block moves, unused tail slots
+    included.  Pairs naming a block outside either pool are skipped (a
+    reading; the pages are silent).  Precondition: the dst ids are distinct.
+    """
+    src = np.asarray(src_pool)
+    out = np.array(dst_pool, copy=True)
+    for s_id, d_id in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if not (0 <= s_id < src.shape[0] and 0 <= d_id < out.shape[0]):
+            continue
+        out[int(d_id)] = src[int(s_id)]
+    return out
+
+
 def gather(pool: np.ndarray, table_row: np.ndarray, length: int, block_size: int) -> np.ndarray:
     """A sequence's cache as a contiguous ``[L, Hkv, D]`` array.
 

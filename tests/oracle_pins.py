@@ -336,6 +336,49 @@ def check_prefill_first_token(prefill, seed=25, bs=4, D=8):
 
 
 # --------------------------------------------------------------------------
+# swap: blocks between a device pool and a host pool
+# --------------------------------------------------------------------------
+
+def check_swap_round_trip(swap_blocks, copy_blocks, seed=41):
+    """Swapping blocks out to a second pool and back in to fresh places
+    leaves their bytes intact (compared as raw bits, NaN patterns included);
+    every untouched block of either pool is unchanged; within one pool the
+    swap is the copy-on-write block copy; ids outside a pool are skipped."""
+    rng = np.random.default_rng(seed)
+    dev = rng.integers(0, 2**16, size=(20, 4, 2, 3), dtype=np.uint16)
+    host = rng.integers(0, 2**16, size=(12, 4, 2, 3), dtype=np.uint16)
+    dev0, host0 = dev.copy(), host.copy()
+    out_pairs = np.array([[3, 0], [17, 5], [8, 11], [0, 2]])
+    host2 = swap_blocks(dev, host, out_pairs)
+    assert np.array_equal(host, host0) and np.array_equal(dev, dev0), "inputs must not change"
+    for s_id, d_id in out_pairs:
+        assert np.array_equal(host2[d_id], dev[s_id]), (s_id, d_id)
+    moved = set(out_pairs[:, 1].tolist())
+    for b in range(host.shape[0]):
+        if b not in moved:
+            assert np.array_equal(host2[b], host[b]), b
+    assert np.array_equal(swap_blocks(dev, host, np.zeros((0, 2), dtype=np.int64)), host)
+    # back in, to other device blocks
+    in_pairs = np.array([[0, 19], [5, 1], [11, 4], [2, 9]])
+    dev2 = swap_blocks(host2, dev, in_pairs)
+    for (s_out, _), (_, d_in) in zip(out_pairs, in_pairs):
+        assert np.array_equal(dev2[d_in], dev[s_out]), (s_out, d_in)
+    back = set(in_pairs[:, 1].tolist())
+    for b in range(dev.shape[0]):
+        if b not in back:
+            assert np.array_equal(dev2[b], dev[b]), b
+    # one pool: the copy-on-write block copy
+    pairs = np.array([[1, 6], [2, 7], [13, 3]])
+    assert np.array_equal(swap_blocks(dev, dev, pairs), copy_blocks(dev, pairs))
+    # ids outside either pool are skipped
+    bad = np.array([[-1, 0], [20, 1], [0, 12], [4, -3], [5, 10]])
+    got = swap_blocks(dev, host, bad)
+    exp = host.copy()
+    exp[10] = dev[5]
+    assert np.array_equal(got, exp)
+
+
+# --------------------------------------------------------------------------
 # e4m3 codec
 # --------------------------------------------------------------------------
 

@@ -247,3 +247,9 @@ def test_prefill_matches_sdpa_random_shapes(seed, G, Hkv, bs, lens, frac):
     ctx = tuple(int(frac * (L - 1)) for L in lens)
     pins.check_prefill_vs_sdpa(paged.prefill, seed=seed, Hq=G * Hkv, Hkv=Hkv, D=8, bs=bs,
                                lens=tuple(lens), ctx=ctx)
+
+
+# ---------------------------------------------------------------- swap
+
+def test_swap_blocks_round_trip():
+    pins.check_swap_round_trip(paged.swap_blocks, paged.copy_blocks)

@@ -265,3 +265,28 @@ def test_real_prefill_passes_the_same_pins():
 def test_prefill_mutant_is_caught(name):
     with pytest.raises(AssertionError):
         prefill_pins(PREFILL_MUTANTS[name])
+
+
+def swap_shifted(src, dst, pairs):
+    return paged.swap_blocks(src, dst, np.asarray(pairs)[:, ::-1] if len(pairs) else pairs)
+
+
+def swap_no_bounds(src, dst, pairs):
+    out = np.array(dst, copy=True)
+    for s_id, d_id in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        out[int(d_id) % out.shape[0]] = src[int(s_id) % src.shape[0]]
+    return out
+
+
+def swap_in_place(src, dst, pairs):
+    out = np.asarray(dst)        # forgets to copy: the caller's array changes
+    for s_id, d_id in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= s_id < src.shape[0] and 0 <= d_id < out.shape[0]:
+            out[int(d_id)] = src[int(s_id)]
+    return out
+
+
+@pytest.mark.parametrize("mutant", [swap_shifted, swap_no_bounds, swap_in_place])
+def test_swap_mutants_are_caught(mutant):
+    with pytest.raises((AssertionError, IndexError)):
+        pins.check_swap_round_trip(mutant, paged.copy_blocks)
