@@ -45,13 +45,15 @@ KERNEL_SOURCES = {
                "paged_kv_cache_412_amd/csrc/pa_decode_valu.hip",
                "paged_kv_cache_412_amd/csrc/pa_decode_mfma.hip"] + _COMMON_SOURCES,
     "prefill": ["paged_kv_cache_412_amd/csrc/pa_prefill.hip"] + _COMMON_SOURCES,
+    "cache": ["paged_kv_cache_412_amd/csrc/pa_cache.hip"] + _COMMON_SOURCES,
 }
 CALIBRATION_BYTES = 1 << 30  # size of the plain copy used to scale the PMC byte counters
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense 16-bit matrix peak
 
 
 def kernel_hash(kernel: str) -> str:
-    family = "prefill" if kernel.startswith("prefill") else "decode"
+    family = ("prefill" if kernel.startswith("prefill") else
+              "cache" if kernel.startswith("copy_blocks") else "decode")
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -72,6 +74,8 @@ def decode_kernel_name(cfg) -> str:
     the vector-ALU kernel otherwise."""
     if cfg.prefill:
         return "prefill_kernel"
+    if cfg.swap:
+        return "copy_blocks_kernel"
     return "decode_mfma_kernel" if cfg.G in (4, 8) and cfg.kv_dtype != "f32" else "decode_valu_kernel"
 
 
@@ -270,6 +274,113 @@ def bench_prefill(args, cfg):
     return 0
 
 
+HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
+
+
+def bench_swap(args, cfg):
+    """Swap workloads: one step = evict N blocks (K and V) from the device
+    pools to pinned host pools, then restore them to other device blocks,
+    two pa_swap_blocks calls.  Bytes move over the host link both ways."""
+    import torch
+
+    from oracle import paged
+    from paged_kv_cache_412_amd import binding, workloads
+
+    print(f"[bench] building swap workload {cfg.name}", file=sys.stderr, flush=True)
+    wl = workloads.make_swap(cfg)
+    N = wl.out_pairs.shape[0]
+    nbytes = 2 * N * wl.block_bytes          # K and V, one direction
+    stream = torch.cuda.current_stream()
+
+    def out():
+        binding.swap_blocks(wl.k_dev, wl.v_dev, wl.k_host, wl.v_host, wl.out_map)
+
+    def back():
+        binding.swap_blocks(wl.k_host, wl.v_host, wl.k_dev, wl.v_dev, wl.in_map)
+
+    for _ in range(args.warmup):
+        out()
+        back()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        out()
+        ev[i][1].record(stream)
+        back()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    out_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    in_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_step = out_ms + in_ms
+    # the link's practical ceiling: the runtime's own pinned copies of the same bytes
+    dev_chunk = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    host_chunk = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    for _ in range(2):
+        host_chunk.copy_(dev_chunk, non_blocking=True)
+        dev_chunk.copy_(host_chunk, non_blocking=True)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    host_chunk.copy_(dev_chunk, non_blocking=True)
+    e[1].record(stream)
+    dev_chunk.copy_(host_chunk, non_blocking=True)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    copy_d2h, copy_h2d = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+    gbs = 2 * nbytes / (ms_step * 1e-3) / 1e9
+    out_gbs = nbytes / (out_ms * 1e-3) / 1e9
+    in_gbs = nbytes / (in_ms * 1e-3) / 1e9
+    res = {
+        "metric": "page-granular swap: GB/s over the host link (evict + restore), % of the link peak",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic (seeded N(0,1) fp16 pools, seeded random victim and target blocks)",
+        "config": {"workload": cfg.name, "blocks_each_way": N, "block_bytes_per_pool": wl.block_bytes,
+                   "block_size": cfg.block_size, "Hkv": cfg.Hkv, "D": cfg.D, "kv_dtype": cfg.kv_dtype,
+                   "bytes_each_way": nbytes},
+        "evict_gbs": round(out_gbs, 2),
+        "restore_gbs": round(in_gbs, 2),
+        "runtime_pinned_copy_gbs": {"d2h": round(nbytes / (copy_d2h * 1e-3) / 1e9, 2),
+                                    "h2d": round(nbytes / (copy_h2d * 1e-3) / 1e9, 2)},
+        "roofline": {"kernel": "copy_blocks_kernel", "bound": "host_link",
+                     "achieved": round(min(out_gbs, in_gbs), 2), "peak": HOST_LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(min(out_gbs, in_gbs) / HOST_LINK_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes,
+                     "avg_launch_ms": {"evict": round(out_ms, 5), "restore": round(in_ms, 5)}},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        kd = parity_storage(wl.k_dev)
+        kh = parity_storage(wl.k_host)
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < min(args.cpu_budget, 5.0) or done == 0:
+            paged.swap_blocks(kd, kh, wl.out_pairs)
+            done += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(done * N * wl.block_bytes / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{done} evictions of the K pool's {N} blocks in host memory, {dt:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def parity_storage(t):
+    from tests import parity
+    return parity.storage(t)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +413,8 @@ def main(argv=None):
     cfg = workloads.CONFIGS[args.workload]
     if cfg.prefill:
         return bench_prefill(args, cfg)
+    if cfg.swap:
+        return bench_swap(args, cfg)
     print(f"[bench] building workload {cfg.name}", file=sys.stderr, flush=True)
     wl = workloads.make(cfg, device="cuda")
     step = DecodeStep(wl, partition_size=args.partition_size)

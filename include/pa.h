@@ -30,7 +30,9 @@
  * Conventions:
  *   - Every call is a host function that validates its arguments, then
  *     enqueues kernels on `stream` (a hipStream_t; NULL = the default
- *     stream) and returns without synchronising.  The library never
+ *     stream) and returns without synchronising.  Validation reads only the
+ *     arguments, except pa_swap_blocks, which also asks the HIP runtime
+ *     which kind of memory each pool is.  The library never
  *     allocates, frees or synchronises device memory; it keeps no state
  *     except a per-device cache of the compute-unit count.
  *   - Host-side validation failures return a pa_status other than PA_OK,
@@ -192,6 +194,26 @@ pa_status pa_reshape_and_cache(const void* k_new, const void* v_new, void* k_cac
  * nothing. */
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int32_t P,
                          int32_t num_blocks, int32_t block_size, int32_t Hkv, int32_t D,
+                         pa_dtype kv_dtype, void* stream);
+
+/* Page-granular swap between two pools (P3 article A: single pages move
+ * between GPU memory and CPU memory instead of whole sequences).  For each of
+ * the P rows (src, dst) of block_mapping (int32 [P][2], device memory),
+ * copies the whole block src of the source pools (src_k, src_v; src_num_blocks
+ * blocks) over block dst of the destination pools (dst_k, dst_v;
+ * dst_num_blocks blocks), every slot and head, K and V.  Both sides have the
+ * block shape [block_size][Hkv][D] of kv_dtype.  Each pool is device memory
+ * or pinned host memory (hipHostMalloc, e.g. a pinned torch tensor), which
+ * the kernel reads or writes over the host link: eviction is device -> host,
+ * restore host -> device.  A pointer the GPU cannot reach (pageable host
+ * memory) returns PA_ERR_UNSUPPORTED; this check asks the HIP runtime about
+ * each pool pointer.  A destination pool overlapping a source pool, other
+ * than being the same pool, returns PA_ERR_SHAPE.  Pairs with an id outside
+ * its pool are skipped.  Precondition: dst ids distinct, and within one pool
+ * no dst is also a src.  P == 0 enqueues nothing. */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const int32_t* block_mapping, int32_t P, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, int32_t block_size, int32_t Hkv, int32_t D,
                          pa_dtype kv_dtype, void* stream);
 
 /* Arguments of one prefill call over a batch (one layer): several new

@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
     L.pa_reshape_and_cache.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    L.pa_swap_blocks.restype = ctypes.c_int
     pargp = ctypes.POINTER(PrefillArgs)
     L.pa_prefill_check.argtypes = [pargp]
     L.pa_prefill_check.restype = ctypes.c_int
@@ -328,3 +330,25 @@ def prefill_slot_mapping(block_tables, seq_lens, q_starts, block_size, slots, st
                                          slots.shape[0], block_tables.shape[1], int(block_size),
                                          _ptr(slots), _stream(stream)), "pa_prefill_slot_mapping")
     return slots
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, kv_dtype=None, stream=None):
+    """pa_swap_blocks: whole blocks from the source pools to the destination
+    pools.  Each pool is a device tensor or a pinned host tensor
+    (``pin_memory=True``); the mapping lives on the GPU."""
+    for t, n in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous 4-d tensor")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{n} must be on the GPU or in pinned host memory")
+    _require(block_mapping, "block_mapping", torch.int32, 2)
+    if block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [P, 2]")
+    if src_k.shape != src_v.shape or dst_k.shape != dst_v.shape or src_k.shape[1:] != dst_k.shape[1:]:
+        raise ValueError("pools must share the block shape [block_size, Hkv, D]")
+    if not (src_k.dtype == src_v.dtype == dst_k.dtype == dst_v.dtype):
+        raise ValueError("pools must share the dtype")
+    NBs, bs, Hkv, D = src_k.shape
+    _check(lib().pa_swap_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(block_mapping),
+                                block_mapping.shape[0], NBs, dst_k.shape[0], bs, Hkv, D,
+                                _pa_dtype(src_k, kv_dtype), _stream(stream)), "pa_swap_blocks")

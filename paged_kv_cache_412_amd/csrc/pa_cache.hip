@@ -124,28 +124,42 @@ __global__ __launch_bounds__(256) void cache_quant_kernel(const char* __restrict
 // ------------------------------------------------------------------ block copy
 
 // Flat grid of P * 2 * slices work-groups: (pair, K or V, slice), where a
-// slice is kSliceChunks 16-byte chunks of one block.
+// slice is kSliceChunks 16-byte chunks of one block.  Source and destination
+// pools may be one pool (copy-on-write) or two (swap between device memory
+// and pinned host memory, which the loads and stores reach over the host
+// link).  Each thread loads all of its chunks before it stores any, so a
+// work-group keeps a whole slice in flight: host-link round trips are long.
 constexpr int kSliceChunks = kCopySliceChunks;
+constexpr int kCopyThreads = 256;
+constexpr int kChunksPerThread = kSliceChunks / kCopyThreads;
+static_assert(kSliceChunks % kCopyThreads == 0, "slice shape");
 
-__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_cache,
-                                                          u32x4* __restrict__ v_cache,
-                                                          const int32_t* __restrict__ mapping,
-                                                          int32_t num_blocks, int64_t block_chunks,
-                                                          int32_t slices) {
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    const u32x4* __restrict__ src_k, const u32x4* __restrict__ src_v, u32x4* __restrict__ dst_k,
+    u32x4* __restrict__ dst_v, const int32_t* __restrict__ mapping, int32_t src_blocks,
+    int32_t dst_blocks, int64_t block_chunks, int32_t slices) {
   const int slice = blockIdx.x % slices;
   const int kv = (blockIdx.x / slices) & 1;
   const int pair = blockIdx.x / (2 * slices);
   const int src = mapping[2 * pair];
   const int dst = mapping[2 * pair + 1];
-  if (static_cast<unsigned>(src) >= static_cast<unsigned>(num_blocks) ||
-      static_cast<unsigned>(dst) >= static_cast<unsigned>(num_blocks))
+  if (static_cast<unsigned>(src) >= static_cast<unsigned>(src_blocks) ||
+      static_cast<unsigned>(dst) >= static_cast<unsigned>(dst_blocks))
     return;
-  u32x4* pool = kv == 0 ? k_cache : v_cache;
-  const u32x4* s = pool + static_cast<size_t>(src) * block_chunks;
-  u32x4* d = pool + static_cast<size_t>(dst) * block_chunks;
-  const int64_t beg = static_cast<int64_t>(slice) * kSliceChunks;
-  const int64_t end = beg + kSliceChunks < block_chunks ? beg + kSliceChunks : block_chunks;
-  for (int64_t i = beg + threadIdx.x; i < end; i += blockDim.x) d[i] = s[i];
+  const u32x4* s = (kv == 0 ? src_k : src_v) + static_cast<size_t>(src) * block_chunks;
+  u32x4* d = (kv == 0 ? dst_k : dst_v) + static_cast<size_t>(dst) * block_chunks;
+  const int64_t beg = static_cast<int64_t>(slice) * kSliceChunks + threadIdx.x;
+  u32x4 v[kChunksPerThread];
+#pragma unroll
+  for (int k = 0; k < kChunksPerThread; ++k) {
+    const int64_t i = beg + static_cast<int64_t>(k) * kCopyThreads;
+    if (i < block_chunks) v[k] = s[i];
+  }
+#pragma unroll
+  for (int k = 0; k < kChunksPerThread; ++k) {
+    const int64_t i = beg + static_cast<int64_t>(k) * kCopyThreads;
+    if (i < block_chunks) d[i] = v[k];
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -192,13 +206,16 @@ hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* 
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int32_t P,
-                              int32_t num_blocks, size_t block_bytes, hipStream_t stream) {
+hipError_t launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const int32_t* mapping, int32_t P, int32_t src_blocks,
+                              int32_t dst_blocks, size_t block_bytes, hipStream_t stream) {
   const int64_t block_chunks = static_cast<int64_t>(block_bytes / 16);
   const int32_t slices = static_cast<int32_t>((block_chunks + kSliceChunks - 1) / kSliceChunks);
   dim3 grid(static_cast<unsigned>(static_cast<int64_t>(P) * 2 * slices));
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, static_cast<u32x4*>(k_cache),
-                     static_cast<u32x4*>(v_cache), mapping, num_blocks, block_chunks, slices);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream,
+                     static_cast<const u32x4*>(src_k), static_cast<const u32x4*>(src_v),
+                     static_cast<u32x4*>(dst_k), static_cast<u32x4*>(dst_v), mapping, src_blocks,
+                     dst_blocks, block_chunks, slices);
   return hipGetLastError();
 }
 

@@ -158,7 +158,10 @@ hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* 
                                     int32_t D, int32_t block_size, int32_t num_blocks,
                                     pa_dtype src_dtype, pa_dtype kv_dtype, float k_inv_scale,
                                     float v_inv_scale, hipStream_t stream);
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* mapping, int32_t P,
-                              int32_t num_blocks, size_t block_bytes, hipStream_t stream);
+// Whole-block copies from the source pools to the destination pools (the
+// same pools for copy-on-write, a device and a pinned host pool for swap).
+hipError_t launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const int32_t* mapping, int32_t P, int32_t src_blocks,
+                              int32_t dst_blocks, size_t block_bytes, hipStream_t stream);
 
 }  // namespace pa

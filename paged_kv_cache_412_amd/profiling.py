@@ -124,7 +124,12 @@ def summarize(workload: str, d: str) -> None:
         if name.startswith(f"pa::{kernel}") and avg_us is None:
             avg_us = a
     kvb = bench_kv_bytes(cfg)
-    if avg_us and cfg.prefill:
+    if avg_us and cfg.swap:
+        lines += ["", f"Bytes per launch (one direction, K and V): {kvb}; at the average duration of "
+                      f"`{kernel}` (evictions and restores together) that is "
+                      f"{kvb / (avg_us * 1e-6) / 1e9:.1f} GB/s over the host link, "
+                      f"{100 * kvb / (avg_us * 1e-6) / 63e9:.1f} % of PCIe 5.0 x16 (63 GB/s)."]
+    elif avg_us and cfg.prefill:
         fl = bench_prefill_flops(cfg)
         lines += ["", f"Algorithmic flops per launch: {fl} (4*D per query head and visible key); at the "
                       f"average duration of `{kernel}` that is {fl / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s, "
@@ -193,6 +198,9 @@ def bench_kv_bytes(cfg) -> int:
     import numpy as np
 
     from paged_kv_cache_412_amd import workloads
+    if cfg.swap:
+        return 2 * int(cfg.swap["blocks"]) * cfg.block_size * cfg.Hkv * cfg.D * \
+            workloads.ELEM_BYTES[cfg.kv_dtype]
     if cfg.prefill:
         news, ctx, _ = workloads.prefill_lengths(cfg)
         lens = news + ctx

@@ -35,6 +35,11 @@ Prefill workloads (several new tokens per sequence, :func:`make_prefill`):
 * ``prefill_fp8`` -- GQA 32/8 with an e4m3 cache, 8 chunks of 2,048 new
   tokens after 0..6144 cached tokens, bf16 queries.
 
+Swap workload (:func:`make_swap`): ``swap13b`` -- 1,024 blocks of the 13B
+layer's shape (16 tokens x 40 heads x 128, fp16: 160 KiB per block and pool)
+evicted to a pinned host pool and restored to other device blocks (P3
+article A: pages move to CPU memory one at a time).
+
 State handed to the step (the "pre-step" state): every sequence's cache holds
 its first L-1 tokens; the decode step appends token L-1 and then attends over
 all L tokens.  Tables hold ceil((L-1)/bs) blocks; the host block manager
@@ -85,6 +90,7 @@ class Config:
     shared: dict = field(default_factory=dict)  # shared-prefix layout parameters
     partition_size: int = 512
     prefill: dict = field(default_factory=dict)  # prefill: inclusive ranges "new", "ctx"
+    swap: dict = field(default_factory=dict)     # swap: blocks moved each way
 
     @property
     def G(self) -> int:
@@ -120,6 +126,9 @@ CONFIGS = {
     "prefill_fp8": Config("prefill_fp8", 9, B=8, Hq=32, Hkv=8, D=128, block_size=16, kv_dtype=E4M3,
                           q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
                           prefill=dict(new=(2048, 2048), ctx=(0, 6144))),
+    # page-granular eviction to pinned host memory and restore (13B block shape)
+    "swap13b": Config("swap13b", 10, B=0, Hq=40, Hkv=40, D=128, block_size=16, kv_dtype=F16,
+                      q_dtype=F16, out_dtype=F16, src_dtype=F16, swap=dict(blocks=1024)),
 }
 
 
@@ -385,3 +394,46 @@ def make_prefill(cfg: Config, device="cpu", poison: bool = True, lengths=None) -
                            num_blocks=NB, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new,
                            v_new=v_new, k_scale=k_scale, v_scale=v_scale,
                            scale=1.0 / float(np.sqrt(D)))
+
+
+@dataclass
+class SwapWorkload:
+    """Device pools, pinned host pools and the two block mappings of one
+    eviction and restore: ``out_map`` (device block -> host block) and
+    ``in_map`` (host block -> another device block), int32 [N, 2] on the GPU."""
+
+    cfg: Config
+    k_dev: torch.Tensor
+    v_dev: torch.Tensor
+    k_host: torch.Tensor
+    v_host: torch.Tensor
+    out_pairs: np.ndarray
+    in_pairs: np.ndarray
+    out_map: torch.Tensor
+    in_map: torch.Tensor
+
+    @property
+    def block_bytes(self) -> int:
+        c = self.cfg
+        return c.block_size * c.Hkv * c.D * ELEM_BYTES[c.kv_dtype]
+
+
+def make_swap(cfg: Config, device="cuda") -> SwapWorkload:
+    """A device pool of 2N + N/8 blocks, N of them (a seeded random choice)
+    evicted to host blocks 0..N-1 and restored to N other device blocks."""
+    N = int(cfg.swap["blocks"])
+    rng = np.random.default_rng(cfg.seed)
+    NB = 2 * N + N // 8
+    perm = rng.permutation(NB)
+    victims, targets = perm[:N], perm[N:2 * N]
+    gen = torch.Generator(device=device).manual_seed(cfg.seed)
+    k_dev, _ = _fill_values((NB, cfg.block_size, cfg.Hkv, cfg.D), cfg.kv_dtype, gen, device)
+    v_dev, _ = _fill_values((NB, cfg.block_size, cfg.Hkv, cfg.D), cfg.kv_dtype, gen, device)
+    shape = (N, cfg.block_size, cfg.Hkv, cfg.D)
+    k_host = torch.zeros(shape, dtype=k_dev.dtype).pin_memory()
+    v_host = torch.zeros(shape, dtype=v_dev.dtype).pin_memory()
+    host_ids = rng.permutation(N)
+    out_pairs = np.stack([victims, host_ids], axis=1).astype(np.int32)
+    in_pairs = np.stack([host_ids, targets], axis=1).astype(np.int32)
+    return SwapWorkload(cfg, k_dev, v_dev, k_host, v_host, out_pairs, in_pairs,
+                        torch.from_numpy(out_pairs).to(device), torch.from_numpy(in_pairs).to(device))

@@ -225,3 +225,24 @@ def test_prefill_slot_mapping_rejections(L):
     assert L.pa_prefill_slot_mapping(None, FAKE, FAKE, 2, 4, 8, 16, FAKE, None) == 1
     assert L.pa_prefill_slot_mapping(FAKE, FAKE, FAKE, 0, 4, 8, 16, FAKE, None) == 2
     assert L.pa_prefill_slot_mapping(None, None, None, 0, 0, 8, 16, None, None) == 0
+
+
+def test_swap_blocks_rejections(L):
+    # every case returns before the runtime is asked about the pointers
+    P = binding
+    F2 = FAKE + (1 << 30)
+    args = lambda **kw: {**dict(sk=FAKE, sv=FAKE + (1 << 28), dk=F2, dv=F2 + (1 << 28), m=FAKE, P=4,
+                                snb=64, dnb=64, bs=16, hkv=8, d=128, dt=P.PA_F16), **kw}
+
+    def call(**kw):
+        a = args(**kw)
+        return L.pa_swap_blocks(a["sk"], a["sv"], a["dk"], a["dv"], a["m"], a["P"], a["snb"], a["dnb"],
+                                a["bs"], a["hkv"], a["d"], a["dt"], None)
+    assert call(P=-1) == 2 and call(snb=0) == 2 and call(dnb=0) == 2 and call(bs=0) == 2
+    assert call(dt=9) == 3
+    assert call(d=3, dt=P.PA_FP8_E4M3, hkv=1, bs=1) == 3            # 3-byte blocks
+    assert call(P=0, sk=None, m=None) == 0                          # nothing to do
+    assert call(sk=None) == 1 and call(m=None) == 1
+    assert call(dk=F2 + 8) == 2                                     # misaligned
+    assert call(dk=FAKE + 4096) == 2                                # dst overlaps src K
+    assert call(dv=F2 + 4096) == 2                                  # dst K and V overlap
