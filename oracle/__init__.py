@@ -40,6 +40,9 @@ Modules:
 * :mod:`oracle.blocks` -- the host-side block bookkeeping the pages describe:
   FIFO free list, per-block reference counts, allocation of a new block only
   when the last one is full, and copy-on-write of shared blocks.
+* :mod:`oracle.prefix_cache` -- the host block manager with content-hashed
+  prefix caching (FNV-1a keys over whole prefixes), LRU reuse of released
+  cached blocks and free-on-finish.
 * :mod:`oracle.sizes` -- the KV-cache size and waste arithmetic the pages
   quote.
 
@@ -48,4 +51,4 @@ than itself (worked example, closed forms, library special cases, brute force,
 invariants) except where its docstring says "parity unpinned".
 """
 
-from . import numerics, fp8, paged, blocks, sizes  # noqa: F401
+from . import numerics, fp8, paged, blocks, prefix_cache, sizes  # noqa: F401
