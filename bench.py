@@ -376,6 +376,95 @@ def bench_swap(args, cfg):
     return 0
 
 
+def replay(manager, ops, budget_s=None, on_add=None):
+    """Run a request-stream trace on a block manager (the library's or the
+    oracle's); returns (operations done, seconds, peak blocks in use)."""
+    is_native = hasattr(manager, "_h")
+    total = manager.free_blocks()
+    peak, done = 0, 0
+    t0 = time.perf_counter()
+    for op in ops:
+        kind = op[0]
+        if kind == "add":
+            sid, cached = manager.add(op[1])
+            if on_add:
+                on_add(len(op[1]), cached)
+        elif kind == "append":
+            manager.append(op[1], op[2])
+        elif kind == "fork":
+            manager.fork(op[1])
+        else:
+            manager.free(op[1]) if is_native else manager.free_seq(op[1])
+        done += 1
+        if kind != "append" or done % 64 == 0:
+            peak = max(peak, total - manager.free_blocks())
+        if budget_s is not None and done % 256 == 0 and time.perf_counter() - t0 > budget_s:
+            break
+    return done, time.perf_counter() - t0, peak
+
+
+def bench_stream(args, cfg):
+    """Block-manager workloads: the library's native manager replays a
+    seeded continuous-batching request stream (host code; no GPU kernel)."""
+    from oracle import prefix_cache as opc
+    from paged_kv_cache_412_amd import binding, workloads
+
+    print(f"[bench] building request stream {cfg.name}", file=sys.stderr, flush=True)
+    ops = workloads.make_stream(cfg)
+    lens = {}
+    NB = cfg.B * -(-(cfg.stream["system_len"][1] + cfg.stream["user_len"][1] +
+                     cfg.stream["gen_len"][1]) // cfg.block_size)
+    stats = {"prompt_tokens": 0, "cached_tokens": 0}
+
+    def count(n, cached):
+        stats["prompt_tokens"] += n
+        stats["cached_tokens"] += cached
+
+    times = []
+    for rep in range(max(1, args.steps)):
+        m = binding.BlockManager(NB, cfg.block_size, True)
+        done, dt, peak_on = replay(m, ops, on_add=count if rep == 0 else None)
+        m.close()
+        times.append(dt)
+    dt = float(np.median(times))
+    m = binding.BlockManager(NB, cfg.block_size, False)
+    _, _, peak_off = replay(m, ops)
+    m.close()
+    kinds = {k: sum(1 for o in ops if o[0] == k) for k in ("add", "append", "fork", "free")}
+    res = {
+        "metric": "host block manager with prefix caching: operations/s; blocks saved by caching",
+        "value": round(len(ops) / dt, 1),
+        "unit": "ops/s",
+        "n_gpus": 1,
+        "steps": max(1, args.steps),
+        "warmup": 0,
+        "ms_per_step": round(dt * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic request stream (seeded token ids, shared system prompts, n=3 samples)",
+        "config": {"workload": cfg.name, "max_live": cfg.B, "block_size": cfg.block_size,
+                   "pool_blocks": NB, **{k: (list(v) if isinstance(v, tuple) else v)
+                                         for k, v in cfg.stream.items()}, "ops": kinds},
+        "prompt_tokens_from_cache": round(stats["cached_tokens"] / max(1, stats["prompt_tokens"]), 4),
+        "peak_blocks_in_use": {"prefix_caching": peak_on, "no_caching": peak_off},
+        "blocks_saved_frac": round(1.0 - peak_on / max(1, peak_off), 4),
+        "note": "host code through the ctypes binding (call overhead included); no device kernel",
+        "roofline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        o = opc.PrefixCache(NB, cfg.block_size, caching=True)
+        done, odt, _ = replay(o, ops, budget_s=min(args.cpu_budget, 10.0))
+        res["cpu_baseline"] = {"value": round(done / odt, 1), "unit": "ops/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {done} of {len(ops)} operations of the same stream, {odt:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def parity_storage(t):
     from tests import parity
     return parity.storage(t)
@@ -409,6 +498,8 @@ def main(argv=None):
         return 2
     if args.copy_calibration:
         return copy_calibration()
+    if workloads.CONFIGS[args.workload].stream:
+        return bench_stream(args, workloads.CONFIGS[args.workload])
     binding.lib()
     cfg = workloads.CONFIGS[args.workload]
     if cfg.prefill:

@@ -76,7 +76,9 @@ typedef enum pa_status {
   PA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent              */
   PA_ERR_UNSUPPORTED = 3, /* dtype / head dim / block size / group not built     */
   PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required          */
-  PA_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch            */
+  PA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch            */
+  PA_ERR_OUT_OF_BLOCKS = 6 /* block manager: no free or evictable block left;     */
+                           /* the operation changed nothing                      */
 } pa_status;
 
 /* Arguments of one decode step over a batch (one layer). */
@@ -281,6 +283,69 @@ pa_status pa_prefill_slot_mapping(const int32_t* block_tables, const int32_t* se
                                   const int32_t* q_starts, int32_t B, int32_t T,
                                   int32_t max_blocks_per_seq, int32_t block_size, int32_t* slots,
                                   void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Host block manager with prefix caching (host memory only; no GPU calls). */
+/*                                                                      */
+/* Which physical block each sequence's table points at (P1 "Sayfalama   */
+/* Nasıl Çalışır": free list, block table, a new block only when the last */
+/* one is full), shared blocks with reference counts and copy-on-write    */
+/* (P1 "Diziler Arasında Blokları Paylaşma"), hashing every block so that */
+/* requests starting with the same tokens share cached blocks (same       */
+/* section: prompt caching), and a finished sequence's blocks returned at */
+/* once (P1 "İlgili Teknikler": continuous batching).                     */
+/*                                                                      */
+/* Rules.  Free blocks leave from the front of a FIFO list (initially     */
+/* free_order, or 0..num_blocks-1) and return to its back.  A full        */
+/* block's key is the 64-bit FNV-1a hash of every token from the start    */
+/* of its sequence through the block (token ids as 4-byte little-endian   */
+/* integers); a hit also matches the block's stored tokens and its        */
+/* parent's key.  Admitting a prompt reuses cached blocks for its leading */
+/* full blocks, stopping at the first miss; new full blocks register     */
+/* their key unless it is taken.  A new block is the front of the free    */
+/* list or, when that is empty, the cached block with no users released   */
+/* longest ago (it loses its key).  Freeing a sequence releases its       */
+/* blocks last block first: keyed blocks stay cached, others go to the   */
+/* free list.  Not thread-safe: one manager per thread, or a lock around  */
+/* it.                                                                   */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager of num_blocks blocks of block_size tokens; prefix_caching 0
+ * turns keys off (no sharing across requests).  free_order: NULL, or a
+ * permutation of 0..num_blocks-1 (host memory).  NULL on invalid arguments
+ * or allocation failure. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, int32_t prefix_caching,
+                               const int32_t* free_order);
+void pa_bm_destroy(pa_block_manager* m);
+
+/* Admit a sequence with n prompt tokens (host array): *seq receives its id
+ * (ids count up from 0 and are never reused), *cached_tokens how many of
+ * its leading tokens sit in reused cached blocks (their K/V need no
+ * recomputation).  PA_ERR_OUT_OF_BLOCKS if the new blocks do not fit. */
+pa_status pa_bm_add(pa_block_manager* m, const int32_t* tokens, int32_t n, int32_t* seq,
+                    int32_t* cached_tokens);
+
+/* Append one token: *slot receives its flat slot (block * block_size +
+ * offset); when the last block was shared, a private copy replaces it in
+ * this sequence's table and (*copy_src, *copy_dst) name the block copy to
+ * run before the cache write (pa_copy_blocks), else both are -1. */
+pa_status pa_bm_append(pa_block_manager* m, int32_t seq, int32_t token, int32_t* slot,
+                       int32_t* copy_src, int32_t* copy_dst);
+
+/* A new sequence sharing every block of seq (parallel sampling, beams). */
+pa_status pa_bm_fork(pa_block_manager* m, int32_t seq, int32_t* new_seq);
+
+/* Release a finished sequence's blocks at once. */
+pa_status pa_bm_free(pa_block_manager* m, int32_t seq);
+
+/* The block table of seq: returns its length and copies up to capacity
+ * entries to out (may be NULL); -1 for an unknown sequence. */
+int32_t pa_bm_table(const pa_block_manager* m, int32_t seq, int32_t* out, int32_t capacity);
+
+/* Tokens of seq (-1 if unknown); free plus evictable blocks; keyed blocks. */
+int32_t pa_bm_length(const pa_block_manager* m, int32_t seq);
+int32_t pa_bm_free_blocks(const pa_block_manager* m);
+int32_t pa_bm_cached_blocks(const pa_block_manager* m);
 
 /* Static description of a status code. */
 const char* pa_status_str(pa_status s);

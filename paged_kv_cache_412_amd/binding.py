@@ -21,7 +21,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "pa.h")
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-          4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH"}
+          4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH", 6: "PA_ERR_OUT_OF_BLOCKS"}
+PA_ERR_OUT_OF_BLOCKS = 6
 DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "e4m3": PA_FP8_E4M3}
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
                torch.uint8: PA_FP8_E4M3, torch.float8_e4m3fn: PA_FP8_E4M3}
@@ -105,6 +106,27 @@ def lib() -> ctypes.CDLL:
     L.pa_copy_blocks.restype = ctypes.c_int
     L.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     L.pa_swap_blocks.restype = ctypes.c_int
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    L.pa_bm_create.argtypes = [i32, i32, i32, vp]
+    L.pa_bm_create.restype = vp
+    L.pa_bm_destroy.argtypes = [vp]
+    L.pa_bm_destroy.restype = None
+    L.pa_bm_add.argtypes = [vp, vp, i32, i32p, i32p]
+    L.pa_bm_add.restype = ctypes.c_int
+    L.pa_bm_append.argtypes = [vp, i32, i32, i32p, i32p, i32p]
+    L.pa_bm_append.restype = ctypes.c_int
+    L.pa_bm_fork.argtypes = [vp, i32, i32p]
+    L.pa_bm_fork.restype = ctypes.c_int
+    L.pa_bm_free.argtypes = [vp, i32]
+    L.pa_bm_free.restype = ctypes.c_int
+    L.pa_bm_table.argtypes = [vp, i32, vp, i32]
+    L.pa_bm_table.restype = i32
+    for name in ("pa_bm_length",):
+        getattr(L, name).argtypes = [vp, i32]
+        getattr(L, name).restype = i32
+    for name in ("pa_bm_free_blocks", "pa_bm_cached_blocks"):
+        getattr(L, name).argtypes = [vp]
+        getattr(L, name).restype = i32
     pargp = ctypes.POINTER(PrefillArgs)
     L.pa_prefill_check.argtypes = [pargp]
     L.pa_prefill_check.restype = ctypes.c_int
@@ -352,3 +374,79 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, kv_dtype=None, stream
     _check(lib().pa_swap_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(block_mapping),
                                 block_mapping.shape[0], NBs, dst_k.shape[0], bs, Hkv, D,
                                 _pa_dtype(src_k, kv_dtype), _stream(stream)), "pa_swap_blocks")
+
+
+class OutOfBlocks(PaError):
+    """The block manager has no free or evictable block; nothing changed."""
+
+
+class BlockManager:
+    """The library's host block manager with prefix caching (pa_bm_* in
+    include/pa.h): argument marshalling only, all bookkeeping is native."""
+
+    def __init__(self, num_blocks: int, block_size: int, prefix_caching: bool = True, free_order=None):
+        import numpy as np
+        self._lib = lib()
+        self.block_size = int(block_size)
+        self._order = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+        ptr = None if self._order is None else self._order.ctypes.data
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size), int(bool(prefix_caching)), ptr)
+        if not self._h:
+            raise ValueError("invalid block manager arguments")
+
+    def close(self):
+        if self._h:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _st(self, status, what):
+        if status == PA_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(status, what, "no free or evictable block")
+        _check(status, what)
+
+    def add(self, tokens):
+        """Admit a prompt; returns (sequence id, cached tokens)."""
+        import numpy as np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        sid, cached = ctypes.c_int32(), ctypes.c_int32()
+        self._st(self._lib.pa_bm_add(self._h, t.ctypes.data if t.size else None, int(t.size),
+                                     ctypes.byref(sid), ctypes.byref(cached)), "pa_bm_add")
+        return sid.value, cached.value
+
+    def append(self, seq: int, token: int):
+        """Append a token; returns (slot, (src, dst) copy or None)."""
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._st(self._lib.pa_bm_append(self._h, int(seq), int(token), ctypes.byref(slot),
+                                        ctypes.byref(src), ctypes.byref(dst)), "pa_bm_append")
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def fork(self, seq: int) -> int:
+        out = ctypes.c_int32()
+        self._st(self._lib.pa_bm_fork(self._h, int(seq), ctypes.byref(out)), "pa_bm_fork")
+        return out.value
+
+    def free(self, seq: int) -> None:
+        self._st(self._lib.pa_bm_free(self._h, int(seq)), "pa_bm_free")
+
+    def table(self, seq: int) -> list:
+        n = self._lib.pa_bm_table(self._h, int(seq), None, 0)
+        if n < 0:
+            raise KeyError(seq)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        self._lib.pa_bm_table(self._h, int(seq), buf, n)
+        return list(buf[:n])
+
+    def length(self, seq: int) -> int:
+        return int(self._lib.pa_bm_length(self._h, int(seq)))
+
+    def free_blocks(self) -> int:
+        return int(self._lib.pa_bm_free_blocks(self._h))
+
+    def cached_blocks(self) -> int:
+        return int(self._lib.pa_bm_cached_blocks(self._h))

@@ -1,7 +1,9 @@
 """Build libpa.so in-tree with hipcc for gfx950.
 
 ``python -m paged_kv_cache_412_amd.build`` compiles every HIP source under
-``csrc/`` (objects in parallel) and links ``paged_kv_cache_412_amd/libpa.so``.
+``csrc/`` with hipcc for gfx950 and every host-only ``.cpp`` source with the
+host compiler (objects in parallel), and links
+``paged_kv_cache_412_amd/libpa.so``.
 """
 
 from __future__ import annotations
@@ -31,9 +33,15 @@ def _hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):   # host-only code
+        cmd = [os.environ.get("CXX", "g++"), *HOST_FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -42,7 +50,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"

@@ -35,6 +35,14 @@ Prefill workloads (several new tokens per sequence, :func:`make_prefill`):
 * ``prefill_fp8`` -- GQA 32/8 with an e4m3 cache, 8 chunks of 2,048 new
   tokens after 0..6144 cached tokens, bf16 queries.
 
+Request stream (:func:`make_stream`): ``prefix_stream`` -- continuous
+batching of 3,000 requests, at most 256 sequences at once; 80 % of prompts
+start with one of 8 system prompts of 256..2048 tokens (P1 "Diziler Arasında
+Blokları Paylaşma": requests with the same system prompt), then 16..256 user
+tokens; a quarter ask for 3 samples that share the prompt (P1 "İlgili
+Teknikler": a request with n=3); each sequence generates 32..256 tokens and is
+freed when done.
+
 Swap workload (:func:`make_swap`): ``swap13b`` -- 1,024 blocks of the 13B
 layer's shape (16 tokens x 40 heads x 128, fp16: 160 KiB per block and pool)
 evicted to a pinned host pool and restored to other device blocks (P3
@@ -91,6 +99,7 @@ class Config:
     partition_size: int = 512
     prefill: dict = field(default_factory=dict)  # prefill: inclusive ranges "new", "ctx"
     swap: dict = field(default_factory=dict)     # swap: blocks moved each way
+    stream: dict = field(default_factory=dict)   # block-manager request stream parameters
 
     @property
     def G(self) -> int:
@@ -126,6 +135,12 @@ CONFIGS = {
     "prefill_fp8": Config("prefill_fp8", 9, B=8, Hq=32, Hkv=8, D=128, block_size=16, kv_dtype=E4M3,
                           q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
                           prefill=dict(new=(2048, 2048), ctx=(0, 6144))),
+    # host block manager: continuous batching over shared system prompts
+    "prefix_stream": Config("prefix_stream", 11, B=256, Hq=40, Hkv=40, D=128, block_size=16,
+                            kv_dtype=F16, q_dtype=F16, out_dtype=F16, src_dtype=F16,
+                            stream=dict(requests=3000, systems=8, system_len=(256, 2048),
+                                        user_len=(16, 256), gen_len=(32, 256), p_system=0.8,
+                                        p_samples=0.25, samples=3)),
     # page-granular eviction to pinned host memory and restore (13B block shape)
     "swap13b": Config("swap13b", 10, B=0, Hq=40, Hkv=40, D=128, block_size=16, kv_dtype=F16,
                       q_dtype=F16, out_dtype=F16, src_dtype=F16, swap=dict(blocks=1024)),
@@ -437,3 +452,40 @@ def make_swap(cfg: Config, device="cuda") -> SwapWorkload:
     in_pairs = np.stack([host_ids, targets], axis=1).astype(np.int32)
     return SwapWorkload(cfg, k_dev, v_dev, k_host, v_host, out_pairs, in_pairs,
                         torch.from_numpy(out_pairs).to(device), torch.from_numpy(in_pairs).to(device))
+
+
+def make_stream(cfg: Config) -> list:
+    """The operation trace of ``cfg``'s request stream, as a list of
+    ("add", tokens) / ("append", seq, token) / ("fork", seq) / ("free", seq)
+    tuples.  Sequence ids are the order of creation (adds and forks), as the
+    block manager numbers them.  Each decode step appends one token to every
+    live sequence; finished sequences are freed; new requests fill the
+    batch up to ``cfg.B`` sequences."""
+    p = cfg.stream
+    rng = np.random.default_rng(cfg.seed)
+    systems = [rng.integers(0, 32000, size=int(rng.integers(p["system_len"][0], p["system_len"][1],
+                                                          endpoint=True))).tolist()
+               for _ in range(p["systems"])]
+    ops, live, next_id, admitted = [], {}, 0, 0
+    while admitted < p["requests"] or live:
+        while admitted < p["requests"] and len(live) + p["samples"] <= cfg.B:
+            prompt = (systems[int(rng.integers(p["systems"]))] if rng.random() < p["p_system"] else [])
+            user = rng.integers(0, 32000, size=int(rng.integers(p["user_len"][0], p["user_len"][1],
+                                                                endpoint=True))).tolist()
+            ops.append(("add", prompt + user))
+            first = next_id
+            next_id += 1
+            live[first] = int(rng.integers(p["gen_len"][0], p["gen_len"][1], endpoint=True))
+            if rng.random() < p["p_samples"]:
+                for _ in range(p["samples"] - 1):
+                    ops.append(("fork", first))
+                    live[next_id] = int(rng.integers(p["gen_len"][0], p["gen_len"][1], endpoint=True))
+                    next_id += 1
+            admitted += 1
+        for sid in list(live):
+            ops.append(("append", sid, int(rng.integers(0, 32000))))
+            live[sid] -= 1
+            if live[sid] == 0:
+                ops.append(("free", sid))
+                del live[sid]
+    return ops

@@ -23,7 +23,9 @@ def test_header_declares_the_path_entry_points():
     for n in ("pa_decode", "pa_decode_partition", "pa_decode_reduce", "pa_decode_workspace_size",
               "pa_decode_partition_size",
               "pa_decode_check", "pa_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
-              "pa_prefill", "pa_prefill_check", "pa_prefill_slot_mapping",
+              "pa_prefill", "pa_prefill_check", "pa_prefill_slot_mapping", "pa_swap_blocks",
+              "pa_bm_create", "pa_bm_destroy", "pa_bm_add", "pa_bm_append", "pa_bm_fork", "pa_bm_free",
+              "pa_bm_table", "pa_bm_length", "pa_bm_free_blocks", "pa_bm_cached_blocks",
               "pa_status_str", "pa_abi_version"):
         assert n in names
 
@@ -35,8 +37,8 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_abi_version_and_status_strings(L):
     assert L.pa_abi_version() == 1
-    for s in range(6):
-        assert L.pa_status_str(s)
+    for s in range(7):
+        assert L.pa_status_str(s) and L.pa_status_str(s) != b"unknown status"
     assert L.pa_status_str(99) == b"unknown status"
 
 
