@@ -101,9 +101,10 @@ typedef struct pa_decode_args {
 } pa_decode_args;
 
 /* Supported decode combinations (others return PA_ERR_UNSUPPORTED):
- *   D in {64, 128}; block_size in {16, 32}; G = Hq/Hkv in {1, 2, 4, 8};
+ *   D in {64, 128}; block_size in {16, 32};
  *   (q, kv) in {(F32,F32), (F16,F16), (BF16,BF16), (BF16,FP8_E4M3),
- *   (F16,FP8_E4M3)}; out_dtype = q_dtype or PA_F32. */
+ *   (F16,FP8_E4M3)}; out_dtype = q_dtype or PA_F32;
+ *   G = Hq/Hkv from 1 to 16, except fp32 caches: G in {1, 2, 4, 8}. */
 
 /* Schedules.
  *   partition_size > 0 (fixed): one work-group per (KV heads, sequence,
@@ -241,7 +242,7 @@ typedef struct pa_prefill_args {
 } pa_prefill_args;
 
 /* Supported prefill combinations (others return PA_ERR_UNSUPPORTED):
- *   D in {64, 128}; block_size in {16, 32}; G = Hq/Hkv in {1, 2, 4, 8};
+ *   D in {64, 128}; block_size in {16, 32}; G = Hq/Hkv from 1 to 16;
  *   (q, kv) in {(F16,F16), (BF16,BF16), (BF16,FP8_E4M3), (F16,FP8_E4M3)};
  *   out_dtype = q_dtype or PA_F32.  No workspace. */
 

@@ -1,5 +1,6 @@
 // pa_decode_mfma.hip -- decode-partition kernel on the matrix cores, used for
-// grouped-query attention with G = Hq/Hkv of 4 or 8 and 16-bit or e4m3 caches.
+// grouped-query attention with G = Hq/Hkv from 3 to 16 and 16-bit or e4m3
+// caches.
 //
 // With grouped-query attention (P1 = Ultralytics glossary page
 // "PagedAttention", section "İlgili Teknikler") the G query heads that share
@@ -48,7 +49,7 @@ namespace pa {
 // KV heads (waves) per work-group
 constexpr int kMfmaHeads = 8;
 
-template <int KV, int Q, int D, int BS, int G, int ST>
+template <int KV, int Q, int D, int BS, int ST>
 __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const DecodeParams p) {
   using M = Mfma<Q>;
   constexpr bool FP8 = KV == PA_FP8_E4M3;
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   constexpr int VW = EPL / 2;                   // dwords of 16-bit V per lane per row
   constexpr int VR = FP8 ? EPL / 4 : EPL / 2;   // dwords of stored V per lane per row
   constexpr int KLD = KR >= 4 ? 4 : KR;         // dwords per K load instruction
-  static_assert(G == 4 || G == 8, "MFMA path serves query groups of 4 or 8");
+  const int G = p.Hq / p.Hkv;  // 3..16: the query group padded to the MFMA's 16 rows
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BS % 16 == 0, "block size");
 
@@ -281,35 +282,26 @@ namespace {
 // register sets in the load pipeline (units in flight per wave, plus one)
 constexpr int kStages = 2;
 
-template <int KV_, int Q_, int D_, int BS_, int G_>
+template <int KV_, int Q_, int D_, int BS_>
 struct Tag {
-  static constexpr int KV = KV_, Q = Q_, D = D_, BS = BS_, G = G_;
+  static constexpr int KV = KV_, Q = Q_, D = D_, BS = BS_;
   static const void* kernel() {
-    return reinterpret_cast<const void*>(&decode_mfma_kernel<KV, Q, D, BS, G, kStages>);
+    return reinterpret_cast<const void*>(&decode_mfma_kernel<KV, Q, D, BS, kStages>);
   }
   static hipError_t launch(const DecodeParams& p, hipStream_t s) {
     const dim3 grid = p.balanced ? dim3(p.head_groups, p.groups, 1)
                                  : dim3(p.head_groups, p.B, p.num_partitions);
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, D, BS, G, kStages>), grid,
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, D, BS, kStages>), grid,
                        dim3(p.heads_per_wg * 64), 0, s, p);
     return hipGetLastError();
   }
 };
 
-template <int KV, int Q, int D, int BS, typename F>
-bool by_group(const DecodeParams& p, F&& f) {
-  switch (p.Hq / p.Hkv) {
-    case 4: f(Tag<KV, Q, D, BS, 4>{}); return true;
-    case 8: f(Tag<KV, Q, D, BS, 8>{}); return true;
-    default: return false;
-  }
-}
-
 template <int KV, int Q, int D, typename F>
 bool by_block(const DecodeParams& p, F&& f) {
   switch (p.block_size) {
-    case 16: return by_group<KV, Q, D, 16>(p, f);
-    case 32: return by_group<KV, Q, D, 32>(p, f);
+    case 16: f(Tag<KV, Q, D, 16>{}); return true;
+    case 32: f(Tag<KV, Q, D, 32>{}); return true;
     default: return false;
   }
 }
@@ -337,7 +329,7 @@ bool dispatch(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype, F&& f)
 int32_t decode_mfma_heads() { return kMfmaHeads; }
 
 bool decode_mfma_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t group) {
-  if (group != 4 && group != 8) return false;
+  if (group < 3 || group > 16) return false;
   return (kv_dtype == PA_F16 && q_dtype == PA_F16) || (kv_dtype == PA_BF16 && q_dtype == PA_BF16) ||
          (kv_dtype == PA_FP8_E4M3 && (q_dtype == PA_BF16 || q_dtype == PA_F16));
 }

@@ -90,9 +90,9 @@ constexpr int64_t kBalancedMaxWaves = 4096;
 constexpr int32_t kMaxPartitions = 65535;
 
 // Everything a prefill launch needs, resolved on the host.  Work-group
-// (sequence b, KV head, query tile) covers kPrefillRows rows of (new token,
-// query head of the KV head's group) pairs: 128 / G consecutive new tokens
-// of sequence b with all G query heads each.
+// (sequence b, KV head, query tile) covers up to kPrefillRows rows of (new
+// token, query head of the KV head's group) pairs: floor(128 / G)
+// consecutive new tokens of sequence b with all G query heads each.
 struct PrefillParams {
   void* out;
   const void* q;
@@ -102,7 +102,7 @@ struct PrefillParams {
   const int32_t* seq_lens;
   const int32_t* q_starts;  // [B+1]
   int32_t B, T, max_q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq;
-  int32_t q_tiles;          // query tiles per (sequence, KV head): ceil(max_q_len*G / 128)
+  int32_t q_tiles;          // query tiles per (sequence, KV head): ceil(max_q_len / floor(128/G))
   int32_t total_groups;     // B * Hkv * q_tiles (the 1-D grid)
   float qk_scale_log2;      // scale * k_scale * log2(e)
   float v_scale;
@@ -141,7 +141,7 @@ int32_t decode_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype k
 int32_t decode_mfma_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype);
 int32_t decode_valu_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype);
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
-// The two partition kernels: matrix cores for query groups of 4 or 8 over
+// The two partition kernels: matrix cores for query groups of 3 to 16 over
 // 16-bit or e4m3 caches, vector ALUs for everything else.
 bool decode_mfma_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t group);
 hipError_t launch_decode_mfma(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,

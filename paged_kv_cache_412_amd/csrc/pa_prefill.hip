@@ -12,10 +12,10 @@
 // Teknikler"); grouped-query attention shares a KV head among G query heads
 // (same section).
 //
-// Work split.  A work-group of four waves owns 128 rows of (new token, query
-// head) pairs of one KV head: 128 / G consecutive new tokens of one sequence
-// with all G heads of the group, so every K/V tile it loads serves all of
-// them.  Wave w owns rows [32w, 32w + 32) as two 16-column MFMA tiles.  The
+// Work split.  A work-group of four waves owns up to 128 rows of (new token,
+// query head) pairs of one KV head: floor(128 / G) consecutive new tokens of
+// one sequence with all G heads of the group (G from 1 to 16), so every K/V
+// tile it loads serves all of them.  Wave w owns rows [32w, 32w + 32) as two 16-column MFMA tiles.  The
 // keys run in tiles of 32 (two 16-token blocks, or one 32-token block): the
 // work-group copies each tile's K and V rows from the pool into LDS (double
 // buffered, the next tile's global loads in flight during the current
@@ -77,7 +77,7 @@ __device__ __forceinline__ int xcd_logical(int i, int n) {
   return x * q + min(x, r) + k;
 }
 
-template <int KV, int Q, int D, int BS, int G>
+template <int KV, int Q, int D, int BS>
 __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(const PrefillParams p) {
   using M = Mfma<Q>;
   constexpr int KVB = Elem<KV>::bytes;
@@ -87,7 +87,8 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   constexpr int KP = kKeys / 32;           // 32-key weighted-sum steps per key tile
   constexpr int EPL = D / 16;              // head-dim values per lane and key row (PV)
   constexpr int KK = D / 32;               // score MFMAs per 16-key tile
-  constexpr int TOK = kPrefillRows / G;    // new tokens per work-group
+  const int G = p.Hq / p.Hkv;              // 1..16 query heads per KV head
+  const int TOK = kPrefillRows / G;        // new tokens per work-group
   constexpr int CH = D / 8;                // 16-byte chunks per LDS row (16-bit values)
   constexpr int ROWB = D * 2;              // LDS bytes per key row
   constexpr int TILE = kKeys * ROWB;
@@ -96,7 +97,6 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   constexpr int PASSES = kKeys / RPP;      // staging loads per thread, K and V each
   static_assert(kPrefillRows == kWaves * RW, "rows per work-group");
   static_assert(kKeys % RPP == 0 && kKeys % 32 == 0, "tile shape");
-  static_assert(G >= 1 && G <= 16 && (G & (G - 1)) == 0, "group size");
   static_assert(EPL % 2 == 0 && (CH == 8 || CH == 16), "head dim");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE];  // [buffer][K, V]
 
@@ -385,31 +385,21 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
 
 // ---------------------------------------------------------------- dispatch
 
-template <int KV_, int Q_, int D_, int BS_, int G_>
+template <int KV_, int Q_, int D_, int BS_>
 struct Tag {
   static hipError_t launch(const PrefillParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((prefill_kernel<KV_, Q_, D_, BS_, G_>), dim3(p.total_groups),
-                       dim3(kWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((prefill_kernel<KV_, Q_, D_, BS_>), dim3(p.total_groups), dim3(kWaves * 64), 0,
+                       s, p);
     return hipGetLastError();
   }
 };
 
-template <int KV, int Q, int D, int BS, typename F>
-bool by_group(int32_t G, F&& f) {
-  switch (G) {
-    case 1: f(Tag<KV, Q, D, BS, 1>{}); return true;
-    case 2: f(Tag<KV, Q, D, BS, 2>{}); return true;
-    case 4: f(Tag<KV, Q, D, BS, 4>{}); return true;
-    case 8: f(Tag<KV, Q, D, BS, 8>{}); return true;
-    default: return false;
-  }
-}
-
 template <int KV, int Q, int D, typename F>
 bool by_block(int32_t bs, int32_t G, F&& f) {
+  if (G < 1 || G > 16) return false;
   switch (bs) {
-    case 16: return by_group<KV, Q, D, 16>(G, f);
-    case 32: return by_group<KV, Q, D, 32>(G, f);
+    case 16: f(Tag<KV, Q, D, 16>{}); return true;
+    case 32: f(Tag<KV, Q, D, 32>{}); return true;
     default: return false;
   }
 }

@@ -70,6 +70,14 @@ def test_decode_check_accepts_valid(L):
                  out_dtype=binding.PA_BF16, k_scale=0.01, v_scale=0.02) == 0
     assert check(L, q_dtype=binding.PA_F16, kv_dtype=binding.PA_F16, out_dtype=binding.PA_F32) == 0
     assert check(L, Hq=64, Hkv=8, D=128) == 0
+    # any group of 1..16 with 16-bit queries over 16-bit or e4m3 caches
+    for G in (1, 2, 3, 4, 5, 6, 7, 8, 12, 16):
+        for kv in (binding.PA_F16, binding.PA_FP8_E4M3):
+            sc = 0.5 if kv == binding.PA_FP8_E4M3 else 1.0
+            assert check(L, Hq=2 * G, Hkv=2, q_dtype=binding.PA_F16, kv_dtype=kv,
+                         out_dtype=binding.PA_F16, k_scale=sc, v_scale=sc) == 0, (G, kv)
+    assert check(L, Hq=34, Hkv=2, q_dtype=binding.PA_F16, kv_dtype=binding.PA_F16,
+                 out_dtype=binding.PA_F16) == 3                                   # G = 17
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -197,8 +205,8 @@ def test_prefill_check_rejections(L):
     assert pcheck(L, out=FAKE + 8) == 2                                     # misaligned
     assert pcheck(L, B=-1) == 2 and pcheck(L, T=-1) == 2 and pcheck(L, max_q_len=-1) == 2
     assert pcheck(L, Hq=3) == 2                                             # Hq % Hkv
-    assert pcheck(L, Hq=6) == 3                                             # G = 3 not built
-    assert pcheck(L, Hq=32) == 3                                            # G = 16 not built
+    assert pcheck(L, Hq=6) == 0 and pcheck(L, Hq=14) == 0 and pcheck(L, Hq=32) == 0   # G = 3, 7, 16
+    assert pcheck(L, Hq=34) == 3                                            # G = 17 not built
     assert pcheck(L, D=96) == 3 and pcheck(L, block_size=8) == 3
     assert pcheck(L, q_dtype=P.PA_F32, kv_dtype=P.PA_F32, out_dtype=P.PA_F32) == 3
     assert pcheck(L, q_dtype=P.PA_F16, kv_dtype=P.PA_BF16) == 3

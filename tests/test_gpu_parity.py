@@ -214,6 +214,25 @@ def test_every_supported_shape(pair, D, bs, G):
     print(f"[ok] max abs err {err:.3e}", flush=True)
 
 
+MFMA_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3")]
+
+
+@pytest.mark.parametrize("G", [3, 5, 6, 7, 12, 16])
+@pytest.mark.parametrize("pair", MFMA_PAIRS, ids=["-".join(p) for p in MFMA_PAIRS])
+def test_other_group_sizes(pair, G):
+    """Groups that are not powers of two, and the full 16 rows of the
+    matrix-core tile (P1 "İlgili Teknikler": grouped-query attention), under
+    both schedules."""
+    qd, kvd = pair
+    for bs, part in ((16, 0), (32, 256)):
+        cfg = workloads.Config(f"group-{qd}-{kvd}-{G}-{bs}", 7, B=4, Hq=3 * G, Hkv=3, D=128,
+                               block_size=bs, kv_dtype=kvd, q_dtype=qd, out_dtype=qd, src_dtype=qd,
+                               lens=(1, bs + 3, 700, 1100))
+        wl, step, exp = run_step(cfg, partition_size=part)
+        err = check_step(wl, step, exp)
+        print(f"[ok] G={G} bs={bs} max abs err {err:.3e}", flush=True)
+
+
 def e4m3_sweep_values(rng):
     """fp32 values around every e4m3 value and midpoint (+-4 ulps), specials,
     and random draws over the whole e4m3 range."""

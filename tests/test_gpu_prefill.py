@@ -76,7 +76,7 @@ def test_prefill_small_all_rows(name):
 @pytest.mark.parametrize("pair", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3")])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("bs", [16, 32])
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 16])
 def test_prefill_every_supported_shape(pair, D, bs, G):
     q, kv = pair
     cfg = cfg_of("prefill70b", name=f"shape_{q}_{kv}_{D}_{bs}_{G}", B=2, Hq=2 * G, Hkv=2, D=D,
