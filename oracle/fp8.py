@@ -1,4 +1,4 @@
-"""OCP 8-bit floating point, e4m3 ("fn") variant, for the oracle (test infrastructure only).
+"""OCP 8-bit floating point, e4m3 ("fn") and e5m2 variants, for the oracle (test infrastructure only).
 
 P1 "İlgili Teknikler" (FP8 cache quantisation) says only that keys and values
 are stored with 8-bit precision, roughly halving cache memory against 16-bit
@@ -8,11 +8,19 @@ NaN, largest finite magnitude 1.75 * 2**8 = 448, subnormals m * 2**-9.
 Quantisation uses one fp32 scale per tensor: the stored code c means
 ``decode(c) * scale``.
 
-Written from that definition, not from any library's source.  Pinned in
-``tests/test_oracle.py``: all 256 codes against torch's
-``float8_e4m3fn`` conversion (a library routine), encode(decode(c)) == c,
-every midpoint between neighbours rounding to the even code, saturation and
-NaN handling.
+The second flavour (P1 "İlgili Teknikler" names no flavour; e5m2 is the
+other OCP format) is e5m2: 1 sign bit, 5 exponent bits with bias 15, 2
+mantissa bits, IEEE-style infinities (exponent field 31, mantissa 0) and NaNs
+(exponent field 31, mantissa not 0), largest finite magnitude 1.75 * 2**15 =
+57344, subnormals m * 2**-16.  Its cache-write encoder rounds to nearest
+even and saturates like the e4m3 one: magnitudes that round past 57344, and
++-inf, become +-57344; NaN becomes 0x7F with the NaN's sign.
+
+Written from those definitions, not from any library's source.  Pinned in
+``tests/test_oracle.py``: all 256 codes of each format against torch's
+``float8_e4m3fn`` / ``float8_e5m2`` conversions (library routines),
+encode(decode(c)) == c, every midpoint between neighbours rounding to the even
+code, saturation and NaN handling.
 """
 
 from __future__ import annotations
@@ -101,3 +109,68 @@ def quantize(x, scale: float) -> np.ndarray:
     inv = np.float32(1.0) / np.float32(scale)                 # fl32(1/scale)
     y = (np.asarray(x, dtype=np.float64).astype(np.float32) * inv).astype(np.float64)
     return encode(y)
+
+
+# ---------------------------------------------------------------- e5m2
+
+E5M2_BIAS = 15
+E5M2_MAX = 57344.0
+E5M2_P = 3
+E5M2_EMIN = 1 - E5M2_BIAS   # -14
+
+
+def decode_code_e5m2(c: int) -> float:
+    """Value of one e5m2 code, straight from the field definition."""
+    s = (c >> 7) & 1
+    E = (c >> 2) & 0x1F
+    m = c & 0x3
+    sign = -1.0 if s else 1.0
+    if E == 0x1F:
+        return sign * float("inf") if m == 0 else math.copysign(float("nan"), sign)
+    if E == 0:
+        return sign * m * 2.0 ** (1 - E5M2_BIAS - 2)      # subnormal: m * 2**-16
+    return sign * (1.0 + m / 4.0) * 2.0 ** (E - E5M2_BIAS)
+
+
+#: float64 value of each of the 256 e5m2 codes
+DECODE_TABLE_E5M2 = np.array([decode_code_e5m2(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e5m2(codes: np.ndarray, scale: float = 1.0) -> np.ndarray:
+    """uint8 e5m2 codes -> float64 values times ``scale`` (exact, as for e4m3)."""
+    return DECODE_TABLE_E5M2[np.asarray(codes, dtype=np.uint8)] * np.float64(np.float32(scale))
+
+
+def round_to_e5m2(y) -> np.ndarray:
+    """Nearest e5m2 value, ties to even, saturating to +-57344 (also +-inf)."""
+    return round_to_format(y, E5M2_P, E5M2_EMIN, E5M2_MAX, saturate=True)
+
+
+def encode_e5m2(y) -> np.ndarray:
+    """float64 -> uint8 e5m2 codes: nearest-even, saturating, NaN -> 0x7F
+    with the NaN's sign.  Fields as for e4m3 with a 2-bit mantissa and bias
+    15: subnormal binade |r| < 2**-14 has mantissa |r| / 2**-16."""
+    y = np.asarray(y, dtype=np.float64)
+    r = round_to_e5m2(y)
+    nan = np.isnan(r)
+    a = np.where(nan, 0.0, np.abs(r))
+    sign = np.where(np.signbit(np.where(nan, y, r)), 0x80, 0).astype(np.int64)
+    sub = a < 2.0 ** E5M2_EMIN
+    m_sub = a / 2.0 ** (E5M2_EMIN - 2)
+    frac, E = np.frexp(np.where(sub, 1.0, a))
+    e = E.astype(np.int64) - 1
+    m_norm = (frac * 2.0 - 1.0) * 4.0
+    mant = np.where(sub, m_sub, m_norm)
+    expf = np.where(sub, 0, e + E5M2_BIAS)
+    if not np.all(mant == np.floor(mant)):
+        raise AssertionError("rounded value not on the e5m2 grid")
+    code = sign | (expf << 2) | mant.astype(np.int64)
+    code = np.where(nan, sign | 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_e5m2(x, scale: float) -> np.ndarray:
+    """The cache-write quantiser for e5m2: ``encode_e5m2(fl32(x * fl32(1/scale)))``."""
+    inv = np.float32(1.0) / np.float32(scale)
+    y = (np.asarray(x, dtype=np.float64).astype(np.float32) * inv).astype(np.float64)
+    return encode_e5m2(y)

@@ -436,3 +436,43 @@ def check_e4m3_quantize(quantize):
         ref = y[keep].to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         got = quantize(x[keep.numpy()], scale)
         assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# e5m2 codec
+# --------------------------------------------------------------------------
+
+def torch_e5m2_values() -> np.ndarray:
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+
+
+def check_e5m2_decode(decode_table):
+    ref = torch_e5m2_values()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(decode_table), nan)
+    assert np.array_equal(decode_table[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(decode_table[~nan]), np.signbit(ref[~nan]))
+
+
+def check_e5m2_encode(encode, decode_table):
+    codes = np.arange(256)
+    finite = np.isfinite(decode_table)
+    assert np.array_equal(encode(decode_table[finite]), codes[finite].astype(np.uint8))
+    vals = decode_table[:0x7C]                         # 0x00 .. 0x7B, increasing, finite
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    even = np.where(np.arange(0x7B) % 2 == 0, np.arange(0x7B), np.arange(1, 0x7C))
+    assert np.array_equal(encode(mids), even.astype(np.uint8)), "ties must round to even"
+    assert np.array_equal(encode(-mids), (even | 0x80).astype(np.uint8))
+    assert np.array_equal(encode(np.nextafter(mids, 0)), np.arange(0x7B).astype(np.uint8))
+    assert np.array_equal(encode(np.nextafter(mids, np.inf)), np.arange(1, 0x7C).astype(np.uint8))
+    sat = encode(np.array([57344.0, 61439.9, 61440.0, 70000.0, np.inf, -np.inf, -1e9]))
+    assert list(sat) == [0x7B] * 5 + [0xFB] * 2, [hex(x) for x in sat]
+    assert encode(np.array([np.nan]))[0] == 0x7F and encode(np.array([-np.nan]))[0] == 0xFF
+    assert encode(np.array([-0.0]))[0] == 0x80 and encode(np.array([0.0]))[0] == 0x00
+    # torch's cast (round to nearest even, no saturation) inside the finite range
+    rng = np.random.default_rng(8)
+    y = np.concatenate([rng.standard_normal(20000) * 3000, rng.uniform(-57344, 57344, 20000),
+                        rng.standard_normal(5000) * 1e-4, mids, -mids]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(encode(y.astype(np.float64)), ref)

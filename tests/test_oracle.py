@@ -253,3 +253,24 @@ def test_prefill_matches_sdpa_random_shapes(seed, G, Hkv, bs, lens, frac):
 
 def test_swap_blocks_round_trip():
     pins.check_swap_round_trip(paged.swap_blocks, paged.copy_blocks)
+
+
+# ---------------------------------------------------------------- e5m2
+
+def test_e5m2_decode_matches_torch():
+    pins.check_e5m2_decode(fp8.DECODE_TABLE_E5M2)
+
+
+def test_e5m2_encode_round_trip_ties_and_saturation():
+    pins.check_e5m2_encode(fp8.encode_e5m2, fp8.DECODE_TABLE_E5M2)
+
+
+def test_e5m2_quantize_matches_torch():
+    rng = np.random.default_rng(9)
+    for scale in (0.01, 0.5, 3.0):
+        x = rng.standard_normal(4096).astype(np.float32) * np.float32(scale * 20000.0)
+        inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32)
+        yt = torch.from_numpy(x) * inv
+        keep = yt.abs() <= 57344
+        ref = yt[keep].to(torch.float8_e5m2).view(torch.uint8).numpy()
+        assert np.array_equal(fp8.quantize_e5m2(x[keep.numpy()], scale), ref)

@@ -290,3 +290,24 @@ def swap_in_place(src, dst, pairs):
 def test_swap_mutants_are_caught(mutant):
     with pytest.raises((AssertionError, IndexError)):
         pins.check_swap_round_trip(mutant, paged.copy_blocks)
+
+
+def e5m2_encode_truncate(y):
+    y = np.asarray(y, dtype=np.float64)
+    r = numerics.round_to_format(np.nextafter(y, 0), 3, -14, 57344.0, saturate=True)
+    return fp8.encode_e5m2(np.where(np.isfinite(y), r, y))
+
+
+def e5m2_encode_overflow_to_inf(y):
+    y = np.asarray(y, dtype=np.float64)
+    out = fp8.encode_e5m2(y)
+    big = np.abs(np.nan_to_num(y, nan=0.0)) > 61440.0
+    return np.where(big, np.where(y > 0, np.uint8(0x7C), np.uint8(0xFC)), out).astype(np.uint8)
+
+
+def test_e5m2_mutants_are_caught():
+    with pytest.raises(AssertionError):
+        pins.check_e5m2_decode(fp8.DECODE_TABLE_E5M2 * 2.0)
+    for enc in (e5m2_encode_truncate, e5m2_encode_overflow_to_inf):
+        with pytest.raises(AssertionError):
+            pins.check_e5m2_encode(enc, fp8.DECODE_TABLE_E5M2)
