@@ -59,15 +59,19 @@ extern "C" {
 
 #define PA_ABI_VERSION 1
 
-/* Element types.  PA_FP8_E4M3 is OCP e4m3 "fn": 1 sign, 4 exponent (bias 7),
- * 3 mantissa bits, S.1111.111 = NaN, max +-448, no infinities; a stored code
- * c means value(c) * scale with one fp32 scale per pool (P1 "İlgili
- * Teknikler": an 8-bit KV cache, about half the memory of 16-bit). */
+/* Element types.  The 8-bit cache formats (P1 "İlgili Teknikler": an 8-bit
+ * KV cache, about half the memory of 16-bit) store a code c meaning
+ * value(c) * scale with one fp32 scale per pool:
+ *   PA_FP8_E4M3  OCP e4m3 "fn": 1 sign, 4 exponent (bias 7), 3 mantissa
+ *                bits, S.1111.111 = NaN, max +-448, no infinities;
+ *   PA_FP8_E5M2  OCP e5m2: 1 sign, 5 exponent (bias 15), 2 mantissa bits,
+ *                IEEE-style infinities and NaNs, max +-57344. */
 typedef enum pa_dtype {
   PA_F32 = 0,
   PA_F16 = 1,
   PA_BF16 = 2,
-  PA_FP8_E4M3 = 3
+  PA_FP8_E4M3 = 3,
+  PA_FP8_E5M2 = 4
 } pa_dtype;
 
 typedef enum pa_status {
@@ -102,8 +106,8 @@ typedef struct pa_decode_args {
 
 /* Supported decode combinations (others return PA_ERR_UNSUPPORTED):
  *   D in {64, 128}; block_size in {16, 32};
- *   (q, kv) in {(F32,F32), (F16,F16), (BF16,BF16), (BF16,FP8_E4M3),
- *   (F16,FP8_E4M3)}; out_dtype = q_dtype or PA_F32;
+ *   (q, kv) in {(F32,F32), (F16,F16), (BF16,BF16), and BF16 or F16 over
+ *   FP8_E4M3 or FP8_E5M2}; out_dtype = q_dtype or PA_F32;
  *   G = Hq/Hkv from 1 to 16, except fp32 caches: G in {1, 2, 4, 8}. */
 
 /* Schedules.
@@ -178,10 +182,11 @@ pa_status pa_slot_mapping(const int32_t* block_tables, const int32_t* positions,
  * every i < T with 0 <= slot_mapping[i] < num_blocks*block_size,
  *   k_cache[slot / bs][slot % bs][:][:] = enc(k_new[i][:][:]), same for V.
  * k_new, v_new: [T][Hkv][D] of src_dtype.  enc is the identity (a bit copy)
- * when src_dtype == kv_dtype.  For kv_dtype == PA_FP8_E4M3 and src_dtype in
- * {F32, F16, BF16}: enc(x) = e4m3(fl32(x * fl32(1/k_scale))) (v_scale for V),
- * rounded to nearest even, saturating to +-448 (also +-inf), NaN -> 0x7F
- * with the NaN's sign.  Other combinations return PA_ERR_UNSUPPORTED. */
+ * when src_dtype == kv_dtype.  For an 8-bit kv_dtype and src_dtype in
+ * {F32, F16, BF16}: enc(x) = fp8(fl32(x * fl32(1/k_scale))) (v_scale for V),
+ * rounded to nearest even and saturating to the format's largest finite
+ * value (+-448 for e4m3, +-57344 for e5m2; +-inf too), NaN -> 0x7F with the
+ * NaN's sign.  Other combinations return PA_ERR_UNSUPPORTED. */
 pa_status pa_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
                                int32_t block_size, int32_t num_blocks, pa_dtype src_dtype,
@@ -243,7 +248,8 @@ typedef struct pa_prefill_args {
 
 /* Supported prefill combinations (others return PA_ERR_UNSUPPORTED):
  *   D in {64, 128}; block_size in {16, 32}; G = Hq/Hkv from 1 to 16;
- *   (q, kv) in {(F16,F16), (BF16,BF16), (BF16,FP8_E4M3), (F16,FP8_E4M3)};
+ *   (q, kv) in {(F16,F16), (BF16,BF16), and BF16 or F16 over FP8_E4M3 or
+ *   FP8_E5M2};
  *   out_dtype = q_dtype or PA_F32.  No workspace. */
 
 /* Validate prefill arguments without touching the GPU. */

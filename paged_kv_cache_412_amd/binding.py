@@ -19,13 +19,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpa.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "pa.h")
 
-PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2 = 0, 1, 2, 3, 4
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
           4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH", 6: "PA_ERR_OUT_OF_BLOCKS"}
 PA_ERR_OUT_OF_BLOCKS = 6
-DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "e4m3": PA_FP8_E4M3}
+DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "e4m3": PA_FP8_E4M3, "e5m2": PA_FP8_E5M2}
+# uint8 pools are taken as e4m3 unless the caller names the format (kv_dtype)
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
-               torch.uint8: PA_FP8_E4M3, torch.float8_e4m3fn: PA_FP8_E4M3}
+               torch.uint8: PA_FP8_E4M3, torch.float8_e4m3fn: PA_FP8_E4M3,
+               torch.float8_e5m2: PA_FP8_E5M2}
 
 
 class LibraryNotBuilt(RuntimeError):

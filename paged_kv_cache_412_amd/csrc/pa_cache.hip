@@ -5,7 +5,8 @@
 //   * Slot of a token: block table entry pos / bs, offset pos % bs (P1
 //     "Sayfalama Nasıl Çalışır", code sketch write loop).
 //   * Cache write: the new token's K and V rows go to that slot; an fp8 cache
-//     quantises them with the pool's scale (P1 "İlgili Teknikler").
+//     (e4m3 or e5m2) quantises them with the pool's scale (P1 "İlgili
+//     Teknikler").
 //   * Block copy: a block that other sequences still use is copied before a
 //     sequence writes into it (P1 "Diziler Arasında Blokları Paylaşma").
 // All three are pure data movement; every byte is moved with 16-byte vector
@@ -57,8 +58,9 @@ __global__ __launch_bounds__(256) void cache_copy_kernel(const u32x4* __restrict
   for (int i = threadIdx.x; i < row_chunks; i += blockDim.x) dst[i] = src[i];
 }
 
-// Quantise 8 source elements to 8 e4m3 codes: code = e4m3(fl32(x * inv_scale)).
-template <int SRC>
+// Quantise 8 source elements to 8 codes of format FMT (e4m3 or e5m2):
+// code = fp8(fl32(x * inv_scale)).
+template <int SRC, int FMT>
 __device__ __forceinline__ u32x2 quantize8(const void* src8, float inv) {
   float x[8];
   if constexpr (SRC == PA_F32) {
@@ -92,8 +94,8 @@ __device__ __forceinline__ u32x2 quantize8(const void* src8, float inv) {
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // one correctly rounded fp32 multiply, then the e4m3 rounding
-      word |= f32_to_e4m3_rne_sat(x[4 * w + i] * inv) << (8 * i);
+      // one correctly rounded fp32 multiply, then the 8-bit rounding
+      word |= f32_to_fp8<FMT>(x[4 * w + i] * inv) << (8 * i);
     }
     out[w] = word;
   }
@@ -101,7 +103,7 @@ __device__ __forceinline__ u32x2 quantize8(const void* src8, float inv) {
 }
 
 // grid (T, 2); each thread quantises groups of 8 elements of one row.
-template <int SRC>
+template <int SRC, int FMT>
 __global__ __launch_bounds__(256) void cache_quant_kernel(const char* __restrict__ k_new,
                                                           const char* __restrict__ v_new,
                                                           u32x2* __restrict__ k_cache,
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void cache_quant_kernel(const char* __restrict
   u32x2* dst = (is_k ? k_cache : v_cache) + static_cast<size_t>(slot) * (row_elems / 8);
   const float inv = is_k ? k_inv : v_inv;
   for (int i = threadIdx.x; i < row_elems / 8; i += blockDim.x)
-    dst[i] = quantize8<SRC>(src + static_cast<size_t>(i) * 8 * SB, inv);
+    dst[i] = quantize8<SRC, FMT>(src + static_cast<size_t>(i) * 8 * SB, inv);
 }
 
 // ------------------------------------------------------------------ block copy
@@ -181,27 +183,26 @@ hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* 
   const int32_t row_elems = Hkv * D;
   dim3 grid(T, 2);
   if (src_dtype == kv_dtype) {
-    int ebytes = kv_dtype == PA_F32 ? 4 : (kv_dtype == PA_FP8_E4M3 ? 1 : 2);
+    int ebytes = kv_dtype == PA_F32 ? 4 : (is_fp8(kv_dtype) ? 1 : 2);
     const int32_t row_chunks = row_elems * ebytes / 16;
     hipLaunchKernelGGL(cache_copy_kernel, grid, dim3(256), 0, stream,
                        static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new),
                        static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slots, row_chunks,
                        num_slots);
-  } else if (src_dtype == PA_F32) {
-    hipLaunchKernelGGL(cache_quant_kernel<PA_F32>, grid, dim3(256), 0, stream,
-                       static_cast<const char*>(k_new), static_cast<const char*>(v_new),
-                       static_cast<u32x2*>(k_cache), static_cast<u32x2*>(v_cache), slots, row_elems,
-                       num_slots, k_inv_scale, v_inv_scale);
-  } else if (src_dtype == PA_F16) {
-    hipLaunchKernelGGL(cache_quant_kernel<PA_F16>, grid, dim3(256), 0, stream,
-                       static_cast<const char*>(k_new), static_cast<const char*>(v_new),
-                       static_cast<u32x2*>(k_cache), static_cast<u32x2*>(v_cache), slots, row_elems,
-                       num_slots, k_inv_scale, v_inv_scale);
   } else {
-    hipLaunchKernelGGL(cache_quant_kernel<PA_BF16>, grid, dim3(256), 0, stream,
-                       static_cast<const char*>(k_new), static_cast<const char*>(v_new),
-                       static_cast<u32x2*>(k_cache), static_cast<u32x2*>(v_cache), slots, row_elems,
-                       num_slots, k_inv_scale, v_inv_scale);
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, static_cast<const char*>(k_new),
+                         static_cast<const char*>(v_new), static_cast<u32x2*>(k_cache),
+                         static_cast<u32x2*>(v_cache), slots, row_elems, num_slots, k_inv_scale,
+                         v_inv_scale);
+    };
+    const bool e5 = kv_dtype == PA_FP8_E5M2;
+    if (src_dtype == PA_F32)
+      e5 ? go(cache_quant_kernel<PA_F32, PA_FP8_E5M2>) : go(cache_quant_kernel<PA_F32, PA_FP8_E4M3>);
+    else if (src_dtype == PA_F16)
+      e5 ? go(cache_quant_kernel<PA_F16, PA_FP8_E5M2>) : go(cache_quant_kernel<PA_F16, PA_FP8_E4M3>);
+    else
+      e5 ? go(cache_quant_kernel<PA_BF16, PA_FP8_E5M2>) : go(cache_quant_kernel<PA_BF16, PA_FP8_E4M3>);
   }
   return hipGetLastError();
 }

@@ -34,8 +34,9 @@
 //   rows, and the 16 lanes of a group cover each row whole (coalesced).
 // The running maximum is kept exact per query: when a block raises it, the
 // accumulators of the affected queries are rescaled (rare after the first
-// blocks).  e4m3 codes are widened to the operand type (bf16 or f16, both
-// hold every e4m3 value exactly) in registers before the MFMAs.
+// blocks).  8-bit codes (e4m3 or e5m2) are widened to the operand type (bf16
+// or f16, both hold every value of either format exactly) in registers
+// before the MFMAs.
 
 #include <hip/hip_runtime.h>
 
@@ -52,7 +53,7 @@ constexpr int kMfmaHeads = 8;
 template <int KV, int Q, int D, int BS, int ST>
 __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const DecodeParams p) {
   using M = Mfma<Q>;
-  constexpr bool FP8 = KV == PA_FP8_E4M3;
+  constexpr bool FP8 = is_fp8(KV);
   constexpr int KVB = FP8 ? 1 : 2;
   constexpr int SS = D / 32;                    // score MFMAs per tile (32 head-dim values each)
   constexpr int EPL = D / 16;                   // V elements per lane per row = PV MFMAs per tile
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
         uint32_t kw[KW];
         if constexpr (FP8) {
 #pragma unroll
-          for (int i = 0; i < KR; ++i) M::widen4(r.k[tt][i], kw[2 * i], kw[2 * i + 1]);
+          for (int i = 0; i < KR; ++i) widen_fp8<Q, KV>(r.k[tt][i], kw[2 * i], kw[2 * i + 1]);
         } else {
 #pragma unroll
           for (int i = 0; i < KW; ++i) kw[i] = r.k[tt][i];
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
         for (int e = 0; e < 4; ++e) {
           if constexpr (FP8) {
 #pragma unroll
-            for (int i = 0; i < VR; ++i) M::widen4(r.v[tt][e][i], vw[e][2 * i], vw[e][2 * i + 1]);
+            for (int i = 0; i < VR; ++i) widen_fp8<Q, KV>(r.v[tt][e][i], vw[e][2 * i], vw[e][2 * i + 1]);
           } else {
 #pragma unroll
             for (int i = 0; i < VW; ++i) vw[e][i] = r.v[tt][e][i];
@@ -321,6 +322,8 @@ bool dispatch(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype, F&& f)
   if (kv_dtype == PA_BF16 && q_dtype == PA_BF16) return by_dim<PA_BF16, PA_BF16>(p, f);
   if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16) return by_dim<PA_FP8_E4M3, PA_BF16>(p, f);
   if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16) return by_dim<PA_FP8_E4M3, PA_F16>(p, f);
+  if (kv_dtype == PA_FP8_E5M2 && q_dtype == PA_BF16) return by_dim<PA_FP8_E5M2, PA_BF16>(p, f);
+  if (kv_dtype == PA_FP8_E5M2 && q_dtype == PA_F16) return by_dim<PA_FP8_E5M2, PA_F16>(p, f);
   return false;
 }
 
@@ -331,7 +334,7 @@ int32_t decode_mfma_heads() { return kMfmaHeads; }
 bool decode_mfma_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t group) {
   if (group < 3 || group > 16) return false;
   return (kv_dtype == PA_F16 && q_dtype == PA_F16) || (kv_dtype == PA_BF16 && q_dtype == PA_BF16) ||
-         (kv_dtype == PA_FP8_E4M3 && (q_dtype == PA_BF16 || q_dtype == PA_F16));
+         (is_fp8(kv_dtype) && (q_dtype == PA_BF16 || q_dtype == PA_F16));
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype,

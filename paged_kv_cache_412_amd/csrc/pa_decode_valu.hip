@@ -133,9 +133,10 @@ struct Ops<PA_BF16, PA_BF16> {
   }
 };
 
-// e4m3 cache with 16-bit queries: codes decoded to fp32, fp32 FMAs.
-template <int Q>
-struct OpsE4M3 {
+// 8-bit cache (e4m3 or e5m2) with 16-bit queries: codes decoded to fp32,
+// fp32 FMAs.
+template <int Q, int FMT>
+struct OpsFP8 {
   static constexpr int CE = 16;
   struct QReg {
     float f[16];
@@ -148,7 +149,7 @@ struct OpsE4M3 {
   }
   __device__ static void to_f32(const Chunk& v, float* o) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e4m3x4_to_f32(v.w[i], o + 4 * i);
+    for (int i = 0; i < 4; ++i) fp8x4_to_f32<FMT>(v.w[i], o + 4 * i);
   }
   __device__ static float dot(const QReg& q, const Chunk& k) {
     float kf[16];
@@ -160,9 +161,13 @@ struct OpsE4M3 {
   }
 };
 template <>
-struct Ops<PA_FP8_E4M3, PA_BF16> : OpsE4M3<PA_BF16> {};
+struct Ops<PA_FP8_E4M3, PA_BF16> : OpsFP8<PA_BF16, PA_FP8_E4M3> {};
 template <>
-struct Ops<PA_FP8_E4M3, PA_F16> : OpsE4M3<PA_F16> {};
+struct Ops<PA_FP8_E4M3, PA_F16> : OpsFP8<PA_F16, PA_FP8_E4M3> {};
+template <>
+struct Ops<PA_FP8_E5M2, PA_BF16> : OpsFP8<PA_BF16, PA_FP8_E5M2> {};
+template <>
+struct Ops<PA_FP8_E5M2, PA_F16> : OpsFP8<PA_F16, PA_FP8_E5M2> {};
 
 // ------------------------------------------------------------------ kernel
 
@@ -378,6 +383,8 @@ bool dispatch(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype, F&& f)
   if (kv_dtype == PA_BF16 && q_dtype == PA_BF16) return by_dim<PA_BF16, PA_BF16>(p, f);
   if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_BF16) return by_dim<PA_FP8_E4M3, PA_BF16>(p, f);
   if (kv_dtype == PA_FP8_E4M3 && q_dtype == PA_F16) return by_dim<PA_FP8_E4M3, PA_F16>(p, f);
+  if (kv_dtype == PA_FP8_E5M2 && q_dtype == PA_BF16) return by_dim<PA_FP8_E5M2, PA_BF16>(p, f);
+  if (kv_dtype == PA_FP8_E5M2 && q_dtype == PA_F16) return by_dim<PA_FP8_E5M2, PA_F16>(p, f);
   return false;
 }
 

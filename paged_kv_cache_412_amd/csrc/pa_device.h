@@ -101,6 +101,13 @@ template <>
 struct Elem<PA_FP8_E4M3> {
   static constexpr int bytes = 1;
 };
+template <>
+struct Elem<PA_FP8_E5M2> {
+  static constexpr int bytes = 1;
+};
+
+// Whether a cache dtype is one of the 8-bit formats.
+constexpr bool is_fp8(int dt) { return dt == PA_FP8_E4M3 || dt == PA_FP8_E5M2; }
 
 // Scalar element of a 16-bit or 32-bit type -> fp32 (exact).
 template <int DT>
@@ -174,6 +181,59 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float y) {
   uint32_t code = ((e << 3) | keep) + up;
   if (code > 0x7eu) code = 0x7eu;                            // [448, 464) rounds into 0x7E
   return sign | code;
+}
+
+// ---------------------------------------------------------------- e5m2 codec
+
+// Decode four e5m2 codes to fp32 (gfx950 bf8 conversion; OCP e5m2: bias 15,
+// IEEE-style inf/NaN, max 57344).
+__device__ __forceinline__ void e5m2x4_to_f32(uint32_t w, float* out) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+// Encode fp32 -> e5m2 code: round to nearest even, magnitudes that round
+// beyond 57344 (and +-inf) saturate to +-57344, NaN -> 0x7F with the NaN's
+// sign.  Integer arithmetic on the fp32 fields, from the format definition:
+//   |y| <  2^-14 : subnormal binade, code = rint(|y| * 2^16)  (0..4; 4 is 2^-14)
+//   |y| >= 2^-14 : keep 2 fraction bits, round the 21 dropped bits half to
+//                  even; a carry moves into the exponent.
+__device__ __forceinline__ uint32_t f32_to_e5m2_rne_sat(float y) {
+  const uint32_t u = f2u(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t ua = u & 0x7fffffffu;
+  if (ua > 0x7f800000u) return sign | 0x7fu;                 // NaN
+  if (ua >= 0x47600000u) return sign | 0x7bu;               // |y| >= 57344 (incl. inf)
+  if (ua < 0x38800000u) {                                    // |y| < 2^-14
+    const float m = __builtin_rintf(u2f(ua) * 65536.0f);     // exact scale, RNE
+    return sign | static_cast<uint32_t>(m);
+  }
+  const uint32_t e = (ua >> 23) - 127u + 15u;                // biased e5m2 exponent, 1..30
+  const uint32_t frac = ua & 0x7fffffu;
+  const uint32_t keep = frac >> 21;
+  const uint32_t rest = frac & 0x1fffffu;
+  const uint32_t up = (rest > 0x100000u) || (rest == 0x100000u && (keep & 1u));
+  uint32_t code = ((e << 2) | keep) + up;
+  if (code > 0x7bu) code = 0x7bu;
+  return sign | code;
+}
+
+// 8-bit code of fp32 y in the cache format FMT (PA_FP8_E4M3 or PA_FP8_E5M2).
+template <int FMT>
+__device__ __forceinline__ uint32_t f32_to_fp8(float y) {
+  if constexpr (FMT == PA_FP8_E5M2) return f32_to_e5m2_rne_sat(y);
+  else return f32_to_e4m3_rne_sat(y);
+}
+
+// Four 8-bit codes of format FMT to fp32 (exact).
+template <int FMT>
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
+  if constexpr (FMT == PA_FP8_E5M2) e5m2x4_to_f32(w, out);
+  else e4m3x4_to_f32(w, out);
 }
 
 // ---------------------------------------------------------------- DPP reductions

@@ -62,6 +62,11 @@ struct Mfma<PA_BF16> {
     lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   }
+  // four e5m2 codes -> two dwords of bf16 pairs (exact)
+  __device__ static void widen4_e5m2(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true));
+  }
 };
 
 template <>
@@ -96,7 +101,19 @@ struct Mfma<PA_F16> {
     lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
   }
+  __device__ static void widen4_e5m2(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, true));
+  }
 };
+
+// Four 8-bit codes of cache format KV (e4m3 or e5m2) -> two dwords of pairs of
+// the operand type Q (bf16 and f16 hold every value of both formats exactly).
+template <int Q, int KV>
+__device__ __forceinline__ void widen_fp8(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  if constexpr (KV == PA_FP8_E5M2) Mfma<Q>::widen4_e5m2(w, lo, hi);
+  else Mfma<Q>::widen4(w, lo, hi);
+}
 
 // Half `sel` (0 = low, 1 = high) of dwords a and b, packed as (a_half, b_half).
 __device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int sel) {

@@ -214,12 +214,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
       if constexpr (KVB == 2) {
         *reinterpret_cast<u32x4*>(kd + lds_off(r, schunk)) = kst[ps];
         *reinterpret_cast<u32x4*>(vd + lds_off(r, schunk)) = vst[ps];
-      } else {  // 16 e4m3 codes -> 16 operand values (exact), two chunks
+      } else {  // 16 8-bit codes -> 16 operand values (exact), two chunks
         uint32_t w[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          M::widen4(kst[ps][i], w[2 * i], w[2 * i + 1]);
-          M::widen4(vst[ps][i], w[8 + 2 * i], w[8 + 2 * i + 1]);
+          widen_fp8<Q, KV>(kst[ps][i], w[2 * i], w[2 * i + 1]);
+          widen_fp8<Q, KV>(vst[ps][i], w[8 + 2 * i], w[8 + 2 * i + 1]);
         }
         *reinterpret_cast<u32x4*>(kd + lds_off(r, 2 * schunk)) = u32x4{w[0], w[1], w[2], w[3]};
         *reinterpret_cast<u32x4*>(kd + lds_off(r, 2 * schunk + 1)) = u32x4{w[4], w[5], w[6], w[7]};
@@ -419,6 +419,8 @@ bool dispatch(pa_dtype q, pa_dtype kv, int32_t D, int32_t bs, int32_t G, F&& f) 
   if (kv == PA_BF16 && q == PA_BF16) return by_dim<PA_BF16, PA_BF16>(D, bs, G, f);
   if (kv == PA_FP8_E4M3 && q == PA_BF16) return by_dim<PA_FP8_E4M3, PA_BF16>(D, bs, G, f);
   if (kv == PA_FP8_E4M3 && q == PA_F16) return by_dim<PA_FP8_E4M3, PA_F16>(D, bs, G, f);
+  if (kv == PA_FP8_E5M2 && q == PA_BF16) return by_dim<PA_FP8_E5M2, PA_BF16>(D, bs, G, f);
+  if (kv == PA_FP8_E5M2 && q == PA_F16) return by_dim<PA_FP8_E5M2, PA_F16>(D, bs, G, f);
   return false;
 }
 

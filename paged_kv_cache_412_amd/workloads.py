@@ -23,7 +23,8 @@ Workloads (shapes follow the pages' examples; P1 = Ultralytics glossary page
 * ``long_fp8`` / ``long_fp8_bs32`` -- long context with an e4m3 cache and one
   fp32 scale per pool (P1 "İlgili Teknikler": GQA and FP8 cache), 32 query /
   8 KV heads, head dim 128, batch 16, lengths uniform in [16384, 32768],
-  block size 16 or 32, bf16 queries and new rows.
+  block size 16 or 32, bf16 queries and new rows.  ``long_e5m2`` is the same
+  with an e5m2 cache (the other 8-bit flavour).
 
 Prefill workloads (several new tokens per sequence, :func:`make_prefill`):
 
@@ -73,9 +74,12 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 import torch
 
-F32, F16, BF16, E4M3 = "f32", "f16", "bf16", "e4m3"
-TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, E4M3: torch.uint8}
-ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
+F32, F16, BF16, E4M3, E5M2 = "f32", "f16", "bf16", "e4m3", "e5m2"
+TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, E4M3: torch.uint8,
+               E5M2: torch.uint8}
+ELEM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1, E5M2: 1}
+FP8_MAX = {E4M3: 448.0, E5M2: 57344.0}
+FP8_TORCH = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
 
 
 @dataclass(frozen=True)
@@ -125,6 +129,8 @@ CONFIGS = {
     "long_fp8_bs32": Config("long_fp8_bs32", 6, B=16, Hq=32, Hkv=8, D=128, block_size=32,
                             kv_dtype=E4M3, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
                             len_range=(16384, 32768)),
+    "long_e5m2": Config("long_e5m2", 12, B=16, Hq=32, Hkv=8, D=128, block_size=16, kv_dtype=E5M2,
+                        q_dtype=BF16, out_dtype=BF16, src_dtype=BF16, len_range=(16384, 32768)),
     # prefill: several new tokens per sequence, causal over the paged context
     "prefill13b": Config("prefill13b", 7, B=16, Hq=40, Hkv=40, D=128, block_size=16, kv_dtype=F16,
                          q_dtype=F16, out_dtype=F16, src_dtype=F16,
@@ -189,17 +195,18 @@ def _ceil_div(a: int, b: int) -> int:
 
 
 def _poison_value(dtype: str):
-    return 0x7F if dtype == E4M3 else float("nan")
+    return 0x7F if dtype in FP8_MAX else float("nan")
 
 
 def _fill_values(shape, dtype: str, gen: torch.Generator, device, sigma: float = 1.0):
-    """N(0, sigma^2) draws rounded to ``dtype``; e4m3 returns (codes, scale)."""
+    """N(0, sigma^2) draws rounded to ``dtype``; 8-bit formats return (codes,
+    scale) with scale = amax / (the format's largest finite value)."""
     x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
     if sigma != 1.0:
         x.mul_(sigma)
-    if dtype == E4M3:
-        scale = float(x.abs().max()) / 448.0
-        codes = (x / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    if dtype in FP8_MAX:
+        scale = float(x.abs().max()) / FP8_MAX[dtype]
+        codes = (x / scale).clamp_(-FP8_MAX[dtype], FP8_MAX[dtype]).to(FP8_TORCH[dtype]).view(torch.uint8)
         return codes, scale
     return x.to(TORCH_DTYPE[dtype]), 1.0
 

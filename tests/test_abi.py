@@ -72,8 +72,8 @@ def test_decode_check_accepts_valid(L):
     assert check(L, Hq=64, Hkv=8, D=128) == 0
     # any group of 1..16 with 16-bit queries over 16-bit or e4m3 caches
     for G in (1, 2, 3, 4, 5, 6, 7, 8, 12, 16):
-        for kv in (binding.PA_F16, binding.PA_FP8_E4M3):
-            sc = 0.5 if kv == binding.PA_FP8_E4M3 else 1.0
+        for kv in (binding.PA_F16, binding.PA_FP8_E4M3, binding.PA_FP8_E5M2):
+            sc = 1.0 if kv == binding.PA_F16 else 0.5
             assert check(L, Hq=2 * G, Hkv=2, q_dtype=binding.PA_F16, kv_dtype=kv,
                          out_dtype=binding.PA_F16, k_scale=sc, v_scale=sc) == 0, (G, kv)
     assert check(L, Hq=34, Hkv=2, q_dtype=binding.PA_F16, kv_dtype=binding.PA_F16,
@@ -188,7 +188,7 @@ def pcheck(L, **kw):
 def test_prefill_check_accepts_supported_combinations(L):
     P = binding
     for q, kv in ((P.PA_F16, P.PA_F16), (P.PA_BF16, P.PA_BF16), (P.PA_BF16, P.PA_FP8_E4M3),
-                  (P.PA_F16, P.PA_FP8_E4M3)):
+                  (P.PA_F16, P.PA_FP8_E4M3), (P.PA_BF16, P.PA_FP8_E5M2), (P.PA_F16, P.PA_FP8_E5M2)):
         for out in (q, P.PA_F32):
             for D in (64, 128):
                 for bs in (16, 32):

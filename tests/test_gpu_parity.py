@@ -169,15 +169,21 @@ def test_peaked_attention(name, sigma):
     check_step(wl, step, exp, out_dtype="f32")
 
 
+FP8_ONE = {"e4m3": 0x38, "e5m2": 0x3C}           # the code of 1.0
+FP8_TABLE = {"e4m3": fp8.DECODE_TABLE, "e5m2": fp8.DECODE_TABLE_E5M2}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("qdt", [torch.bfloat16, torch.float16])
-def test_e4m3_decode_every_code_exactly(G, qdt):
+def test_fp8_decode_every_code_exactly(fmt, G, qdt):
     """L = 1 puts all weight on one V row, so out = decode(code) * v_scale
-    exactly, on the vector path (G <= 2) and the matrix-core path (G >= 4)."""
-    print(f"\n[case] e4m3 decode of all 256 codes, G={G} q={qdt}", flush=True)
+    exactly (infinities and NaNs included), on the vector path (G <= 2) and
+    the matrix-core path (G >= 4), for both 8-bit formats."""
+    print(f"\n[case] {fmt} decode of all 256 codes, G={G} q={qdt}", flush=True)
     D, bs, NB = 128, 16, 4
     dev = "cuda"
-    k = torch.full((NB, bs, 1, D), 0x38, dtype=torch.uint8, device=dev)      # 1.0
+    k = torch.full((NB, bs, 1, D), FP8_ONE[fmt], dtype=torch.uint8, device=dev)
     v = torch.zeros((NB, bs, 1, D), dtype=torch.uint8, device=dev)
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
     v[1, 0, 0, :] = codes[:128].to(dev)
@@ -186,9 +192,9 @@ def test_e4m3_decode_every_code_exactly(G, qdt):
     tables = torch.tensor([[1], [2]], dtype=torch.int32, device=dev)
     lens = torch.tensor([1, 1], dtype=torch.int32, device=dev)
     out = torch.empty((2, G, D), dtype=torch.float32, device=dev)
-    binding.decode(out, q, k, v, tables, lens, 0.1, 1.0, 1.0, kv_dtype="e4m3")
+    binding.decode(out, q, k, v, tables, lens, 0.1, 1.0, 1.0, kv_dtype=fmt)
     torch.cuda.synchronize()
-    ref = fp8.DECODE_TABLE
+    ref = FP8_TABLE[fmt]
     nan = np.isnan(ref)
     for h in range(G):
         got = out[:, h].cpu().numpy().reshape(256).astype(np.float64)
@@ -197,7 +203,8 @@ def test_e4m3_decode_every_code_exactly(G, qdt):
 
 
 # every (q, kv) pair, head dim, block size and group size the library builds
-DTYPE_PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3")]
+DTYPE_PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3"),
+               ("bf16", "e5m2"), ("f16", "e5m2")]
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
@@ -214,7 +221,7 @@ def test_every_supported_shape(pair, D, bs, G):
     print(f"[ok] max abs err {err:.3e}", flush=True)
 
 
-MFMA_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3")]
+MFMA_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e5m2")]
 
 
 @pytest.mark.parametrize("G", [3, 5, 6, 7, 12, 16])
@@ -233,12 +240,18 @@ def test_other_group_sizes(pair, G):
         print(f"[ok] G={G} bs={bs} max abs err {err:.3e}", flush=True)
 
 
-def e4m3_sweep_values(rng):
-    """fp32 values around every e4m3 value and midpoint (+-4 ulps), specials,
-    and random draws over the whole e4m3 range."""
-    vals = fp8.DECODE_TABLE[:0x7F]
+def fp8_sweep_values(rng, fmt):
+    """fp32 values around every finite value and midpoint of the format (+-4
+    ulps), just past its largest value, specials, and random draws over its
+    whole range."""
+    table = FP8_TABLE[fmt]
+    top = 0x7F if fmt == "e4m3" else 0x7C
+    vals = table[:top]
+    big = table[top - 1]
     mids = (vals[:-1] + vals[1:]) / 2
-    pts = np.concatenate([vals, mids, [464.0, 465.0, 479.0, 480.0, 1e6, 2.0 ** -10, 3 * 2.0 ** -11]])
+    step = vals[-1] - vals[-2]
+    pts = np.concatenate([vals, mids, [big + step / 2 - 1, big + step / 2, big + step, 1e6 * big,
+                                       vals[1] / 2, vals[1] * 1.5]])
     pts32 = pts.astype(np.float32)
     around = [pts32]
     for k in range(1, 5):
@@ -249,17 +262,22 @@ def e4m3_sweep_values(rng):
     x = np.concatenate(around + down)
     x = np.concatenate([x, -x, np.array([np.inf, -np.inf, np.nan, -np.nan, 0.0, -0.0,
                                          1e-45, -1e-45], dtype=np.float32)])
-    rand = (rng.standard_normal(1 << 22) * np.exp2(rng.uniform(-12, 10, 1 << 22))).astype(np.float32)
+    lo, hi = (-12, 10) if fmt == "e4m3" else (-18, 17)
+    rand = (rng.standard_normal(1 << 22) * np.exp2(rng.uniform(lo, hi, 1 << 22))).astype(np.float32)
     return np.concatenate([x, rand]).astype(np.float32)
 
 
+QUANT = {"e4m3": fp8.quantize, "e5m2": fp8.quantize_e5m2}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("src", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("scale", [1.0, 0.0123])
-def test_e4m3_cache_write_bit_exact(src, scale):
-    print(f"\n[case] e4m3 cache write src={src} scale={scale}", flush=True)
+def test_fp8_cache_write_bit_exact(fmt, src, scale):
+    print(f"\n[case] {fmt} cache write src={src} scale={scale}", flush=True)
     rng = np.random.default_rng(5)
     if src == "f32":
-        x = e4m3_sweep_values(rng)
+        x = fp8_sweep_values(rng, fmt)
         xt = torch.from_numpy(x)
     else:
         # every 16-bit pattern, exhaustively
@@ -277,11 +295,11 @@ def test_e4m3_cache_write_bit_exact(src, scale):
     k_cache = torch.zeros((NB, bs, Hkv, D), dtype=torch.uint8, device="cuda")
     v_cache = torch.zeros_like(k_cache)
     slots = torch.arange(T, dtype=torch.int32, device="cuda")
-    binding.reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, scale, scale * 2, kv_dtype="e4m3")
+    binding.reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, scale, scale * 2, kv_dtype=fmt)
     torch.cuda.synchronize()
     src_vals = parity.widen(parity.storage(xt), src)
-    ref_k = fp8.quantize(src_vals, scale).reshape(-1)
-    ref_v = fp8.quantize(parity.widen(parity.storage(xt.flip(0).contiguous()), src), scale * 2).reshape(-1)
+    ref_k = QUANT[fmt](src_vals, scale).reshape(-1)
+    ref_v = QUANT[fmt](parity.widen(parity.storage(xt.flip(0).contiguous()), src), scale * 2).reshape(-1)
     got_k = k_cache.cpu().numpy().reshape(-1)[: T * row]
     got_v = v_cache.cpu().numpy().reshape(-1)[: T * row]
     bad = np.nonzero(got_k != ref_k)[0]

@@ -73,7 +73,8 @@ def test_prefill_small_all_rows(name):
     print(f"[ok] {name} max abs err {err:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("pair", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3")])
+@pytest.mark.parametrize("pair", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3"),
+                                  ("bf16", "e5m2"), ("f16", "e5m2")])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 16])
