@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 /* Element types.  The 8-bit cache formats (P1 "İlgili Teknikler": an 8-bit
  * KV cache, about half the memory of 16-bit) store a code c meaning
@@ -102,6 +102,10 @@ typedef struct pa_decode_args {
                                /* a multiple of block_size; 0: balanced schedule      */
   void* workspace;             /* device scratch (layout below), 16-byte aligned      */
   size_t workspace_bytes;      /* >= pa_decode_workspace_size(args)                   */
+  const float* k_scales;       /* NULL, or per-KV-head scales [Hkv] (device memory)   */
+  const float* v_scales;       /* for an 8-bit cache: replace k_scale / v_scale, head */
+                               /* g's codes meaning value * k_scales[g]; both or      */
+                               /* neither; positive and finite (not checked)          */
 } pa_decode_args;
 
 /* Supported decode combinations (others return PA_ERR_UNSUPPORTED):
@@ -148,6 +152,7 @@ pa_status pa_decode_check(const pa_decode_args* a);
  * query head h, with g = h / (Hq/Hkv) and L = seq_lens[b]:
  *   s_t   = scale * k_scale * sum_d q[b,h,d] * K[t,g,d]      for t < L
  *   out   = v_scale * sum_t exp(s_t - max s) V[t,g,:] / sum_t exp(s_t - max s)
+ * (k_scales[g] and v_scales[g] in place of k_scale and v_scale when given)
  * where K[t,g,:] is row (t mod bs, g) of block block_tables[b][t / bs].
  * L = 0 gives zeros.  fp32 accumulation; out rounded to nearest even.
  * Equivalent to pa_decode_partition followed by pa_decode_reduce. */
@@ -191,6 +196,19 @@ pa_status pa_reshape_and_cache(const void* k_new, const void* v_new, void* k_cac
                                const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
                                int32_t block_size, int32_t num_blocks, pa_dtype src_dtype,
                                pa_dtype kv_dtype, float k_scale, float v_scale, void* stream);
+
+/* Cache write into an 8-bit cache with one scale per KV head (P1 "İlgili
+ * Teknikler": 8-bit caches; a finer scale than one per pool).  As
+ * pa_reshape_and_cache with src_dtype in {F32, F16, BF16} and kv_dtype
+ * 8-bit, except that head g of every row uses k_scales[g] (v_scales[g] for
+ * V): enc(x) = fp8(fl32(x * fl32(1/k_scales[g]))).  k_scales, v_scales:
+ * device arrays [Hkv] of positive finite fp32 (not checked).  Other dtype
+ * combinations return PA_ERR_UNSUPPORTED. */
+pa_status pa_reshape_and_cache_scales(const void* k_new, const void* v_new, void* k_cache,
+                                      void* v_cache, const int32_t* slot_mapping, int32_t T,
+                                      int32_t Hkv, int32_t D, int32_t block_size,
+                                      int32_t num_blocks, pa_dtype src_dtype, pa_dtype kv_dtype,
+                                      const float* k_scales, const float* v_scales, void* stream);
 
 /* Copy-on-write block copy (P1 "Diziler Arasında Blokları Paylaşma": a
  * sequence about to write into a block that other sequences still use gets a
@@ -244,6 +262,8 @@ typedef struct pa_prefill_args {
   float scale;                 /* softmax scale, e.g. 1/sqrt(D)                       */
   float k_scale, v_scale;      /* fp8 dequantisation scales; must be 1 otherwise      */
   pa_dtype q_dtype, kv_dtype, out_dtype;
+  const float* k_scales;       /* NULL, or per-KV-head scales [Hkv] (device memory),  */
+  const float* v_scales;       /* as in pa_decode_args                                */
 } pa_prefill_args;
 
 /* Supported prefill combinations (others return PA_ERR_UNSUPPORTED):

@@ -52,6 +52,7 @@ class DecodeArgs(ctypes.Structure):
         ("v_scale", ctypes.c_float), ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
         ("out_dtype", ctypes.c_int), ("partition_size", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
     ]
 
 
@@ -66,7 +67,7 @@ class PrefillArgs(ctypes.Structure):
         ("D", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32), ("scale", ctypes.c_float), ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float), ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
-        ("out_dtype", ctypes.c_int),
+        ("out_dtype", ctypes.c_int), ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
     ]
 
 
@@ -104,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                        ctypes.c_int, f32, f32, vp]
     L.pa_reshape_and_cache.restype = ctypes.c_int
+    L.pa_reshape_and_cache_scales.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                              ctypes.c_int, vp, vp, vp]
+    L.pa_reshape_and_cache_scales.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     L.pa_copy_blocks.restype = ctypes.c_int
     L.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
@@ -178,8 +182,20 @@ def _require(t: torch.Tensor, name: str, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
+def _head_scales(args, k_scales, v_scales, Hkv):
+    """Per-KV-head scale tensors (fp32 [Hkv] on the GPU) into args."""
+    if k_scales is None and v_scales is None:
+        return
+    for t, n in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        _require(t, n, torch.float32, 1)
+        if t.shape[0] != Hkv:
+            raise ValueError(f"{n} must hold one scale per KV head")
+    args.k_scales, args.v_scales = k_scales.data_ptr(), v_scales.data_ptr()
+
+
 def decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0, v_scale=1.0,
-                partition_size=0, workspace=None, kv_dtype=None) -> DecodeArgs:
+                partition_size=0, workspace=None, kv_dtype=None, k_scales=None,
+                v_scales=None) -> DecodeArgs:
     """Build ``pa_decode_args`` from tensors (shapes per include/pa.h)."""
     for t, n, nd in ((out, "out", 3), (q, "q", 3), (k_cache, "k_cache", 4), (v_cache, "v_cache", 4)):
         _require(t, n, ndim=nd)
@@ -201,6 +217,7 @@ def decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale
     a.kv_dtype = _pa_dtype(k_cache, kv_dtype)
     a.out_dtype = _pa_dtype(out)
     a.partition_size = int(partition_size)
+    _head_scales(a, k_scales, v_scales, Hkv)
     if workspace is not None:
         _require(workspace, "workspace")
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -243,10 +260,10 @@ def decode_reduce_run(args: DecodeArgs, stream=None) -> None:
 
 
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0, v_scale=1.0,
-           partition_size=0, workspace=None, kv_dtype=None, stream=None):
+           partition_size=0, workspace=None, kv_dtype=None, stream=None, k_scales=None, v_scales=None):
     """pa_decode on tensors; allocates the workspace with torch when none is given."""
     a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale,
-                    partition_size, workspace, kv_dtype)
+                    partition_size, workspace, kv_dtype, k_scales, v_scales)
     keep = None
     if workspace is None:
         keep = alloc_workspace(a, q.device)
@@ -267,7 +284,9 @@ def slot_mapping(block_tables, positions, block_size, slots, stream=None):
 
 
 def reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, k_scale=1.0, v_scale=1.0,
-                      kv_dtype=None, stream=None):
+                      kv_dtype=None, stream=None, k_scales=None, v_scales=None):
+    """pa_reshape_and_cache, or pa_reshape_and_cache_scales when per-KV-head
+    scale tensors (fp32 [Hkv] on the GPU) are given."""
     _require(k_new, "k_new", ndim=3)
     _require(v_new, "v_new", ndim=3)
     _require(k_cache, "k_cache", ndim=4)
@@ -279,6 +298,17 @@ def reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, k_scale=1.0, v_scal
         raise ValueError("inconsistent shapes")
     if tuple(v_cache.shape) != tuple(k_cache.shape) or v_new.dtype != k_new.dtype:
         raise ValueError("K and V must match")
+    if k_scales is not None or v_scales is not None:
+        for t, n in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+            _require(t, n, torch.float32, 1)
+            if t.shape[0] != Hkv:
+                raise ValueError(f"{n} must hold one scale per KV head")
+        _check(lib().pa_reshape_and_cache_scales(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                                 _ptr(slots), T, Hkv, D, bs, NB, _pa_dtype(k_new),
+                                                 _pa_dtype(k_cache, kv_dtype), _ptr(k_scales),
+                                                 _ptr(v_scales), _stream(stream)),
+               "pa_reshape_and_cache_scales")
+        return
     _check(lib().pa_reshape_and_cache(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(slots), T, Hkv, D, bs, NB, _pa_dtype(k_new),
                                       _pa_dtype(k_cache, kv_dtype), float(k_scale), float(v_scale),
@@ -298,7 +328,7 @@ def copy_blocks(k_cache, v_cache, block_mapping, kv_dtype=None, stream=None):
 
 
 def prefill_args(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, max_q_len, scale,
-                 k_scale=1.0, v_scale=1.0, kv_dtype=None) -> PrefillArgs:
+                 k_scale=1.0, v_scale=1.0, kv_dtype=None, k_scales=None, v_scales=None) -> PrefillArgs:
     """Build ``pa_prefill_args`` from tensors (shapes per include/pa.h).
     ``max_q_len`` is a host integer: the most new tokens of any sequence."""
     for t, n, nd in ((out, "out", 3), (q, "q", 3), (k_cache, "k_cache", 4), (v_cache, "v_cache", 4)):
@@ -323,6 +353,7 @@ def prefill_args(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, max
     a.q_dtype = _pa_dtype(q)
     a.kv_dtype = _pa_dtype(k_cache, kv_dtype)
     a.out_dtype = _pa_dtype(out)
+    _head_scales(a, k_scales, v_scales, Hkv)
     return a
 
 
@@ -335,10 +366,10 @@ def prefill_run(args: PrefillArgs, stream=None) -> None:
 
 
 def prefill(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, max_q_len, scale,
-            k_scale=1.0, v_scale=1.0, kv_dtype=None, stream=None):
+            k_scale=1.0, v_scale=1.0, kv_dtype=None, stream=None, k_scales=None, v_scales=None):
     """pa_prefill on tensors."""
     prefill_run(prefill_args(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, max_q_len,
-                             scale, k_scale, v_scale, kv_dtype), stream)
+                             scale, k_scale, v_scale, kv_dtype, k_scales, v_scales), stream)
     return out
 
 

@@ -110,7 +110,10 @@ __global__ __launch_bounds__(256) void cache_quant_kernel(const char* __restrict
                                                           u32x2* __restrict__ v_cache,
                                                           const int32_t* __restrict__ slots,
                                                           int32_t row_elems, int64_t num_slots,
-                                                          float k_inv, float v_inv) {
+                                                          float k_inv, float v_inv,
+                                                          const float* __restrict__ k_scales,
+                                                          const float* __restrict__ v_scales,
+                                                          int32_t D) {
   constexpr int SB = Elem<SRC>::bytes;
   const int t = blockIdx.x;
   const int slot = slots[t];
@@ -119,8 +122,13 @@ __global__ __launch_bounds__(256) void cache_quant_kernel(const char* __restrict
   const char* src = (is_k ? k_new : v_new) + static_cast<size_t>(t) * row_elems * SB;
   u32x2* dst = (is_k ? k_cache : v_cache) + static_cast<size_t>(slot) * (row_elems / 8);
   const float inv = is_k ? k_inv : v_inv;
-  for (int i = threadIdx.x; i < row_elems / 8; i += blockDim.x)
-    dst[i] = quantize8<SRC, FMT>(src + static_cast<size_t>(i) * 8 * SB, inv);
+  const float* heads = is_k ? k_scales : v_scales;
+  for (int i = threadIdx.x; i < row_elems / 8; i += blockDim.x) {
+    // per-head scales: fl32(1 / scale) of the head these 8 elements belong
+    // to (a correctly rounded division, as the pool-wide inverse on the host)
+    const float hinv = heads ? 1.0f / heads[(8 * i) / D] : inv;
+    dst[i] = quantize8<SRC, FMT>(src + static_cast<size_t>(i) * 8 * SB, hinv);
+  }
 }
 
 // ------------------------------------------------------------------ block copy
@@ -178,7 +186,8 @@ hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* 
                                     void* v_cache, const int32_t* slots, int32_t T, int32_t Hkv,
                                     int32_t D, int32_t block_size, int32_t num_blocks,
                                     pa_dtype src_dtype, pa_dtype kv_dtype, float k_inv_scale,
-                                    float v_inv_scale, hipStream_t stream) {
+                                    float v_inv_scale, const float* k_scales,
+                                    const float* v_scales, hipStream_t stream) {
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
   const int32_t row_elems = Hkv * D;
   dim3 grid(T, 2);
@@ -194,7 +203,7 @@ hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* 
       hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, static_cast<const char*>(k_new),
                          static_cast<const char*>(v_new), static_cast<u32x2*>(k_cache),
                          static_cast<u32x2*>(v_cache), slots, row_elems, num_slots, k_inv_scale,
-                         v_inv_scale);
+                         v_inv_scale, k_scales, v_scales, D);
     };
     const bool e5 = kv_dtype == PA_FP8_E5M2;
     if (src_dtype == PA_F32)

@@ -218,19 +218,19 @@ __device__ __forceinline__ void store_out_n(void* base, size_t i, const float* v
 
 // Finish N elements [d0, d0+N) of query h of a segment: out (the segment
 // covers its sequence) or its partials row.  m, l: the query's final running
-// max and sum; acc: its unnormalised sums.
+// max and sum; acc: its unnormalised sums; vs: the V scale of its KV head.
 template <int N>
 __device__ __forceinline__ void store_segment(const DecodeParams& p, const SegmentDest& dst, int h,
-                                              int d0, float m, float l, const float* acc) {
+                                              int d0, float m, float l, const float* acc, float vs) {
   float v[N];
   if (dst.complete) {
 #pragma unroll
-    for (int k = 0; k < N; ++k) v[k] = l > 0.f ? (acc[k] / l) * p.v_scale : 0.f;
+    for (int k = 0; k < N; ++k) v[k] = l > 0.f ? (acc[k] / l) * vs : 0.f;
     store_out_n<N>(p.out, (dst.out_row + h) * p.D + d0, v, p.out_dtype);
   } else {
     const size_t r = dst.part_row + h;
 #pragma unroll
-    for (int k = 0; k < N; ++k) v[k] = acc[k] * p.v_scale;
+    for (int k = 0; k < N; ++k) v[k] = acc[k] * vs;
     store_f32_n<N>(p.ws_acc + r * p.D + d0, v);
     if (d0 == 0) {
       p.ws_m[r] = m;

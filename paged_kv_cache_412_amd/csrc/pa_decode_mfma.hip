@@ -93,7 +93,9 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   const int v_off = head_off + 4 * grp * row_stride + EPL * lo * KVB;
   const char* kpool = static_cast<const char*>(p.k_cache);
   const char* vpool = static_cast<const char*>(p.v_cache);
-  const float qk = p.qk_scale_log2;
+  // score scale in log2 units and V scale of this wave's KV head
+  const float qk = p.k_scales ? p.qk_scale_log2 * p.k_scales[g] : p.qk_scale_log2;
+  const float vs = p.v_scales ? p.v_scales[g] : p.v_scale;
 
   struct Raw {
     uint32_t k[TT][KR];
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
         float o[EPL];
 #pragma unroll
         for (int mm = 0; mm < EPL; ++mm) o[mm] = O[mm][i];
-        store_segment<EPL>(p, dst, q, EPL * lo, mq, lq, o);
+        store_segment<EPL>(p, dst, q, EPL * lo, mq, lq, o, vs);
       }
     }
   });

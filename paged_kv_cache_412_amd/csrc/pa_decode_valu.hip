@@ -199,7 +199,9 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
   const int lane_off = static_cast<int>(g * D * KVB + c * 16 + tg * row_stride);
   const char* kpool = static_cast<const char*>(p.k_cache);
   const char* vpool = static_cast<const char*>(p.v_cache);
-  const float qk = p.qk_scale_log2;
+  // score scale in log2 units and V scale of this wave's KV head
+  const float qk = p.k_scales ? p.qk_scale_log2 * p.k_scales[g] : p.qk_scale_log2;
+  const float vs = p.v_scales ? p.v_scales[g] : p.v_scale;
 
   struct Buf {
     Chunk k[NL], v[NL];
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
 
     if (tg == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) store_segment<CE>(p, dst, h, c * CE, m[h], l[h], acc[h]);
+      for (int h = 0; h < G; ++h) store_segment<CE>(p, dst, h, c * CE, m[h], l[h], acc[h], vs);
     }
   });
 }

@@ -41,8 +41,10 @@ struct DecodeParams {
   int32_t heads_per_wg;    // waves (KV heads) per work-group
   int32_t head_groups;     // ceil(Hkv / heads_per_wg)
   int32_t groups;          // balanced: work-groups per head group
-  float qk_scale_log2;     // scale * k_scale * log2(e)
+  float qk_scale_log2;     // scale * k_scale * log2(e) (scale * log2(e) with per-head scales)
   float v_scale;
+  const float* k_scales;   // per-head scales [Hkv] (device) or nullptr
+  const float* v_scales;
   int32_t out_dtype;
 };
 
@@ -104,8 +106,10 @@ struct PrefillParams {
   int32_t B, T, max_q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq;
   int32_t q_tiles;          // query tiles per (sequence, KV head): ceil(max_q_len / floor(128/G))
   int32_t total_groups;     // B * Hkv * q_tiles (the 1-D grid)
-  float qk_scale_log2;      // scale * k_scale * log2(e)
+  float qk_scale_log2;      // scale * k_scale * log2(e) (scale * log2(e) with per-head scales)
   float v_scale;
+  const float* k_scales;    // per-head scales [Hkv] (device) or nullptr
+  const float* v_scales;
   int32_t out_dtype;
 };
 
@@ -153,11 +157,14 @@ hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* positions, int32_t B,
                                int32_t max_blocks, int32_t block_size, int32_t* slots,
                                hipStream_t stream);
+// The cache write; an 8-bit cache takes one inverse scale per pool, or (when
+// k_scales is not null) one scale per KV head from device arrays.
 hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache,
                                     void* v_cache, const int32_t* slots, int32_t T, int32_t Hkv,
                                     int32_t D, int32_t block_size, int32_t num_blocks,
                                     pa_dtype src_dtype, pa_dtype kv_dtype, float k_inv_scale,
-                                    float v_inv_scale, hipStream_t stream);
+                                    float v_inv_scale, const float* k_scales,
+                                    const float* v_scales, hipStream_t stream);
 // Whole-block copies from the source pools to the destination pools (the
 // same pools for copy-on-write, a device and a pinned host pool for swap).
 hipError_t launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,

@@ -137,7 +137,8 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   // the queries negated (exact for 16-bit values), so the running max can be
   // taken over unscaled scores; c = 0 is taken as the smallest normal float
   // (every weight still rounds to 1) so that masked scores stay -inf.
-  const float c_in = p.qk_scale_log2;
+  const float c_in = p.k_scales ? p.qk_scale_log2 * p.k_scales[kvh] : p.qk_scale_log2;
+  const float vs = p.v_scales ? p.v_scales[kvh] : p.v_scale;
   const uint32_t qflip = c_in < 0.f ? 0x80008000u : 0u;
   const float c = fmaxf(fabsf(c_in), 1.17549435e-38f);
 
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
     if (!valid[nt]) continue;
     // lt > 0: the running max never exceeds the largest score seen, whose
     // weight 2^(s - m) is therefore about 1 or more
-    const float inv = p.v_scale / lt;
+    const float inv = vs / lt;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float v[EPL];

@@ -22,7 +22,7 @@ import torch
 
 from . import binding
 from .blocks import BlockManager
-from .workloads import TORCH_DTYPE, Workload, pad_tables
+from .workloads import TORCH_DTYPE, Workload, pad_tables, scale_args
 
 
 class DecodeStep:
@@ -45,9 +45,11 @@ class DecodeStep:
         odt = out_dtype or cfg.out_dtype
         self.out = torch.empty((cfg.B, cfg.Hq, cfg.D), dtype=TORCH_DTYPE[odt], device=dev)
         self.kv_dtype = cfg.kv_dtype
+        self.k_scale, self.v_scale, self.k_scales, self.v_scales = scale_args(wl, dev)
         self.args = binding.decode_args(self.out, wl.q, wl.k_pool, wl.v_pool, self.block_tables,
-                                        self.seq_lens, wl.scale, wl.k_scale, wl.v_scale,
-                                        partition_size, None, cfg.kv_dtype)
+                                        self.seq_lens, wl.scale, self.k_scale, self.v_scale,
+                                        partition_size, None, cfg.kv_dtype, self.k_scales,
+                                        self.v_scales)
         self.workspace = binding.alloc_workspace(self.args, dev)
 
     # individual stages (each one C-ABI call)
@@ -60,8 +62,8 @@ class DecodeStep:
 
     def cache_write(self, stream=None):
         wl = self.wl
-        binding.reshape_and_cache(wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, self.slots, wl.k_scale,
-                                  wl.v_scale, self.kv_dtype, stream)
+        binding.reshape_and_cache(wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, self.slots, self.k_scale,
+                                  self.v_scale, self.kv_dtype, stream, self.k_scales, self.v_scales)
 
     def decode_partition(self, stream=None):
         binding.decode_partition_run(self.args, stream)
@@ -105,9 +107,11 @@ class PrefillStep:
         odt = out_dtype or cfg.out_dtype
         self.out = torch.empty((wl.T, cfg.Hq, cfg.D), dtype=TORCH_DTYPE[odt], device=dev)
         self.kv_dtype = cfg.kv_dtype
+        self.k_scale, self.v_scale, self.k_scales, self.v_scales = scale_args(wl, dev)
         self.args = binding.prefill_args(self.out, wl.q, wl.k_pool, wl.v_pool, self.block_tables,
                                          self.seq_lens, self.q_starts, self.max_q_len, wl.scale,
-                                         wl.k_scale, wl.v_scale, cfg.kv_dtype)
+                                         self.k_scale, self.v_scale, cfg.kv_dtype, self.k_scales,
+                                         self.v_scales)
 
     def slot_mapping(self, stream=None):
         binding.prefill_slot_mapping(self.block_tables, self.seq_lens, self.q_starts,
@@ -115,8 +119,8 @@ class PrefillStep:
 
     def cache_write(self, stream=None):
         wl = self.wl
-        binding.reshape_and_cache(wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, self.slots, wl.k_scale,
-                                  wl.v_scale, self.kv_dtype, stream)
+        binding.reshape_and_cache(wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, self.slots, self.k_scale,
+                                  self.v_scale, self.kv_dtype, stream, self.k_scales, self.v_scales)
 
     def attention(self, stream=None):
         binding.prefill_run(self.args, stream)

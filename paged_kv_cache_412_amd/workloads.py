@@ -24,7 +24,8 @@ Workloads (shapes follow the pages' examples; P1 = Ultralytics glossary page
   fp32 scale per pool (P1 "İlgili Teknikler": GQA and FP8 cache), 32 query /
   8 KV heads, head dim 128, batch 16, lengths uniform in [16384, 32768],
   block size 16 or 32, bf16 queries and new rows.  ``long_e5m2`` is the same
-  with an e5m2 cache (the other 8-bit flavour).
+  with an e5m2 cache (the other 8-bit flavour); ``long_fp8_heads`` uses one
+  scale per KV head, with head magnitudes spread over 2^-4..2^4.
 
 Prefill workloads (several new tokens per sequence, :func:`make_prefill`):
 
@@ -104,6 +105,7 @@ class Config:
     prefill: dict = field(default_factory=dict)  # prefill: inclusive ranges "new", "ctx"
     swap: dict = field(default_factory=dict)     # swap: blocks moved each way
     stream: dict = field(default_factory=dict)   # block-manager request stream parameters
+    head_scales: bool = False   # 8-bit caches: one scale per KV head instead of one per pool
 
     @property
     def G(self) -> int:
@@ -129,6 +131,9 @@ CONFIGS = {
     "long_fp8_bs32": Config("long_fp8_bs32", 6, B=16, Hq=32, Hkv=8, D=128, block_size=32,
                             kv_dtype=E4M3, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
                             len_range=(16384, 32768)),
+    "long_fp8_heads": Config("long_fp8_heads", 13, B=16, Hq=32, Hkv=8, D=128, block_size=16,
+                             kv_dtype=E4M3, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
+                             len_range=(16384, 32768), head_scales=True),
     "long_e5m2": Config("long_e5m2", 12, B=16, Hq=32, Hkv=8, D=128, block_size=16, kv_dtype=E5M2,
                         q_dtype=BF16, out_dtype=BF16, src_dtype=BF16, len_range=(16384, 32768)),
     # prefill: several new tokens per sequence, causal over the paged context
@@ -198,12 +203,24 @@ def _poison_value(dtype: str):
     return 0x7F if dtype in FP8_MAX else float("nan")
 
 
-def _fill_values(shape, dtype: str, gen: torch.Generator, device, sigma: float = 1.0):
+def _fill_values(shape, dtype: str, gen: torch.Generator, device, sigma: float = 1.0,
+                 per_head: bool = False):
     """N(0, sigma^2) draws rounded to ``dtype``; 8-bit formats return (codes,
-    scale) with scale = amax / (the format's largest finite value)."""
+    scale) with scale = amax / (the format's largest finite value).  With
+    ``per_head`` (8-bit pools [NB, bs, Hkv, D]) each KV head's draws are first
+    multiplied by 2^u, u uniform in [-4, 4], and the scale is a float32 array
+    with one amax-based scale per head."""
     x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
     if sigma != 1.0:
         x.mul_(sigma)
+    if dtype in FP8_MAX and per_head:
+        H = shape[2]
+        mag = torch.exp2(torch.rand(H, generator=gen, device=device) * 8.0 - 4.0)
+        x.mul_(mag.view(1, 1, H, 1))
+        amax = x.abs().amax(dim=(0, 1, 3))
+        scale = (amax / FP8_MAX[dtype]).to(torch.float32)
+        codes = (x / scale.view(1, 1, H, 1)).clamp_(-FP8_MAX[dtype], FP8_MAX[dtype])
+        return codes.to(FP8_TORCH[dtype]).view(torch.uint8), scale.cpu().numpy()
     if dtype in FP8_MAX:
         scale = float(x.abs().max()) / FP8_MAX[dtype]
         codes = (x / scale).clamp_(-FP8_MAX[dtype], FP8_MAX[dtype]).to(FP8_TORCH[dtype]).view(torch.uint8)
@@ -283,8 +300,8 @@ def _make_shared(cfg: Config, device, poison: bool, q_sigma: float) -> Workload:
 
 def _values(cfg, device, gen, lens, tables, NB, free, refs, poison, q_sigma) -> Workload:
     bs, Hkv, D = cfg.block_size, cfg.Hkv, cfg.D
-    k_pool, k_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device)
-    v_pool, v_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device)
+    k_pool, k_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device, per_head=cfg.head_scales)
+    v_pool, v_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device, per_head=cfg.head_scales)
     if poison:
         pv = _poison_value(cfg.kv_dtype)
         used = np.zeros(NB, dtype=bool)
@@ -391,8 +408,8 @@ def make_prefill(cfg: Config, device="cpu", poison: bool = True, lengths=None) -
     NB = cfg.pool_blocks or int(np.ceil(need * (1.0 + cfg.slack)))
     free = [int(b) for b in rng.permutation(NB)]
     tables = [[free.pop(0) for _ in range(_ceil_div(int(L), bs))] for L in lens]
-    k_pool, k_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device)
-    v_pool, v_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device)
+    k_pool, k_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device, per_head=cfg.head_scales)
+    v_pool, v_scale = _fill_values((NB, bs, Hkv, D), cfg.kv_dtype, gen, device, per_head=cfg.head_scales)
     if poison:
         pv = _poison_value(cfg.kv_dtype)
         used = np.zeros(NB, dtype=bool)
@@ -496,3 +513,13 @@ def make_stream(cfg: Config) -> list:
                 ops.append(("free", sid))
                 del live[sid]
     return ops
+
+
+def scale_args(wl, device):
+    """(k_scale, v_scale, k_scales, v_scales) for the library: pool-wide
+    floats, or per-head device tensors with the floats left at 1."""
+    if isinstance(wl.k_scale, np.ndarray):
+        ks = torch.from_numpy(np.ascontiguousarray(wl.k_scale, dtype=np.float32)).to(device)
+        vs = torch.from_numpy(np.ascontiguousarray(wl.v_scale, dtype=np.float32)).to(device)
+        return 1.0, 1.0, ks, vs
+    return wl.k_scale, wl.v_scale, None, None

@@ -35,7 +35,17 @@ def storage(t: torch.Tensor) -> np.ndarray:
     raise TypeError(t.dtype)
 
 
-def widen(raw: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+def widen(raw: np.ndarray, dtype: str, scale=1.0) -> np.ndarray:
+    """Raw storage to float64 values; for 8-bit codes ``scale`` is the pool's
+    fp32 scale, or an array of one scale per KV head for ``raw`` shaped
+    [..., Hkv, D]."""
+    if np.ndim(scale) > 0:
+        per = np.asarray(scale, dtype=np.float32).astype(np.float64)[:, None]
+        return widen(raw, dtype, 1.0) * per
+    return _widen(raw, dtype, scale)
+
+
+def _widen(raw: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
     if dtype == "f32":
         return numerics.f32_bits_to_f64(raw)
     if dtype == "f16":
@@ -53,9 +63,14 @@ def encode_rows(rows: np.ndarray, src_dtype: str, kv_dtype: str, scale: float) -
     """The oracle's cache-write encoding of new rows (raw storage in, raw out)."""
     if src_dtype == kv_dtype:
         return rows
-    if kv_dtype == "e5m2":
-        return fp8.quantize_e5m2(widen(rows, src_dtype), scale)
-    return fp8.quantize(widen(rows, src_dtype), scale)
+    quant = fp8.quantize_e5m2 if kv_dtype == "e5m2" else fp8.quantize
+    if np.ndim(scale) > 0:          # one scale per KV head: rows [T, Hkv, D]
+        vals = widen(rows, src_dtype)
+        out = np.empty(rows.shape, dtype=np.uint8)
+        for h in range(rows.shape[1]):
+            out[:, h, :] = quant(vals[:, h, :], float(scale[h]))
+        return out
+    return quant(widen(rows, src_dtype), scale)
 
 
 @dataclass

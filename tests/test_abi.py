@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.pa_abi_version() == 1
+    assert L.pa_abi_version() == 2
     for s in range(7):
         assert L.pa_status_str(s) and L.pa_status_str(s) != b"unknown status"
     assert L.pa_status_str(99) == b"unknown status"
@@ -256,3 +256,25 @@ def test_swap_blocks_rejections(L):
     assert call(dk=F2 + 8) == 2                                     # misaligned
     assert call(dk=FAKE + 4096) == 2                                # dst overlaps src K
     assert call(dv=F2 + 4096) == 2                                  # dst K and V overlap
+
+
+def test_per_head_scales_validation(L):
+    k = ctypes.c_void_p(FAKE)
+    # both or neither; 8-bit caches only
+    assert check(L, q_dtype=binding.PA_BF16, kv_dtype=binding.PA_FP8_E4M3, out_dtype=binding.PA_BF16,
+                 k_scale=1.0, v_scale=1.0, k_scales=FAKE, v_scales=FAKE) == 0
+    assert check(L, q_dtype=binding.PA_BF16, kv_dtype=binding.PA_FP8_E5M2, out_dtype=binding.PA_BF16,
+                 k_scales=FAKE, v_scales=0) == 1
+    assert check(L, k_scales=FAKE, v_scales=FAKE) == 3                   # fp32 cache
+    assert pcheck(L, kv_dtype=binding.PA_FP8_E4M3, k_scales=FAKE, v_scales=FAKE) == 0
+    assert pcheck(L, kv_dtype=binding.PA_FP8_E4M3, k_scales=FAKE) == 1
+    assert pcheck(L, k_scales=FAKE, v_scales=FAKE) == 3                  # bf16 cache
+    f = L.pa_reshape_and_cache_scales
+    # (k_new, v_new, k_cache, v_cache, slots, T, Hkv, D, bs, NB, src, kv, k_scales, v_scales, stream)
+    args = [FAKE] * 5 + [4, 8, 128, 16, 64, binding.PA_BF16, binding.PA_FP8_E4M3, FAKE, FAKE, None]
+    assert f(*args[:12], None, FAKE, None) == 1
+    assert f(*args[:10], binding.PA_BF16, binding.PA_BF16, FAKE, FAKE, None) == 3   # not quantising
+    assert f(*args[:10], binding.PA_FP8_E4M3, binding.PA_FP8_E4M3, FAKE, FAKE, None) == 3
+    assert f(*args[:5], 0, *args[6:]) == 0                                         # T = 0
+    assert f(*args[:5], -1, *args[6:]) == 2
+    del k

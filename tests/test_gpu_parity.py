@@ -30,6 +30,10 @@ SMALL = {
                       shared=dict(prompts=3, samples=3, prefix=1024, stem=(64, 512))),
     "long_fp8": replace(C["long_fp8"], B=2, Hq=8, Hkv=2),
     "long_fp8_bs32": replace(C["long_fp8_bs32"], B=2, Hq=8, Hkv=2),
+    "long_fp8_heads": replace(C["long_fp8_heads"], B=2, Hq=8, Hkv=2),
+    "long_e5m2": replace(C["long_e5m2"], B=2, Hq=8, Hkv=2),
+    "long_e5m2_heads": replace(C["long_e5m2"], name="long_e5m2_heads", B=3, Hq=6, Hkv=3,
+                               head_scales=True, len_range=(100, 3000)),
 }
 
 
@@ -65,7 +69,8 @@ def test_step_small_all_outputs(name):
     print(f"[ok] {name} max abs err {err:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["llama13b", "llama70b", "shared", "long_fp8", "long_fp8_bs32"])
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "shared", "long_fp8", "long_fp8_bs32",
+                                  "long_fp8_heads", "long_e5m2"])
 def test_step_full_size_sampled(name):
     cfg = C[name]
     rng = np.random.default_rng(7)
@@ -391,3 +396,33 @@ def test_errors_surface_as_exceptions():
     with pytest.raises(binding.PaError) as e:
         binding.decode(out, q, k, k, tables, lens, 0.1)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_per_head_scale_cache_write_bit_exact(fmt, src):
+    """pa_reshape_and_cache_scales: head g of every row quantised with its own
+    scale, fl32(1 / scale) on the device equal to the oracle's."""
+    print(f"\n[case] per-head {fmt} cache write src={src}", flush=True)
+    rng = np.random.default_rng(12)
+    Hkv, D, bs, T = 8, 128, 16, 4096
+    scales = (np.exp2(rng.uniform(-12, 6, Hkv)) * rng.uniform(1, 2, Hkv)).astype(np.float32)
+    x = fp8_sweep_values(rng, fmt)[: T * Hkv * D]
+    x = np.resize(x, T * Hkv * D).reshape(T, Hkv, D) * scales[None, :, None]
+    xt = torch.from_numpy(x.astype(np.float32))
+    if src == "bf16":
+        xt = xt.to(torch.bfloat16)
+    NB = T // bs
+    k_cache = torch.zeros((NB, bs, Hkv, D), dtype=torch.uint8, device="cuda")
+    v_cache = torch.zeros_like(k_cache)
+    slots = torch.arange(T, dtype=torch.int32, device="cuda")
+    ks = torch.from_numpy(scales).cuda()
+    vs = torch.from_numpy(scales[::-1].copy()).cuda()
+    binding.reshape_and_cache(xt.cuda(), xt.cuda(), k_cache, v_cache, slots, kv_dtype=fmt,
+                              k_scales=ks, v_scales=vs)
+    torch.cuda.synchronize()
+    raw = parity.storage(xt)
+    exp_k = parity.encode_rows(raw, src, fmt, scales)
+    exp_v = parity.encode_rows(raw, src, fmt, scales[::-1].copy())
+    assert np.array_equal(k_cache.cpu().numpy().reshape(T, Hkv, D), exp_k)
+    assert np.array_equal(v_cache.cpu().numpy().reshape(T, Hkv, D), exp_v)

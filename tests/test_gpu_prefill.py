@@ -31,6 +31,11 @@ SMALL = {
     "prefill13b": cfg_of("prefill13b", B=3, Hq=4, Hkv=4, prefill=dict(new=(100, 300), ctx=(0, 0))),
     "prefill70b": cfg_of("prefill70b", B=3, Hq=16, Hkv=2, prefill=dict(new=(40, 200), ctx=(0, 400))),
     "prefill_fp8": cfg_of("prefill_fp8", B=3, Hq=8, Hkv=2, prefill=dict(new=(50, 200), ctx=(0, 500))),
+    "prefill_fp8_heads": cfg_of("prefill_fp8", name="prefill_fp8_heads", B=3, Hq=12, Hkv=4,
+                                head_scales=True, prefill=dict(new=(50, 200), ctx=(0, 500))),
+    "prefill_e5m2_heads": cfg_of("prefill_fp8", name="prefill_e5m2_heads", B=3, Hq=6, Hkv=3,
+                                 kv_dtype="e5m2", head_scales=True,
+                                 prefill=dict(new=(50, 200), ctx=(0, 500))),
 }
 
 
