@@ -34,7 +34,9 @@
 //     lanes of a group read each row whole.  Lane l then holds output
 //     columns d = (D/16)*(4*grp + r) + mm of query row lo: D/4 contiguous
 //     values, stored with 16-byte writes.
-// Softmax runs in log2 units on the score layout.  The weights enter the
+// Softmax runs in log2 units on the score layout, with no cross-lane
+// traffic in the common case (each lane checks its own scores against the
+// shared running max).  The weights enter the
 // weighted sum rounded to the 16-bit operand type, and the running sum adds
 // up exactly those rounded weights (one more MFMA per tile, against a row of
 // ones), so the output is a weighted mean of V rows (a dominant key returns
@@ -286,9 +288,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
             for (int r = 0; r < 4; ++r)
               if (k0 + 16 * ks + 4 * grp + r > pos[nt]) s[ks][nt][r] = ninf;
       }
-      // tile max per query (unscaled, then scaled: c > 0).  IEEE maximum
-      // (v_maximum3_f32): the scores hold no signalling NaNs to quiet
-      float mx[NT];
+      // This lane's max over its own scores of each query (unscaled; IEEE
+      // maximum, v_maximum3_f32: the scores hold no signalling NaNs).  Only
+      // when some lane exceeds the running max by more than the allowed lag
+      // does the wave reduce across its lanes and rescale: the common path
+      // needs no cross-lane traffic, and every weight stays below 2^kSlack.
+      float lmx[NT];
       bool up = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -297,15 +302,17 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
           for (int r = (ks == 0 ? 1 : 0); r < 4; ++r) x = vmax(x, s[ks][nt][r]);
-        x = vmax(x, u2f(__builtin_amdgcn_ds_bpermute(xor16, f2u(x))));
-        x = vmax(x, u2f(__builtin_amdgcn_ds_bpermute(xor32, f2u(x))));
-        mx[nt] = x * c;
-        up = up || mx[nt] > m[nt] + kSlack;
+        lmx[nt] = x;
+        up = up || x * c > m[nt] + kSlack;
       }
       if (__ballot(up)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const float mn = fmaxf(m[nt], mx[nt]);
+          // the query's max over all four lane groups, in log2 units (c > 0)
+          float x = lmx[nt];
+          x = vmax(x, u2f(__builtin_amdgcn_ds_bpermute(xor16, f2u(x))));
+          x = vmax(x, u2f(__builtin_amdgcn_ds_bpermute(xor32, f2u(x))));
+          const float mn = fmaxf(m[nt], x * c);
           const float alpha = fast_exp2(m[nt] - mn);
           m[nt] = mn;
           l[nt] *= alpha;  // all four copies
