@@ -114,7 +114,7 @@ struct PrefillParams {
 };
 
 constexpr int kPrefillRows = 128;  // (token, head) rows per work-group: 4 waves x 32
-constexpr int kPrefillKeys = 32;   // keys per LDS tile of the prefill kernel
+constexpr int kPrefillKeys = 64;   // keys per LDS tile of the prefill kernel
 
 bool prefill_serves(pa_dtype q_dtype, pa_dtype kv_dtype, int32_t D, int32_t block_size,
                     int32_t group);

@@ -15,11 +15,12 @@
 // Work split.  A work-group of four waves owns up to 128 rows of (new token,
 // query head) pairs of one KV head: floor(128 / G) consecutive new tokens of
 // one sequence with all G heads of the group (G from 1 to 16), so every K/V
-// tile it loads serves all of them.  Wave w owns rows [32w, 32w + 32) as two 16-column MFMA tiles.  The
-// keys run in tiles of 32 (two 16-token blocks, or one 32-token block): the
-// work-group copies each tile's K and V rows from the pool into LDS (double
-// buffered, the next tile's global loads in flight during the current
-// tile's matrix work), and every wave reads its MFMA operands from there.
+// tile it loads serves all of them.  Wave w owns rows [32w, 32w + 32) as
+// two 16-column MFMA tiles.  The keys run in tiles of 64 (four 16-token
+// blocks or two 32-token ones): the work-group copies each tile's K and V
+// rows from the pool into LDS (double buffered, the next tile's loads in
+// flight during the current tile's matrix work), and every wave reads its
+// MFMA operands from there.
 //
 // Contractions (lane l, lo = l % 16, grp = l / 16; layouts in pa_mfma.h):
 //   S^T = K Q^T, one 16x16x32 MFMA per 32 head-dim values: A = 16 key rows
@@ -172,9 +173,19 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   // resource of 0 bytes and rows past the last key an offset past the end,
   // and both read as zeros.  Every path thus issues the same loads, and the
   // compiler's wait counts stay exact (loads retire in order).
+  //
+  // 16-bit K/V go from the pool straight into LDS (buffer loads with the LDS
+  // bit): one such load fills 1 KiB from a wave-uniform base, lane i at byte
+  // 16 i, which is WROWS whole rows, so the lane at physical chunk pc of row
+  // r fetches the logical chunk pc ^ swizzle(r) that belongs there.  The
+  // next tile's fills run during the current tile's matrix work, into the
+  // buffer no wave reads in this iteration; each wave waits for its own
+  // fills before the barrier that ends the iteration.  8-bit K/V are loaded
+  // into registers and widened to the 16-bit operand type on their way to LDS.
   constexpr int TB = kKeys / BS > 0 ? kKeys / BS : 1;  // blocks per key tile
   constexpr int WROWS = 64 / CPR;                       // rows one wave stages per pass
   static_assert(WROWS <= BS && BS % WROWS == 0, "a wave's rows in one block");
+  static_assert(KVB != 2 || WROWS * ROWB == 1024, "one LDS fill per wave and pass");
   const int64_t row_stride = static_cast<int64_t>(p.Hkv) * D * KVB;
   const uint32_t blk_bytes = static_cast<uint32_t>(row_stride * BS);
   const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
@@ -183,14 +194,14 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int srow = threadIdx.x / CPR, schunk = threadIdx.x % CPR;
   const bool wave_stages = wv * WROWS < RPP;  // uniform: whole waves stage or not
-  const int col = kvh * D * KVB + schunk * 16;
-  u32x4 kst[PASSES], vst[PASSES];
+  u32x4 kst[KVB == 2 ? 1 : PASSES], vst[KVB == 2 ? 1 : PASSES];  // 8-bit codes in flight
   // ids of the blocks of a tile, lane t < TB holding its t-th block
   auto load_ids = [&](int j) {
     return static_cast<int>(
         __builtin_amdgcn_raw_buffer_load_b32(trs, (j * TB + (lid % TB)) * 4, 0, 0));
   };
-  auto fetch = [&](int j, int ids) {
+  // issue tile j's loads (into LDS buffer buf for 16-bit K/V)
+  auto fetch = [&](int j, int ids, int buf) {
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int row0 = ps * RPP + wv * WROWS;          // first row this wave stages
@@ -201,23 +212,37 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
       const char* vb = static_cast<const char*>(p.v_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
       const __amdgpu_buffer_rsrc_t kr = block_rsrc(kb, ok ? blk_bytes : 0u);
       const __amdgpu_buffer_rsrc_t vr = block_rsrc(vb, ok ? blk_bytes : 0u);
-      const int key = j * kKeys + ps * RPP + srow;
-      const int voff = key < n_keys ? static_cast<int>((key % BS) * row_stride) + col : 0x7fffff00;
-      kst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, voff, 0, 0));
-      vst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 0, 0));
+      const int r = ps * RPP + srow;                   // this lane's row of the tile
+      const int key = j * kKeys + r;
+      const int row_off = static_cast<int>((key % BS) * row_stride) + kvh * D * KVB;
+      if constexpr (KVB == 2) {
+        const int sw = CH == 16 ? (r & 15) : ((r >> 1) & 7);
+        const int voff = key < n_keys ? row_off + ((schunk ^ sw) << 4) : 0x7fffff00;
+        if (wave_stages) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              kr, (__attribute__((address_space(3))) void*)(lds[buf][0] + row0 * ROWB), 16, voff, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              vr, (__attribute__((address_space(3))) void*)(lds[buf][1] + row0 * ROWB), 16, voff, 0, 0, 0);
+        }
+      } else {
+        const int voff = key < n_keys ? row_off + schunk * 16 : 0x7fffff00;
+        kst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, voff, 0, 0));
+        vst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 0, 0));
+      }
     }
   };
+  // complete the fetched tile in LDS buffer buf (before the barrier)
   auto stage = [&](int buf) {
-    if (!wave_stages) return;
+    if constexpr (KVB == 2) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's LDS fills have landed
+    } else {
+      if (!wave_stages) return;
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int r = ps * RPP + srow;
-      uint8_t* kd = lds[buf][0];
-      uint8_t* vd = lds[buf][1];
-      if constexpr (KVB == 2) {
-        *reinterpret_cast<u32x4*>(kd + lds_off(r, schunk)) = kst[ps];
-        *reinterpret_cast<u32x4*>(vd + lds_off(r, schunk)) = vst[ps];
-      } else {  // 16 8-bit codes -> 16 operand values (exact), two chunks
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int r = ps * RPP + srow;
+        uint8_t* kd = lds[buf][0];
+        uint8_t* vd = lds[buf][1];
+        // 16 8-bit codes -> 16 operand values (exact), two chunks
         uint32_t w[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -251,7 +276,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   const int xor16 = (lid ^ 16) << 2, xor32 = (lid ^ 32) << 2;
 
   int ids_next = load_ids(1);  // tile 1's blocks (consumed one iteration later)
-  fetch(0, load_ids(0));
+  fetch(0, load_ids(0), 0);
   stage(0);
   __syncthreads();
 
@@ -261,7 +286,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
     // iteration (past the last tile they read zeros into a buffer no one reads)
     const int ids = ids_next;
     ids_next = load_ids(j + 2);
-    fetch(j + 1, ids);
+    fetch(j + 1, ids, (j + 1) & 1);
     if (wave_active && k0 <= pmax) {
       const uint8_t* Kt = lds[j & 1][0];
       const uint8_t* Vt = lds[j & 1][1];
