@@ -129,14 +129,23 @@ __device__ __forceinline__ void for_each_segment(const DecodeParams& p, int hg, 
 // included).  `consume(j0, ok, buf)` folds logical blocks j0..j0+UB-1 into the
 // running state; bit u of ok is clear for a block that counts no valid token
 // (an id outside the pool, or past the partition's end).
+// Logical block j is sub-block j % 2^sub of table entry j / 2^sub; its id
+// is entry * 2^sub + j % 2^sub (blocks of the pool seen as 2^sub smaller ones).
 template <int ST, int UB, typename Buf, typename Load, typename Consume>
 __device__ __forceinline__ void walk_blocks(const int32_t* table, const PartitionSpan& s,
-                                            int num_blocks, int lane, Load&& load,
+                                            int num_blocks, int sub, int lane, Load&& load,
                                             Consume&& consume) {
   for (int base = s.jbeg; base < s.jend; base += 64) {
     const int cnt = min(64, s.jend - base);
-    int ids = lane < cnt ? table[base + lane] : -1;
-    if (static_cast<unsigned>(ids) >= static_cast<unsigned>(num_blocks)) ids = -1;
+    int ids = -1;
+    if (lane < cnt) {
+      const int j = base + lane;
+      const int e = table[j >> sub];
+      // entries outside the pool (num_blocks >> sub table blocks) count none
+      ids = static_cast<unsigned>(e) < static_cast<unsigned>(num_blocks >> sub)
+                ? (e << sub) | (j & ((1 << sub) - 1))
+                : -1;
+    }
     const int units = (cnt + UB - 1) / UB;
     // ids of unit k (k uniform; 64 is a multiple of UB, so a unit never
     // straddles two 64-block chunks)

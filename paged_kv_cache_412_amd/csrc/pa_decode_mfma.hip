@@ -57,9 +57,13 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   constexpr int KVB = FP8 ? 1 : 2;
   constexpr int SS = D / 32;                    // score MFMAs per tile (32 head-dim values each)
   constexpr int EPL = D / 16;                   // V elements per lane per row = PV MFMAs per tile
-  constexpr int TPB = BS / 16;                  // 16-token tiles per block
-  constexpr int UB = BS == 16 ? 2 : 1;          // blocks per pipeline unit (32 tokens)
-  constexpr int TT = UB * TPB;                  // 16-token tiles per unit
+  // 8-token blocks: a 16-token tile spans two blocks, so each lane reads
+  // through its own address (its K row's block, its V rows' block) instead
+  // of one buffer resource per block
+  constexpr bool SPLIT = BS < 16;
+  constexpr int TPB = SPLIT ? 1 : BS / 16;      // 16-token tiles per block (or per 16/BS blocks)
+  constexpr int UB = 32 / BS;                   // blocks per pipeline unit (32 tokens)
+  constexpr int TT = 2;                         // 16-token tiles per unit
   constexpr int KW = D / 8;                     // dwords of 16-bit K per lane per tile
   constexpr int KR = FP8 ? D / 16 : D / 8;      // dwords of stored K per lane per tile
   constexpr int VW = EPL / 2;                   // dwords of 16-bit V per lane per row
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   constexpr int KLD = KR >= 4 ? 4 : KR;         // dwords per K load instruction
   const int G = p.Hq / p.Hkv;  // 3..16: the query group padded to the MFMA's 16 rows
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(BS % 16 == 0, "block size");
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -93,6 +97,10 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   const int v_off = head_off + 4 * grp * row_stride + EPL * lo * KVB;
   const char* kpool = static_cast<const char*>(p.k_cache);
   const char* vpool = static_cast<const char*>(p.v_cache);
+  // 8-token blocks: K row lo of a tile is row lo % 8 of the tile's block
+  // lo / 8; V rows 4*grp + e are rows 4*(grp % 2) + e of block grp / 2
+  const int k_off8 = head_off + (lo & 7) * row_stride + (FP8 ? grp * (D / 4) : grp * 16);
+  const int v_off8 = head_off + 4 * (grp & 1) * row_stride + EPL * lo * KVB;
   // score scale in log2 units and V scale of this wave's KV head
   const float qk = p.k_scales ? p.qk_scale_log2 * p.k_scales[g] : p.qk_scale_log2;
   const float vs = p.v_scales ? p.v_scales[g] : p.v_scale;
@@ -102,8 +110,32 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
     uint32_t v[TT][4][VR];
   };
 
-  // Loads of the unit's blocks (nothing is read for an id < 0).
+  // Loads of the unit's blocks (nothing is read for an id < 0; with 8-token
+  // blocks block 0 is read instead, and consume() excludes those rows).
   auto load = [&](const int (&id)[UB], Raw& r) {
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int kb = lo < 8 ? id[2 * tt] : id[2 * tt + 1];
+        const int vb = grp < 2 ? id[2 * tt] : id[2 * tt + 1];
+        const char* kp = kpool + static_cast<size_t>(kb < 0 ? 0 : kb) * blk_bytes + k_off8;
+        const char* vp = vpool + static_cast<size_t>(vb < 0 ? 0 : vb) * blk_bytes + v_off8;
+        if constexpr (FP8) {
+          global_load<KLD, 0>(kp, &r.k[tt][0]);
+          if constexpr (KR > KLD) global_load<KLD, 16>(kp, &r.k[tt][KLD]);
+        } else {
+          global_load<4, 0>(kp, &r.k[tt][0]);
+          global_load<4, 64>(kp, &r.k[tt][4]);
+          if constexpr (SS > 2) {
+            global_load<4, 128>(kp, &r.k[tt][8]);
+            global_load<4, 192>(kp, &r.k[tt][12]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) global_load<VR, 0>(vp + e * row_stride, r.v[tt][e]);
+      }
+      return;
+    }
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
       const int blk = id[ub];
@@ -166,13 +198,26 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
     float l_part = 0.f;      // this lane's share of the running sum of query lo
 
     auto consume = [&](int j0, unsigned ok, Raw& r) {
-      // valid rows of each 16-token tile; a block that is not ok counts none
-      int valid[TT];
+      // valid rows of each 16-token tile (a mask, bit r for row r); a block
+      // that is not ok counts none
+      uint32_t vmask[TT];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const int ub = tt / TPB;
-        const int first = (j0 + ub) * BS + (tt % TPB) * 16;
-        valid[tt] = (ok >> ub) & 1u ? min(16, max(0, span.L - first)) : 0;
+        if constexpr (SPLIT) {
+          uint32_t mk = 0;
+#pragma unroll
+          for (int h = 0; h < 16 / BS; ++h) {
+            const int ub = tt * (16 / BS) + h;
+            const int n = (ok >> ub) & 1u ? min(BS, max(0, span.L - (j0 + ub) * BS)) : 0;
+            mk |= ((1u << n) - 1u) << (h * BS);
+          }
+          vmask[tt] = mk;
+        } else {
+          const int ub = tt / TPB;
+          const int first = (j0 + ub) * BS + (tt % TPB) * 16;
+          const int n = (ok >> ub) & 1u ? min(16, max(0, span.L - first)) : 0;
+          vmask[tt] = (1u << n) - 1u;
+        }
       }
       float sc[TT][4];
 #pragma unroll
@@ -191,7 +236,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // rows past the end may hold anything (NaN included): excluded outright
-          sc[tt][i] = 4 * grp + i < valid[tt] ? S[i] * qk : -__builtin_inff();
+          sc[tt][i] = (vmask[tt] >> (4 * grp + i)) & 1u ? S[i] * qk : -__builtin_inff();
         }
       }
       float bm = sc[0][0];
@@ -226,11 +271,11 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
         }
         const uint32_t pa0 = M::pack2(pw[0], pw[1]);
         const uint32_t pa1 = M::pack2(pw[2], pw[3]);
-        if (valid[tt] < 16) {
+        if (vmask[tt] != 0xffffu) {
           // zero the V rows past the end so that 0 * NaN cannot reach the sum
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (4 * grp + e >= valid[tt]) {
+            if (!((vmask[tt] >> (4 * grp + e)) & 1u)) {
 #pragma unroll
               for (int i = 0; i < VR; ++i) r.v[tt][e][i] = 0u;
             }
@@ -256,8 +301,9 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
       }
     };
 
-    const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
-    walk_blocks<ST, UB, Raw>(table, span, p.num_blocks, lane, load, consume);
+    const int32_t* table =
+        p.block_tables + static_cast<size_t>(b) * (p.max_blocks_per_seq >> p.sub_shift);
+    walk_blocks<ST, UB, Raw>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
 
     // l of query lo summed over the four lane groups; every lane then fetches
     // m and l of the queries whose accumulators it holds (4*grp + i)
@@ -303,6 +349,7 @@ struct Tag {
 template <int KV, int Q, int D, typename F>
 bool by_block(const DecodeParams& p, F&& f) {
   switch (p.block_size) {
+    case 8: f(Tag<KV, Q, D, 8>{}); return true;
     case 16: f(Tag<KV, Q, D, 16>{}); return true;
     case 32: f(Tag<KV, Q, D, 32>{}); return true;
     default: return false;

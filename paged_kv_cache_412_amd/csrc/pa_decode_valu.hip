@@ -285,8 +285,9 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
       }
     };
 
-    const int32_t* table = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
-    walk_blocks<ST, 1, Buf>(table, span, p.num_blocks, lane, load, consume);
+    const int32_t* table =
+        p.block_tables + static_cast<size_t>(b) * (p.max_blocks_per_seq >> p.sub_shift);
+    walk_blocks<ST, 1, Buf>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
 
     // merge the per-lane states of the TPL row groups that own the same
     // chunk; the butterfly leaves the merged state in every lane
@@ -363,6 +364,11 @@ bool by_group(const DecodeParams& p, F&& f) {
 template <int KV, int Q, int D, typename F>
 bool by_block(const DecodeParams& p, F&& f) {
   switch (p.block_size) {
+    case 8:
+      // a wave load of TPL rows must lie in one block: not so for 8-bit
+      // caches at D = 64 (16 rows per load)
+      if constexpr (8 % (64 * Ops<KV, Q>::CE / D) == 0) return by_group<KV, Q, D, 8>(p, f);
+      return false;
     case 16: return by_group<KV, Q, D, 16>(p, f);
     case 32: return by_group<KV, Q, D, 32>(p, f);
     default: return false;

@@ -78,6 +78,25 @@ __device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, int voff, 
   }
 }
 
+// N dwords (1, 2 or 4) at byte IMM of a per-lane address (non-temporal, as
+// the buffer loads).  For reads whose rows lie in different blocks per lane.
+template <int N, int IMM = 0>
+__device__ __forceinline__ void global_load(const char* p, uint32_t* out) {
+  if constexpr (N == 4) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + IMM));
+    out[0] = v[0];
+    out[1] = v[1];
+    out[2] = v[2];
+    out[3] = v[3];
+  } else if constexpr (N == 2) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p + IMM));
+    out[0] = v[0];
+    out[1] = v[1];
+  } else {
+    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p + IMM));
+  }
+}
+
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 

@@ -34,7 +34,12 @@ struct DecodeParams {
   float* ws_m;    // partial rows: running max (log2 units)
   float* ws_l;    // partial rows: running sum
   int32_t* prefix;  // balanced: [B+1] block-count prefix sums
+  // block_size, num_blocks and max_blocks_per_seq count the blocks the
+  // kernels walk: 2^sub_shift of them make one block of the table (a block
+  // is contiguous, so its halves are blocks of half the size); table rows
+  // hold max_blocks_per_seq >> sub_shift entries
   int32_t B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq;
+  int32_t sub_shift;
   int32_t partition_size;  // fixed: tokens per partition
   int32_t num_partitions;  // fixed: partitions of the longest possible sequence
   int32_t balanced;        // 1 = balanced schedule

@@ -431,8 +431,17 @@ template <int KV, int Q, int D, typename F>
 bool by_block(int32_t bs, int32_t G, F&& f) {
   if (G < 1 || G > 16) return false;
   switch (bs) {
+    case 8:
+      // the rows one wave stages per pass must lie in one block: 64 / (16-byte
+      // chunks per row) rows, 16 for 8-bit caches at D = 64
+      if constexpr (D * Elem<KV>::bytes >= 128) {
+        f(Tag<KV, Q, D, 8>{});
+        return true;
+      }
+      return false;
     case 16: f(Tag<KV, Q, D, 16>{}); return true;
     case 32: f(Tag<KV, Q, D, 32>{}); return true;
+    case 64: f(Tag<KV, Q, D, 64>{}); return true;
     default: return false;
   }
 }

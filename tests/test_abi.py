@@ -86,7 +86,8 @@ def test_decode_check_accepts_valid(L):
     (dict(max_blocks_per_seq=0), 2), (dict(partition_size=24), 2),
     (dict(q=FAKE + 4), 2), (dict(k_scale=2.0), 2), (dict(scale=float("inf")), 2),
     (dict(B=70000), 2),
-    (dict(D=96), 3), (dict(block_size=8), 3), (dict(Hq=24, Hkv=8), 3), (dict(Hq=32, Hkv=2), 3),
+    (dict(D=96), 3), (dict(block_size=12), 3), (dict(block_size=128), 3), (dict(Hq=24, Hkv=8), 3),
+    (dict(Hq=32, Hkv=2), 3),
     (dict(q_dtype=binding.PA_F16), 3), (dict(out_dtype=binding.PA_BF16), 3),
     (dict(kv_dtype=binding.PA_FP8_E4M3, q_dtype=binding.PA_F32), 3), (dict(q_dtype=7), 3),
     (dict(workspace=0), 4), (dict(workspace_bytes=64), 4),   # the balanced schedule needs one
@@ -98,6 +99,29 @@ def test_decode_check_accepts_valid(L):
 ])
 def test_decode_check_rejects(L, kw, status):
     assert check(L, **kw) == status
+
+
+def test_decode_check_block_sizes(L):
+    P = binding
+    for bs in (8, 16, 32, 64):
+        for D in (64, 128):
+            assert check(L, block_size=bs, D=D) == 0, (bs, D)                      # fp32, vector ALU
+            for G in (1, 2, 8):
+                for kv in (P.PA_F16, P.PA_FP8_E4M3):
+                    sc = 1.0 if kv == P.PA_F16 else 0.5
+                    st = check(L, block_size=bs, D=D, Hq=2 * G, Hkv=2, q_dtype=P.PA_F16, kv_dtype=kv,
+                               out_dtype=P.PA_F16, k_scale=sc, v_scale=sc)
+                    # the one gap: 8-bit caches at D = 64 in 8-token blocks on the vector ALU
+                    want = 3 if (bs == 8 and D == 64 and kv == P.PA_FP8_E4M3 and G <= 2) else 0
+                    assert st == want, (bs, D, G, kv)
+    # partitions are whole blocks
+    assert check(L, block_size=64, partition_size=64, max_blocks_per_seq=16) == 0
+    assert check(L, block_size=64, partition_size=32) == 2
+    # 64-token blocks are walked as 32-token halves: twice the ids must fit int32
+    assert check(L, block_size=64, num_blocks=1 << 30, max_blocks_per_seq=1) == 2
+    assert check(L, block_size=64, num_blocks=(1 << 30) - 1, max_blocks_per_seq=1) == 0
+    assert check(L, block_size=64, B=40000, max_blocks_per_seq=30000) == 2
+    assert check(L, block_size=32, B=40000, max_blocks_per_seq=30000) == 0
 
 
 def test_workspace_size_formula_fixed_partitions(L):
@@ -191,10 +215,13 @@ def test_prefill_check_accepts_supported_combinations(L):
                   (P.PA_F16, P.PA_FP8_E4M3), (P.PA_BF16, P.PA_FP8_E5M2), (P.PA_F16, P.PA_FP8_E5M2)):
         for out in (q, P.PA_F32):
             for D in (64, 128):
-                for bs in (16, 32):
+                for bs in (8, 16, 32, 64):
+                    # rows a wave stages must lie in one block: not so for
+                    # 8-bit caches at D = 64 in 8-token blocks
+                    want = 3 if (bs == 8 and D == 64 and kv in (P.PA_FP8_E4M3, P.PA_FP8_E5M2)) else 0
                     for Hq in (2, 4, 8, 16):
                         assert pcheck(L, q_dtype=q, kv_dtype=kv, out_dtype=out, D=D, block_size=bs,
-                                      Hq=Hq) == 0, (q, kv, out, D, bs, Hq)
+                                      Hq=Hq) == want, (q, kv, out, D, bs, Hq)
 
 
 def test_prefill_check_rejections(L):
@@ -207,7 +234,7 @@ def test_prefill_check_rejections(L):
     assert pcheck(L, Hq=3) == 2                                             # Hq % Hkv
     assert pcheck(L, Hq=6) == 0 and pcheck(L, Hq=14) == 0 and pcheck(L, Hq=32) == 0   # G = 3, 7, 16
     assert pcheck(L, Hq=34) == 3                                            # G = 17 not built
-    assert pcheck(L, D=96) == 3 and pcheck(L, block_size=8) == 3
+    assert pcheck(L, D=96) == 3 and pcheck(L, block_size=12) == 3 and pcheck(L, block_size=128) == 3
     assert pcheck(L, q_dtype=P.PA_F32, kv_dtype=P.PA_F32, out_dtype=P.PA_F32) == 3
     assert pcheck(L, q_dtype=P.PA_F16, kv_dtype=P.PA_BF16) == 3
     assert pcheck(L, out_dtype=P.PA_F16) == 3

@@ -35,6 +35,13 @@ SMALL = {
     "long_e5m2_heads": replace(C["long_e5m2"], name="long_e5m2_heads", B=3, Hq=6, Hkv=3,
                                head_scales=True, len_range=(100, 3000)),
 }
+# the other block sizes (P1 "Sayfalama Nasıl Çalışır": the block size is a
+# parameter): 8 reads a 16-token tile from two blocks, 64 is walked as two
+# 32-token halves
+for _base in ("tiny", "llama13b", "llama70b", "long_fp8"):
+    for _bs in (8, 64):
+        SMALL[f"{_base}_bs{_bs}"] = replace(SMALL[_base], name=f"{_base}_bs{_bs}", block_size=_bs)
+OTHER_BS = [f"{b}_bs{x}" for b in ("tiny", "llama13b", "llama70b", "long_fp8") for x in (8, 64)]
 
 
 def run_step(cfg, seqs=None, partition_size=0, out_dtype=None, q_sigma=1.0):
@@ -80,7 +87,8 @@ def test_step_full_size_sampled(name):
     print(f"[ok] {name} full size, seqs {seqs}, max abs err {err:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["llama13b", "llama70b", "long_fp8"])
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "long_fp8", "llama13b_bs8", "llama70b_bs64",
+                                  "long_fp8_bs8", "long_fp8_bs64"])
 @pytest.mark.parametrize("part", [16, 64, 2048])
 def test_partition_sizes(name, part):
     cfg = SMALL[name]
@@ -90,7 +98,7 @@ def test_partition_sizes(name, part):
     check_step(wl, step, exp)
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama13b", "llama70b", "long_fp8"])
+@pytest.mark.parametrize("name", ["tiny", "llama13b", "llama70b", "long_fp8"] + OTHER_BS)
 def test_edge_lengths(name):
     base = SMALL[name]
     bs = base.block_size
@@ -102,7 +110,8 @@ def test_edge_lengths(name):
     assert np.array_equal(out[0], np.zeros_like(out[0])), "L = 0 must give zeros"
 
 
-@pytest.mark.parametrize("name", ["llama13b", "llama70b", "long_fp8", "long_fp8_bs32"])
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "long_fp8", "long_fp8_bs32", "llama13b_bs8",
+                                  "llama70b_bs8", "llama13b_bs64", "long_fp8_bs64"])
 @pytest.mark.parametrize("shape", ["one_long", "many_short"])
 def test_balanced_schedule_extremes(name, shape):
     """The default (balanced) schedule: one long sequence split over every
@@ -213,11 +222,13 @@ DTYPE_PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("pair", DTYPE_PAIRS, ids=["-".join(p) for p in DTYPE_PAIRS])
 def test_every_supported_shape(pair, D, bs, G):
     qd, kvd = pair
+    if bs == 8 and D == 64 and kvd in ("e4m3", "e5m2") and G <= 2:
+        pytest.skip("not built: the vector-ALU kernel's 16-row loads do not fit 8-token blocks")
     cfg = workloads.Config(f"shape-{qd}-{kvd}-{D}-{bs}-{G}", 7, B=4, Hq=2 * G, Hkv=2, D=D,
                            block_size=bs, kv_dtype=kvd, q_dtype=qd, out_dtype=qd, src_dtype=qd,
                            lens=(1, bs + 3, 700, 1100))
@@ -236,7 +247,7 @@ def test_other_group_sizes(pair, G):
     matrix-core tile (P1 "İlgili Teknikler": grouped-query attention), under
     both schedules."""
     qd, kvd = pair
-    for bs, part in ((16, 0), (32, 256)):
+    for bs, part in ((16, 0), (32, 256), (8, 0), (64, 128)):
         cfg = workloads.Config(f"group-{qd}-{kvd}-{G}-{bs}", 7, B=4, Hq=3 * G, Hkv=3, D=128,
                                block_size=bs, kv_dtype=kvd, q_dtype=qd, out_dtype=qd, src_dtype=qd,
                                lens=(1, bs + 3, 700, 1100))

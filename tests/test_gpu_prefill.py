@@ -36,6 +36,12 @@ SMALL = {
     "prefill_e5m2_heads": cfg_of("prefill_fp8", name="prefill_e5m2_heads", B=3, Hq=6, Hkv=3,
                                  kv_dtype="e5m2", head_scales=True,
                                  prefill=dict(new=(50, 200), ctx=(0, 500))),
+    "prefill70b_bs8": cfg_of("prefill70b", name="prefill70b_bs8", B=3, Hq=16, Hkv=2, block_size=8,
+                             prefill=dict(new=(40, 200), ctx=(0, 400))),
+    "prefill70b_bs64": cfg_of("prefill70b", name="prefill70b_bs64", B=3, Hq=16, Hkv=2, block_size=64,
+                              prefill=dict(new=(40, 200), ctx=(0, 400))),
+    "prefill_fp8_bs64": cfg_of("prefill_fp8", name="prefill_fp8_bs64", B=3, Hq=8, Hkv=2, block_size=64,
+                               prefill=dict(new=(50, 200), ctx=(0, 500))),
 }
 
 
@@ -81,10 +87,12 @@ def test_prefill_small_all_rows(name):
 @pytest.mark.parametrize("pair", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3"),
                                   ("bf16", "e5m2"), ("f16", "e5m2")])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 16])
 def test_prefill_every_supported_shape(pair, D, bs, G):
     q, kv = pair
+    if bs == 8 and D == 64 and kv in ("e4m3", "e5m2"):
+        pytest.skip("not built: a wave stages 16 rows of an 8-bit D = 64 cache, more than a block")
     cfg = cfg_of("prefill70b", name=f"shape_{q}_{kv}_{D}_{bs}_{G}", B=2, Hq=2 * G, Hkv=2, D=D,
                  block_size=bs, kv_dtype=kv, q_dtype=q, out_dtype=q, src_dtype=q,
                  prefill=dict(new=(1, 150), ctx=(0, 90)))
