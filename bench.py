@@ -572,7 +572,9 @@ def main(argv=None):
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": nbytes, "avg_launch_ms": round(part_ms, 5)},
+                     "traffic": traffic, "algorithmic_bytes": nbytes, "avg_launch_ms": round(part_ms, 5),
+                     "launch_scope": ("pa_decode_partition call: plan kernel, then the attention kernel"
+                                      if partition == 0 else "pa_decode_partition call: the attention kernel")},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

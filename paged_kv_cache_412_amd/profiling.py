@@ -130,14 +130,25 @@ def summarize(workload: str, d: str) -> None:
     ktrace = _find(d, f"trace_{workload}_kernel_trace.csv")
     if ktrace is not None:
         with open(ktrace, newline="") as f:
-            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-                    for r in csv.DictReader(f) if _short(r["Kernel_Name"]).startswith(f"pa::{kernel}")]
+            trace_rows = list(csv.DictReader(f))
+
+        def durations(name):
+            return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                    for r in trace_rows if _short(r["Kernel_Name"]).startswith(f"pa::{name}")]
+
+        durs = durations(kernel)
         last = durs[-STEPS * (2 if cfg.swap else 1):]
         if last:
             timed_us = sum(last) / len(last)
             lines += ["", f"`{kernel}`: mean over the {len(last)} launches bench.py times (the last ones of "
                           f"the run, from the kernel trace): {timed_us:.2f} us; over all {len(durs)} "
                           f"launches, warm-up included: {sum(durs) / len(durs):.2f} us."]
+        plan = durations("decode_plan_kernel")[-STEPS:]
+        if plan and last and not cfg.prefill and not cfg.swap:
+            plan_us = sum(plan) / len(plan)
+            lines += [f"bench.py's events bracket the `pa_decode_partition` call, which launches "
+                      f"`decode_plan_kernel` ({plan_us:.2f} us) and then `{kernel}`: "
+                      f"{plan_us + timed_us:.2f} us together on the kernel trace, launch gap excluded."]
     kvb = bench_kv_bytes(cfg)
     rate_us = timed_us or avg_us
     if avg_us and cfg.swap:

@@ -136,6 +136,20 @@ CONFIGS = {
                              len_range=(16384, 32768), head_scales=True),
     "long_e5m2": Config("long_e5m2", 12, B=16, Hq=32, Hkv=8, D=128, block_size=16, kv_dtype=E5M2,
                         q_dtype=BF16, out_dtype=BF16, src_dtype=BF16, len_range=(16384, 32768)),
+    # the 13B and 70B decode layers with other block sizes (8: a matrix-core
+    # tile spans two blocks; 64: walked as 32-token halves)
+    "llama13b_bs8": Config("llama13b_bs8", 14, B=64, Hq=40, Hkv=40, D=128, block_size=8,
+                           kv_dtype=F16, q_dtype=F16, out_dtype=F16, src_dtype=F16,
+                           len_range=(128, 2048)),
+    "llama13b_bs64": Config("llama13b_bs64", 15, B=64, Hq=40, Hkv=40, D=128, block_size=64,
+                            kv_dtype=F16, q_dtype=F16, out_dtype=F16, src_dtype=F16,
+                            len_range=(128, 2048)),
+    "llama70b_bs8": Config("llama70b_bs8", 16, B=256, Hq=64, Hkv=8, D=128, block_size=8,
+                           kv_dtype=BF16, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
+                           lens=(4096,) * 256),
+    "llama70b_bs64": Config("llama70b_bs64", 17, B=256, Hq=64, Hkv=8, D=128, block_size=64,
+                            kv_dtype=BF16, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
+                            lens=(4096,) * 256),
     # prefill: several new tokens per sequence, causal over the paged context
     "prefill13b": Config("prefill13b", 7, B=16, Hq=40, Hkv=40, D=128, block_size=16, kv_dtype=F16,
                          q_dtype=F16, out_dtype=F16, src_dtype=F16,
