@@ -275,6 +275,26 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   // the same query column) for ds_bpermute
   const int xor16 = (lid ^ 16) << 2, xor32 = (lid ^ 32) << 2;
 
+  // value rows of 32-key step kp: keys 32*kp + 4*grp + e (e < 4) and
+  // 32*kp + 16 + 4*grp + e - 4, this lane's D/16 head-dim values of each
+  auto read_v = [&](const uint8_t* Vt, int kp, uint32_t (&vr)[8][EPL / 2]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = 32 * kp + (e < 4 ? 0 : 16) + 4 * grp + (e & 3);
+      if constexpr (EPL == 8) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(Vt + lds_off(key, lo));
+        vr[e][0] = x[0];
+        vr[e][1] = x[1];
+        vr[e][2] = x[2];
+        vr[e][3] = x[3];
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(Vt + lds_off(key, lo >> 1) + ((lo & 1) << 3));
+        vr[e][0] = x[0];
+        vr[e][1] = x[1];
+      }
+    }
+  };
+
   int ids_next = load_ids(1);  // tile 1's blocks (consumed one iteration later)
   fetch(0, load_ids(0), 0);
   stage(0);
@@ -303,6 +323,10 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
           for (int nt = 0; nt < NT; ++nt) s[ks][nt] = M::mma32(a, qv[nt][kk], s[ks][nt]);
         }
       }
+      // the first value rows, read now so that their LDS latency hides
+      // behind the softmax
+      uint32_t vrow[2][8][EPL / 2];
+      read_v(Vt, 0, vrow[0]);
       // mask keys after each query's position (only near the diagonal)
       if (k0 + kKeys - 1 > pmin) {
 #pragma unroll
@@ -365,24 +389,9 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
           // result is an exact weighted mean of V rows under those weights
           l[nt] = M::mma32(ones, pb[nt], l[nt]);
         }
-        // value rows: keys 32*kp + 4*grp + e (e < 4) and 32*kp + 16 + 4*grp + e - 4
-        uint32_t vr[8][EPL / 2];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = 32 * kp + (e < 4 ? 0 : 16) + 4 * grp + (e & 3);
-          if constexpr (EPL == 8) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(Vt + lds_off(key, lo));
-            vr[e][0] = x[0];
-            vr[e][1] = x[1];
-            vr[e][2] = x[2];
-            vr[e][3] = x[3];
-          } else {
-            const u32x2 x =
-                *reinterpret_cast<const u32x2*>(Vt + lds_off(key, lo >> 1) + ((lo & 1) << 3));
-            vr[e][0] = x[0];
-            vr[e][1] = x[1];
-          }
-        }
+        // the next step's value rows go out before this step's products
+        if (kp + 1 < KP) read_v(Vt, kp + 1, vrow[(kp + 1) & 1]);
+        uint32_t (&vr)[8][EPL / 2] = vrow[kp & 1];
 #pragma unroll
         for (int mm = 0; mm < EPL; ++mm) {
           const u32x4 a = {pick_halves(vr[0][mm / 2], vr[1][mm / 2], mm & 1),

@@ -77,7 +77,8 @@ def test_step_small_all_outputs(name):
 
 
 @pytest.mark.parametrize("name", ["llama13b", "llama70b", "shared", "long_fp8", "long_fp8_bs32",
-                                  "long_fp8_heads", "long_e5m2"])
+                                  "long_fp8_heads", "long_e5m2", "llama13b_bs8", "llama70b_bs8",
+                                  "llama13b_bs64", "llama70b_bs64"])
 def test_step_full_size_sampled(name):
     cfg = C[name]
     rng = np.random.default_rng(7)
@@ -396,6 +397,31 @@ def test_decode_is_deterministic():
     step.decode_reduce()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), step.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "llama13b_bs8", "llama70b_bs8", "llama13b_bs64",
+                                  "llama70b_bs64", "long_fp8_bs8"])
+@pytest.mark.parametrize("part", [0, 64])
+def test_ids_outside_the_pool_touch_nothing_else(name, part):
+    """Table entries outside [0, num_blocks) in one sequence's table (negative
+    and past the pool, also inside a 16-token tile of 8-token blocks and in
+    either half of a 64-token block): that sequence's result is meaningless,
+    but the call reads nothing outside the pool and every other sequence's
+    output is bit-identical to the run with the valid table."""
+    cfg = SMALL[name]
+    wl, step, exp = run_step(cfg, partition_size=part)
+    check_step(wl, step, exp)
+    good = step.out.clone()
+    bad = step.block_tables.clone()
+    n = len(step.tables_list[0])
+    assert n >= 3
+    for j in range(0, n, 2):
+        bad[0, j] = -1 if j % 4 == 0 else wl.num_blocks + 3 * j + 1
+    step.args.block_tables = bad.data_ptr()
+    step.decode_partition()
+    step.decode_reduce()
+    torch.cuda.synchronize()
+    assert torch.equal(step.out[1:].view(torch.int16), good[1:].view(torch.int16))
 
 
 def test_errors_surface_as_exceptions():
