@@ -526,7 +526,7 @@ def main(argv=None):
     print(f"[bench] {args.steps} steps, {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
     # per-stage durations, events on the same stream around each C-ABI call
-    stages = ["slot_mapping", "copy_blocks", "cache_write", "decode_partition", "decode_reduce"]
+    stages = list(DecodeStep.STAGES)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(args.steps)]
     torch.cuda.synchronize()

@@ -214,6 +214,24 @@ pa_status pa_reshape_and_cache_scales(const void* k_new, const void* v_new, void
                                       int32_t num_blocks, pa_dtype src_dtype, pa_dtype kv_dtype,
                                       const float* k_scales, const float* v_scales, void* stream);
 
+/* The slot mapping and the cache write of one new token per sequence in one
+ * launch (P1 "Sayfalama Nasıl Çalışır": the token's slot from its block
+ * table, then its K/V rows written there).  Equivalent to
+ *   pa_slot_mapping(block_tables, positions, B, max_blocks_per_seq,
+ *                   block_size, slots)
+ * followed by pa_reshape_and_cache (k_scales null) or
+ * pa_reshape_and_cache_scales (k_scales and v_scales device arrays [Hkv]) of
+ * the B rows k_new, v_new [B][Hkv][D] at those slots.  slots (int32 [B],
+ * device) receives the slots and may be NULL.  Rows whose slot is -1 or
+ * outside the pool are not written.  Argument checks are those of the two
+ * calls; k_scale and v_scale are ignored when k_scales is given. */
+pa_status pa_append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       const int32_t* block_tables, const int32_t* positions, int32_t B,
+                       int32_t max_blocks_per_seq, int32_t* slots, int32_t Hkv, int32_t D,
+                       int32_t block_size, int32_t num_blocks, pa_dtype src_dtype,
+                       pa_dtype kv_dtype, float k_scale, float v_scale, const float* k_scales,
+                       const float* v_scales, void* stream);
+
 /* Copy-on-write block copy (P1 "Diziler Arasında Blokları Paylaşma": a
  * sequence about to write into a block that other sequences still use gets a
  * copy first; P3 article A, shared prefix support).  For each of the P rows

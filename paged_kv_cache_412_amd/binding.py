@@ -108,6 +108,9 @@ def lib() -> ctypes.CDLL:
     L.pa_reshape_and_cache_scales.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                               ctypes.c_int, vp, vp, vp]
     L.pa_reshape_and_cache_scales.restype = ctypes.c_int
+    L.pa_append_kv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_float, ctypes.c_float, vp, vp, vp]
+    L.pa_append_kv.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     L.pa_copy_blocks.restype = ctypes.c_int
     L.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
@@ -313,6 +316,44 @@ def reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, k_scale=1.0, v_scal
                                       _ptr(slots), T, Hkv, D, bs, NB, _pa_dtype(k_new),
                                       _pa_dtype(k_cache, kv_dtype), float(k_scale), float(v_scale),
                                       _stream(stream)), "pa_reshape_and_cache")
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, block_tables, positions, slots=None, k_scale=1.0,
+              v_scale=1.0, kv_dtype=None, stream=None, k_scales=None, v_scales=None):
+    """pa_append_kv: the slot mapping and the cache write of one new token per
+    sequence in one launch; the slots go to ``slots`` when it is given."""
+    _require(k_new, "k_new", ndim=3)
+    _require(v_new, "v_new", ndim=3)
+    _require(k_cache, "k_cache", ndim=4)
+    _require(v_cache, "v_cache", ndim=4)
+    _require(block_tables, "block_tables", torch.int32, 2)
+    _require(positions, "positions", torch.int32, 1)
+    B, Hkv, D = k_new.shape
+    NB, bs, Hkv2, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("inconsistent shapes")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_new.dtype != k_new.dtype:
+        raise ValueError("K and V must match")
+    if block_tables.shape[0] != B or positions.shape[0] != B:
+        raise ValueError("batch mismatch")
+    if slots is not None:
+        _require(slots, "slots", torch.int32, 1)
+        if slots.shape[0] != B:
+            raise ValueError("batch mismatch")
+    if (k_scales is None) != (v_scales is None):
+        raise ValueError("per-head scales come in pairs")
+    for t, n in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if t is not None:
+            _require(t, n, torch.float32, 1)
+            if t.shape[0] != Hkv:
+                raise ValueError(f"{n} must hold one scale per KV head")
+    _check(lib().pa_append_kv(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_tables), _ptr(positions), B, block_tables.shape[1],
+                              _ptr(slots) if slots is not None else None, Hkv, D, bs, NB,
+                              _pa_dtype(k_new), _pa_dtype(k_cache, kv_dtype), float(k_scale),
+                              float(v_scale), _ptr(k_scales) if k_scales is not None else None,
+                              _ptr(v_scales) if v_scales is not None else None, _stream(stream)),
+           "pa_append_kv")
 
 
 def copy_blocks(k_cache, v_cache, block_mapping, kv_dtype=None, stream=None):

@@ -24,12 +24,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ slot mapping
 
-__global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* __restrict__ tables,
-                                                           const int32_t* __restrict__ positions,
-                                                           int32_t B, int32_t max_blocks,
-                                                           int32_t bs, int32_t* __restrict__ slots) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
+// Slot of sequence b's token at positions[b]: -1 for a negative position, a
+// position past the table, a negative block id or a slot past int32.
+__device__ __forceinline__ int slot_of(const int32_t* __restrict__ tables,
+                                       const int32_t* __restrict__ positions, int b, int max_blocks,
+                                       int bs) {
   const int pos = positions[b];
   int slot = -1;
   if (pos >= 0 && pos / bs < max_blocks) {
@@ -37,7 +36,25 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* __rest
     const int64_t s = static_cast<int64_t>(blk) * bs + pos % bs;
     if (blk >= 0 && s <= INT32_MAX) slot = static_cast<int>(s);
   }
-  slots[b] = slot;
+  return slot;
+}
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* __restrict__ tables,
+                                                           const int32_t* __restrict__ positions,
+                                                           int32_t B, int32_t max_blocks,
+                                                           int32_t bs, int32_t* __restrict__ slots) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  slots[b] = slot_of(tables, positions, b, max_blocks, bs);
+}
+
+// The slot of cache-write row t (grid (T, 2)): given, or computed from the
+// table and position (and then stored once, by the K work-group).
+__device__ __forceinline__ int row_slot(const SlotSource& src, int t, int bs) {
+  if (src.slots) return src.slots[t];
+  const int slot = slot_of(src.tables, src.positions, t, src.max_blocks, bs);
+  if (src.slots_out && blockIdx.y == 0 && threadIdx.x == 0) src.slots_out[t] = slot;
+  return slot;
 }
 
 // ------------------------------------------------------------------ cache write
@@ -48,10 +65,10 @@ __global__ __launch_bounds__(256) void cache_copy_kernel(const u32x4* __restrict
                                                          const u32x4* __restrict__ v_new,
                                                          u32x4* __restrict__ k_cache,
                                                          u32x4* __restrict__ v_cache,
-                                                         const int32_t* __restrict__ slots,
+                                                         const SlotSource slots, int32_t bs,
                                                          int32_t row_chunks, int64_t num_slots) {
   const int t = blockIdx.x;
-  const int slot = slots[t];
+  const int slot = row_slot(slots, t, bs);
   if (slot < 0 || slot >= num_slots) return;
   const u32x4* src = (blockIdx.y == 0 ? k_new : v_new) + static_cast<size_t>(t) * row_chunks;
   u32x4* dst = (blockIdx.y == 0 ? k_cache : v_cache) + static_cast<size_t>(slot) * row_chunks;
@@ -108,7 +125,7 @@ __global__ __launch_bounds__(256) void cache_quant_kernel(const char* __restrict
                                                           const char* __restrict__ v_new,
                                                           u32x2* __restrict__ k_cache,
                                                           u32x2* __restrict__ v_cache,
-                                                          const int32_t* __restrict__ slots,
+                                                          const SlotSource slots, int32_t bs,
                                                           int32_t row_elems, int64_t num_slots,
                                                           float k_inv, float v_inv,
                                                           const float* __restrict__ k_scales,
@@ -116,7 +133,7 @@ __global__ __launch_bounds__(256) void cache_quant_kernel(const char* __restrict
                                                           int32_t D) {
   constexpr int SB = Elem<SRC>::bytes;
   const int t = blockIdx.x;
-  const int slot = slots[t];
+  const int slot = row_slot(slots, t, bs);
   if (slot < 0 || slot >= num_slots) return;
   const bool is_k = blockIdx.y == 0;
   const char* src = (is_k ? k_new : v_new) + static_cast<size_t>(t) * row_elems * SB;
@@ -183,7 +200,7 @@ hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* posit
 }
 
 hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache,
-                                    void* v_cache, const int32_t* slots, int32_t T, int32_t Hkv,
+                                    void* v_cache, const SlotSource& slots, int32_t T, int32_t Hkv,
                                     int32_t D, int32_t block_size, int32_t num_blocks,
                                     pa_dtype src_dtype, pa_dtype kv_dtype, float k_inv_scale,
                                     float v_inv_scale, const float* k_scales,
@@ -196,13 +213,13 @@ hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* 
     const int32_t row_chunks = row_elems * ebytes / 16;
     hipLaunchKernelGGL(cache_copy_kernel, grid, dim3(256), 0, stream,
                        static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new),
-                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slots, row_chunks,
-                       num_slots);
+                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), slots, block_size,
+                       row_chunks, num_slots);
   } else {
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, static_cast<const char*>(k_new),
                          static_cast<const char*>(v_new), static_cast<u32x2*>(k_cache),
-                         static_cast<u32x2*>(v_cache), slots, row_elems, num_slots, k_inv_scale,
+                         static_cast<u32x2*>(v_cache), slots, block_size, row_elems, num_slots, k_inv_scale,
                          v_inv_scale, k_scales, v_scales, D);
     };
     const bool e5 = kv_dtype == PA_FP8_E5M2;

@@ -56,14 +56,56 @@ struct SegmentDest {
   size_t part_row;  // partials row of query 0
 };
 
+// The balanced schedule's prefix sums, prefix[b] = blocks of sequences
+// before b and prefix[B] = all blocks.  With p.inline_plan every work-group
+// computes them into LDS (its threads take contiguous runs of sequences, a
+// wave scan and one pass over the wave totals; two barriers), and
+// work-group (0, 0) also stores them where the reduce kernel reads them;
+// otherwise the plan kernel has written them to p.prefix.  Every thread of
+// the work-group calls this, before any of them leaves.
+struct PlanLds {
+  int32_t prefix[kInlinePlanMaxB + 1];
+  int32_t wave_sum[16];
+};
+
+__device__ __forceinline__ const int32_t* schedule_prefix(const DecodeParams& p, PlanLds& lds) {
+  if (!p.inline_plan) return p.prefix;
+  const int T = blockDim.x, t = threadIdx.x, lane = t & 63;
+  auto nblk = [&](int b) { return (clamped_len(p, b) + p.block_size - 1) / p.block_size; };
+  const int run = (p.B + T - 1) / T;
+  const int b0 = min(p.B, t * run), b1 = min(p.B, b0 + run);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += nblk(b);
+  int x = local;  // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) lds.wave_sum[t >> 6] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < (t >> 6); ++w) base += lds.wave_sum[w];
+  int acc = base + x - local;
+  for (int b = b0; b < b1; ++b) {
+    lds.prefix[b] = acc;
+    acc += nblk(b);
+  }
+  if (t == T - 1) lds.prefix[p.B] = base + x;
+  __syncthreads();
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = t; i <= p.B; i += T) p.prefix[i] = lds.prefix[i];
+  return lds.prefix;
+}
+
 // Calls fn(b, span, dest) for every segment this wave works on, for KV head
 // g = head_group * NW + wave.  Fixed schedule: work-group (hg, b, part) has
 // one segment, partition `part` of sequence b.  Balanced schedule:
 // work-group (hg, w) walks the sequences that overlap blocks
 // [w*F/groups, (w+1)*F/groups) of the concatenated block list.
 template <typename Fn>
-__device__ __forceinline__ void for_each_segment(const DecodeParams& p, int hg, int wave, int G,
-                                                 Fn&& fn) {
+__device__ __forceinline__ void for_each_segment(const DecodeParams& p, const int32_t* prefix, int hg,
+                                                 int wave, int G, Fn&& fn) {
   const int g = hg * p.heads_per_wg + wave;
   if (!p.balanced) {
     const int b = blockIdx.y;
@@ -83,7 +125,7 @@ __device__ __forceinline__ void for_each_segment(const DecodeParams& p, int hg, 
     return;
   }
   const int w = blockIdx.y;
-  const int64_t F = p.prefix[p.B];
+  const int64_t F = prefix[p.B];
   const int n = balanced_groups(p, F);
   if (w >= n) return;  // fewer blocks than work-groups: the rest idle
   const int64_t x0 = balanced_start(F, w, n);
@@ -92,14 +134,14 @@ __device__ __forceinline__ void for_each_segment(const DecodeParams& p, int hg, 
   int lo = 0, hi = p.B;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (p.prefix[mid] <= x0) lo = mid;
+    if (prefix[mid] <= x0) lo = mid;
     else hi = mid;
   }
   int which = 0;
   for (int b = lo; b < p.B; ++b) {
-    const int64_t pb = p.prefix[b];
+    const int64_t pb = prefix[b];
     if (pb >= x1) break;
-    const int64_t pn = p.prefix[b + 1];
+    const int64_t pn = prefix[b + 1];
     if (pn <= x0 || pn == pb) continue;  // before the range, or no blocks
     PartitionSpan s;
     s.L = clamped_len(p, b);

@@ -77,6 +77,8 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = blockIdx.x;
   const int g = hg * p.heads_per_wg + wave;
+  __shared__ PlanLds plan_lds;
+  const int32_t* prefix = schedule_prefix(p, plan_lds);  // every thread, before any leaves
   if (g >= p.Hkv) return;  // last head group of a head count that is not a multiple
   const int lo = lane & 15;
   const int grp = lane >> 4;
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
     }
   };
 
-  for_each_segment(p, hg, wave, G, [&](int b, const PartitionSpan& span, const SegmentDest& dst) {
+  for_each_segment(p, prefix, hg, wave, G, [&](int b, const PartitionSpan& span, const SegmentDest& dst) {
     // Q^T operand: query lo of the group, zero rows beyond G.
     uint32_t qw[KW];
     if (lo < G) {

@@ -189,6 +189,8 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = blockIdx.x;
   const int g = hg * p.heads_per_wg + wave;
+  __shared__ PlanLds plan_lds;
+  const int32_t* prefix = schedule_prefix(p, plan_lds);  // every thread, before any leaves
   if (g >= p.Hkv) return;  // last head group of a head count that is not a multiple
   const int c = lane % LPT;   // chunk of the row this lane owns
   const int tg = lane / LPT;  // row within a wave load
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
     for (int i = 0; i < NL; ++i) buffer_load<4>(vr, lane_off, i * TPL * row_stride, r.v[i].w);
   };
 
-  for_each_segment(p, hg, wave, G, [&](int b, const PartitionSpan& span, const SegmentDest& dst) {
+  for_each_segment(p, prefix, hg, wave, G, [&](int b, const PartitionSpan& span, const SegmentDest& dst) {
     typename O::QReg qr[G];
     {
       const char* qrow =

@@ -23,6 +23,11 @@ namespace pa {
 //    concatenation of all sequences (F = prefix[B]).  It writes the output of
 //    every sequence it covers whole and partials only for the (at most two)
 //    sequences it covers in part; rows are balanced_row(...).
+// Balanced schedule: up to this many sequences, the attention kernel's
+// work-groups compute the block-count prefix sums themselves (in LDS) instead
+// of a plan kernel launched before them.
+constexpr int kInlinePlanMaxB = 1024;
+
 struct DecodeParams {
   void* out;
   const void* q;
@@ -46,6 +51,7 @@ struct DecodeParams {
   int32_t heads_per_wg;    // waves (KV heads) per work-group
   int32_t head_groups;     // ceil(Hkv / heads_per_wg)
   int32_t groups;          // balanced: work-groups per head group
+  int32_t inline_plan;     // balanced, B <= kInlinePlanMaxB: each work-group computes the plan
   float qk_scale_log2;     // scale * k_scale * log2(e) (scale * log2(e) with per-head scales)
   float v_scale;
   const float* k_scales;   // per-head scales [Hkv] (device) or nullptr
@@ -162,10 +168,20 @@ hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* positions, int32_t B,
                                int32_t max_blocks, int32_t block_size, int32_t* slots,
                                hipStream_t stream);
+// Where the cache write takes each row's slot: from `slots`, or (slots null)
+// computed from the row's block table and position as the slot mapping does,
+// and then also stored to slots_out when that is not null.
+struct SlotSource {
+  const int32_t* slots;
+  const int32_t* tables;     // [T][max_blocks]
+  const int32_t* positions;  // [T]
+  int32_t max_blocks;
+  int32_t* slots_out;
+};
 // The cache write; an 8-bit cache takes one inverse scale per pool, or (when
 // k_scales is not null) one scale per KV head from device arrays.
 hipError_t launch_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache,
-                                    void* v_cache, const int32_t* slots, int32_t T, int32_t Hkv,
+                                    void* v_cache, const SlotSource& slots, int32_t T, int32_t Hkv,
                                     int32_t D, int32_t block_size, int32_t num_blocks,
                                     pa_dtype src_dtype, pa_dtype kv_dtype, float k_inv_scale,
                                     float v_inv_scale, const float* k_scales,

@@ -65,13 +65,30 @@ class DecodeStep:
         binding.reshape_and_cache(wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, self.slots, self.k_scale,
                                   self.v_scale, self.kv_dtype, stream, self.k_scales, self.v_scales)
 
+    def append_kv(self, stream=None):
+        """Slot mapping and cache write in one launch (pa_append_kv)."""
+        wl = self.wl
+        binding.append_kv(wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, self.block_tables, self.positions,
+                          self.slots, self.k_scale, self.v_scale, self.kv_dtype, stream, self.k_scales,
+                          self.v_scales)
+
     def decode_partition(self, stream=None):
         binding.decode_partition_run(self.args, stream)
 
     def decode_reduce(self, stream=None):
         binding.decode_reduce_run(self.args, stream)
 
+    # the step: copy-on-write copies first (the new token may land in a
+    # copied block), then the new token's slot and K/V rows, attention, reduce
+    STAGES = ("copy_blocks", "append_kv", "decode_partition", "decode_reduce")
+
     def run(self, stream=None):
+        for s in self.STAGES:
+            getattr(self, s)(stream)
+        return self.out
+
+    def run_unfused(self, stream=None):
+        """The same step with the slot mapping and the cache write as two calls."""
         self.slot_mapping(stream)
         self.copy_blocks(stream)
         self.cache_write(stream)

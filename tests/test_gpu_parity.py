@@ -463,3 +463,53 @@ def test_per_head_scale_cache_write_bit_exact(fmt, src):
     exp_v = parity.encode_rows(raw, src, fmt, scales[::-1].copy())
     assert np.array_equal(k_cache.cpu().numpy().reshape(T, Hkv, D), exp_k)
     assert np.array_equal(v_cache.cpu().numpy().reshape(T, Hkv, D), exp_v)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama13b", "llama70b_bs8", "long_fp8_bs64", "long_e5m2_heads",
+                                  "long_fp8_heads"])
+def test_append_kv_equals_slot_mapping_then_cache_write(name):
+    """pa_append_kv (one launch) leaves the same slots and the same pools, byte
+    for byte, as pa_slot_mapping followed by pa_reshape_and_cache, with
+    positions that are negative or past the table mixed in."""
+    cfg = SMALL[name]
+    print(f"\n[case] append_kv {name} bs={cfg.block_size} kv={cfg.kv_dtype}", flush=True)
+    wl = workloads.make(cfg, device="cuda")
+    step = DecodeStep(wl)
+    pos = step.positions.clone()
+    pos[0] = -1
+    pos[-1] = step.block_tables.shape[1] * cfg.block_size + 3
+    step.positions = pos
+    k0, v0 = wl.k_pool.clone(), wl.v_pool.clone()
+    step.slot_mapping()
+    step.cache_write()
+    torch.cuda.synchronize()
+    want_slots = step.slots.clone()
+    want_k, want_v = wl.k_pool.clone(), wl.v_pool.clone()
+    wl.k_pool.copy_(k0)
+    wl.v_pool.copy_(v0)
+    step.slots.fill_(12345)
+    step.append_kv()
+    torch.cuda.synchronize()
+    assert torch.equal(step.slots, want_slots)
+    assert want_slots[0].item() == -1 and want_slots[-1].item() == -1
+    assert torch.equal(wl.k_pool.view(torch.uint8), want_k.view(torch.uint8))
+    assert torch.equal(wl.v_pool.view(torch.uint8), want_v.view(torch.uint8))
+
+
+def test_slot_mapping_matches_the_oracle():
+    """pa_slot_mapping against the oracle's slot formula, every position of
+    every table entry plus negative positions and positions past the table."""
+    from oracle import paged
+    rng = np.random.default_rng(21)
+    for bs in (8, 16, 32, 64):
+        B, MB = 300, 7
+        tables = rng.integers(0, 5000, size=(B, MB)).astype(np.int32)
+        pos = rng.integers(-3, MB * bs, size=B).astype(np.int32)
+        past = rng.choice(B, 20, replace=False)      # positions past the table: slot -1
+        exp = paged.slot_mapping(tables.astype(np.int64), pos.astype(np.int64), bs)
+        pos[past] = MB * bs + rng.integers(0, 3 * bs, 20)
+        exp[past] = -1
+        slots = torch.full((B,), 7, dtype=torch.int32, device="cuda")
+        binding.slot_mapping(torch.from_numpy(tables).cuda(), torch.from_numpy(pos).cuda(), bs, slots)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots.cpu().numpy(), exp), bs
