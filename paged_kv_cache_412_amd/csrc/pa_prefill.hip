@@ -96,10 +96,11 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   constexpr int ROWB = D * 2;              // LDS bytes per key row
   constexpr int TILE = kKeys * ROWB;
   constexpr int CPR = D * KVB / 16;        // 16-byte global chunks per key row
-  constexpr int RPP = (kWaves * 64 / CPR) < kKeys ? (kWaves * 64 / CPR) : kKeys;
-  constexpr int PASSES = kKeys / RPP;      // staging loads per thread, K and V each
+  constexpr int WR = kKeys / kWaves;        // rows of a tile each wave stages
+  constexpr int WROWS = 64 / CPR;          // rows one wave load covers
+  constexpr int PASSES = WR / WROWS;       // staging loads per thread, K and V each
   static_assert(kPrefillRows == kWaves * RW, "rows per work-group");
-  static_assert(kKeys % RPP == 0 && kKeys % 32 == 0, "tile shape");
+  static_assert(WR % WROWS == 0 && kKeys % 32 == 0, "tile shape");
   static_assert(EPL % 2 == 0 && (CH == 8 || CH == 16), "head dim");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE];  // [buffer][K, V]
 
@@ -167,12 +168,14 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   const int pmin = ctx + t0 + wtok0;
   const int pmax = ctx + t0 + min((wave * RW + RW - 1) / G, ntok - 1);
 
-  // ---- staging: thread -> (key row within the pass, 16-byte chunk).  The
-  // rows one wave stages in one pass lie in one block, so each wave reads
-  // them through one buffer resource over that block: absent blocks get a
-  // resource of 0 bytes and rows past the last key an offset past the end,
-  // and both read as zeros.  Every path thus issues the same loads, and the
-  // compiler's wait counts stay exact (loads retire in order).
+  // ---- staging: wave wv stages the tile's rows [wv*WR, wv*WR + WR), WROWS
+  // rows per load (lane -> row within the load, 16-byte chunk).  The rows
+  // of one load lie in one block, and with blocks of WR rows or more all of
+  // a wave's rows do, so the wave builds its buffer resources over that
+  // block once per tile.  Absent blocks get a resource of 0 bytes and rows
+  // past the last key an offset past the end, and both read as zeros.  Every
+  // path thus issues the same loads, and the compiler's wait counts stay
+  // exact (loads retire in order).
   //
   // 16-bit K/V go from the pool straight into LDS (buffer loads with the LDS
   // bit): one such load fills 1 KiB from a wave-uniform base, lane i at byte
@@ -183,8 +186,8 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   // fills before the barrier that ends the iteration.  8-bit K/V are loaded
   // into registers and widened to the 16-bit operand type on their way to LDS.
   constexpr int TB = kKeys / BS > 0 ? kKeys / BS : 1;  // blocks per key tile
-  constexpr int WROWS = 64 / CPR;                       // rows one wave stages per pass
-  static_assert(WROWS <= BS && BS % WROWS == 0, "a wave's rows in one block");
+  static_assert(WROWS <= BS && BS % WROWS == 0, "a wave load's rows in one block");
+  constexpr bool ONE_BLOCK = BS >= WR;                  // all of a wave's rows in one block
   static_assert(KVB != 2 || WROWS * ROWB == 1024, "one LDS fill per wave and pass");
   const int64_t row_stride = static_cast<int64_t>(p.Hkv) * D * KVB;
   const uint32_t blk_bytes = static_cast<uint32_t>(row_stride * BS);
@@ -192,38 +195,40 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   const int nblk = (n_keys + BS - 1) / BS;  // table entries this work-group reads
   const __amdgpu_buffer_rsrc_t trs = block_rsrc(table, static_cast<uint32_t>(nblk) * 4u);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int srow = threadIdx.x / CPR, schunk = threadIdx.x % CPR;
-  const bool wave_stages = wv * WROWS < RPP;  // uniform: whole waves stage or not
+  const int srow = lid / CPR, schunk = lid % CPR;  // row within a wave load, 16-byte chunk
   u32x4 kst[KVB == 2 ? 1 : PASSES], vst[KVB == 2 ? 1 : PASSES];  // 8-bit codes in flight
   // ids of the blocks of a tile, lane t < TB holding its t-th block
   auto load_ids = [&](int j) {
     return static_cast<int>(
         __builtin_amdgcn_raw_buffer_load_b32(trs, (j * TB + (lid % TB)) * 4, 0, 0));
   };
-  // issue tile j's loads (into LDS buffer buf for 16-bit K/V)
+  // issue tile j's loads (into LDS buffer buf for 16-bit K/V).  Wave wv
+  // stages rows [wv*WR, wv*WR + WR) of the tile, WROWS per load.
   auto fetch = [&](int j, int ids, int buf) {
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int row0 = ps * RPP + wv * WROWS;          // first row this wave stages
+    __amdgpu_buffer_rsrc_t kr, vr;
+    auto block_of = [&](int row0) {  // resources over the block holding tile row row0
       const int blk = __builtin_amdgcn_readlane(ids, (row0 / BS) % TB);
-      const int key0 = j * kKeys + row0;
-      const bool ok = wave_stages && key0 < n_keys && blk >= 0 && blk < p.num_blocks;
+      const bool ok = blk >= 0 && blk < p.num_blocks;
       const char* kb = static_cast<const char*>(p.k_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
       const char* vb = static_cast<const char*>(p.v_cache) + static_cast<int64_t>(ok ? blk : 0) * blk_bytes;
-      const __amdgpu_buffer_rsrc_t kr = block_rsrc(kb, ok ? blk_bytes : 0u);
-      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vb, ok ? blk_bytes : 0u);
-      const int r = ps * RPP + srow;                   // this lane's row of the tile
-      const int key = j * kKeys + r;
+      kr = block_rsrc(kb, ok ? blk_bytes : 0u);
+      vr = block_rsrc(vb, ok ? blk_bytes : 0u);
+    };
+    if constexpr (ONE_BLOCK) block_of(wv * WR);
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int row0 = wv * WR + ps * WROWS;          // first row of this wave load
+      if constexpr (!ONE_BLOCK) block_of(row0);
+      const int r = row0 + srow;                      // this lane's row of the tile
+      const int key = j * kKeys + r;                  // rows past the last key read zeros
       const int row_off = static_cast<int>((key % BS) * row_stride) + kvh * D * KVB;
       if constexpr (KVB == 2) {
         const int sw = CH == 16 ? (r & 15) : ((r >> 1) & 7);
         const int voff = key < n_keys ? row_off + ((schunk ^ sw) << 4) : 0x7fffff00;
-        if (wave_stages) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              kr, (__attribute__((address_space(3))) void*)(lds[buf][0] + row0 * ROWB), 16, voff, 0, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              vr, (__attribute__((address_space(3))) void*)(lds[buf][1] + row0 * ROWB), 16, voff, 0, 0, 0);
-        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void*)(lds[buf][0] + row0 * ROWB), 16, voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void*)(lds[buf][1] + row0 * ROWB), 16, voff, 0, 0, 0);
       } else {
         const int voff = key < n_keys ? row_off + schunk * 16 : 0x7fffff00;
         kst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, voff, 0, 0));
@@ -236,10 +241,9 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
     if constexpr (KVB == 2) {
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's LDS fills have landed
     } else {
-      if (!wave_stages) return;
 #pragma unroll
       for (int ps = 0; ps < PASSES; ++ps) {
-        const int r = ps * RPP + srow;
+        const int r = wv * WR + ps * WROWS + srow;
         uint8_t* kd = lds[buf][0];
         uint8_t* vd = lds[buf][1];
         // 16 8-bit codes -> 16 operand values (exact), two chunks
