@@ -202,6 +202,21 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
     return static_cast<int>(
         __builtin_amdgcn_raw_buffer_load_b32(trs, (j * TB + (lid % TB)) * 4, 0, 0));
   };
+  // each lane's byte offset inside a block for its row of every load (the
+  // same in every tile: kKeys is a multiple of the block size), its head's
+  // column and its 16-byte chunk included (for 16-bit K/V the logical chunk
+  // the swizzle puts at the lane's LDS position)
+  static_assert(kKeys % BS == 0, "tiles start on block boundaries");
+  int lane_off[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int r = wv * WR + ps * WROWS + srow;
+    int c = schunk;
+    if constexpr (KVB == 2) c ^= CH == 16 ? (r & 15) : ((r >> 1) & 7);
+    lane_off[ps] = static_cast<int>((r % BS) * row_stride) + kvh * D * KVB + (c << 4);
+  }
+  const int lane_row = wv * WR + srow;  // this lane's row of the tile in its first load
+
   // issue tile j's loads (into LDS buffer buf for 16-bit K/V).  Wave wv
   // stages rows [wv*WR, wv*WR + WR) of the tile, WROWS per load.
   auto fetch = [&](int j, int ids, int buf) {
@@ -219,18 +234,14 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
     for (int ps = 0; ps < PASSES; ++ps) {
       const int row0 = wv * WR + ps * WROWS;          // first row of this wave load
       if constexpr (!ONE_BLOCK) block_of(row0);
-      const int r = row0 + srow;                      // this lane's row of the tile
-      const int key = j * kKeys + r;                  // rows past the last key read zeros
-      const int row_off = static_cast<int>((key % BS) * row_stride) + kvh * D * KVB;
+      // rows past the last key read zeros (an offset past the end)
+      const int voff = lane_row + ps * WROWS < n_keys - j * kKeys ? lane_off[ps] : 0x7fffff00;
       if constexpr (KVB == 2) {
-        const int sw = CH == 16 ? (r & 15) : ((r >> 1) & 7);
-        const int voff = key < n_keys ? row_off + ((schunk ^ sw) << 4) : 0x7fffff00;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             kr, (__attribute__((address_space(3))) void*)(lds[buf][0] + row0 * ROWB), 16, voff, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             vr, (__attribute__((address_space(3))) void*)(lds[buf][1] + row0 * ROWB), 16, voff, 0, 0, 0);
       } else {
-        const int voff = key < n_keys ? row_off + schunk * 16 : 0x7fffff00;
         kst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, voff, 0, 0));
         vst[ps] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 0, 0));
       }
