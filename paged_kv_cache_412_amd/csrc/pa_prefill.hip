@@ -29,12 +29,15 @@
 //     for keys 4*grp + r of each 16-key half.
 //   O^T += V^T P^T, one 16x16x32 MFMA per 16 head-dim rows: B = P^T straight
 //     from the score registers (slots e < 4: keys 4*grp + e of the first
-//     half, e >= 4: the same of the second half); A = V^T, where MFMA number
-//     mm maps row lo to head-dim d = (D/16)*lo + mm, so each lane reads one
-//     contiguous D/16-element run of each of its eight key rows and the 16
-//     lanes of a group read each row whole.  Lane l then holds output
-//     columns d = (D/16)*(4*grp + r) + mm of query row lo: D/4 contiguous
-//     values, stored with 16-byte writes.
+//     half, e >= 4: the same of the second half); A = V^T, MFMA number mm
+//     covering head dims 16*mm + [0, 16).  Lane l needs head dim 16*mm + lo
+//     of its eight keys: two transposing LDS reads (ds_read_b64_tr_b16) give
+//     it directly.  In such a read each lane of a 16-lane group addresses
+//     four consecutive 16-bit values, and lane d receives value d % 4 of the
+//     runs addressed by lanes d/4 + 4k, k = 0..3; so lane lo addresses key
+//     row 4*grp + lo/4 (+16 for the second half), head dims 16*mm + 4*(lo%4)
+//     .. + 3, and receives head dim 16*mm + lo of keys 4*grp .. 4*grp + 3.
+//     Lane l then holds output columns 16*mm + 4*grp + r of query row lo.
 // Softmax runs in log2 units on the score layout, with no cross-lane
 // traffic in the common case (each lane checks its own scores against the
 // shared running max).  The weights enter the
@@ -105,13 +108,14 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE];  // [buffer][K, V]
 
   // LDS placement of 16-byte chunk c of key row r: XOR-swizzled so that the
-  // 16 lanes that read one chunk column of 16 rows (K operands), the lanes
-  // that read one row whole (V operands) and the staging writes each touch
-  // distinct banks.
-  auto lds_off = [](int r, int c) {
-    const int sw = CH == 16 ? (r & 15) : ((r >> 1) & 7);
-    return r * ROWB + ((c ^ sw) << 4);
+  // reads of one chunk column of 16 rows (K operands), the transposing reads
+  // of two adjacent chunks of 4 consecutive rows (V operands: the rows'
+  // swizzles differ in bits 1-2) and the staging writes (whole rows) each
+  // touch distinct banks.
+  auto swz = [](int r) {
+    return ((r & 3) << 1) | ((r >> 2) & 1) | (CH == 16 ? (r & 8) : 0);
   };
+  auto lds_off = [&](int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); };
 
   const int lid = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   for (int ps = 0; ps < PASSES; ++ps) {
     const int r = wv * WR + ps * WROWS + srow;
     int c = schunk;
-    if constexpr (KVB == 2) c ^= CH == 16 ? (r & 15) : ((r >> 1) & 7);
+    if constexpr (KVB == 2) c ^= swz(r);
     lane_off[ps] = static_cast<int>((r % BS) * row_stride) + kvh * D * KVB + (c << 4);
   }
   const int lane_row = wv * WR + srow;  // this lane's row of the tile in its first load
@@ -292,21 +296,28 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
 
   // value rows of 32-key step kp: keys 32*kp + 4*grp + e (e < 4) and
   // 32*kp + 16 + 4*grp + e - 4, this lane's D/16 head-dim values of each
-  auto read_v = [&](const uint8_t* Vt, int kp, uint32_t (&vr)[8][EPL / 2]) {
+  // LDS operand addresses split into a per-lane part and a constant: K row
+  // 16*ks + lo and V row 16*h + 4*grp + e (h, e < 4 fixed per read) take
+  // the swizzle of rows lo and 4*grp + e, so their offsets are koff[kk] +
+  // 16*ks*ROWB and voff4[e] + 16*h*ROWB.
+  int koff[KK], vtr[EPL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = 32 * kp + (e < 4 ? 0 : 16) + 4 * grp + (e & 3);
-      if constexpr (EPL == 8) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(Vt + lds_off(key, lo));
-        vr[e][0] = x[0];
-        vr[e][1] = x[1];
-        vr[e][2] = x[2];
-        vr[e][3] = x[3];
-      } else {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(Vt + lds_off(key, lo >> 1) + ((lo & 1) << 3));
-        vr[e][0] = x[0];
-        vr[e][1] = x[1];
-      }
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = lds_off(lo, grp * KK + kk);
+  // transposing reads of V: within each 16-lane group, lane lo addresses
+  // row 4*grp + lo/4, head dims 16*mm + 4*(lo%4) .. + 3, and then receives
+  // head dim 16*mm + lo of rows 4*grp .. 4*grp + 3
+#pragma unroll
+  for (int mm = 0; mm < EPL; ++mm)
+    vtr[mm] = lds_off(4 * grp + (lo >> 2), 2 * mm + ((lo >> 1) & 1)) + ((lo & 1) << 3);
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  auto read_v = [&](const uint8_t* Vt, int kp, u32x4 (&va)[EPL]) {
+#pragma unroll
+    for (int mm = 0; mm < EPL; ++mm) {
+      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + 32 * kp * ROWB));
+      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + (32 * kp + 16) * ROWB));
+      const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
+      va[mm] = u32x4{y0[0], y0[1], y1[0], y1[1]};
     }
   };
 
@@ -333,15 +344,15 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
         for (int nt = 0; nt < NT; ++nt) s[ks][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(Kt + lds_off(16 * ks + lo, grp * KK + kk));
+          const u32x4 a = *reinterpret_cast<const u32x4*>(Kt + koff[kk] + 16 * ks * ROWB);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) s[ks][nt] = M::mma32(a, qv[nt][kk], s[ks][nt]);
         }
       }
       // the first value rows, read now so that their LDS latency hides
       // behind the softmax
-      uint32_t vrow[2][8][EPL / 2];
-      read_v(Vt, 0, vrow[0]);
+      u32x4 vop[2][EPL];
+      read_v(Vt, 0, vop[0]);
       // mask keys after each query's position (only near the diagonal)
       if (k0 + kKeys - 1 > pmin) {
 #pragma unroll
@@ -404,17 +415,12 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
           // result is an exact weighted mean of V rows under those weights
           l[nt] = M::mma32(ones, pb[nt], l[nt]);
         }
-        // the next step's value rows go out before this step's products
-        if (kp + 1 < KP) read_v(Vt, kp + 1, vrow[(kp + 1) & 1]);
-        uint32_t (&vr)[8][EPL / 2] = vrow[kp & 1];
+        // the next step's value operands go out before this step's products
+        if (kp + 1 < KP) read_v(Vt, kp + 1, vop[(kp + 1) & 1]);
 #pragma unroll
         for (int mm = 0; mm < EPL; ++mm) {
-          const u32x4 a = {pick_halves(vr[0][mm / 2], vr[1][mm / 2], mm & 1),
-                           pick_halves(vr[2][mm / 2], vr[3][mm / 2], mm & 1),
-                           pick_halves(vr[4][mm / 2], vr[5][mm / 2], mm & 1),
-                           pick_halves(vr[6][mm / 2], vr[7][mm / 2], mm & 1)};
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[nt][mm] = M::mma32(a, pb[nt], o[nt][mm]);
+          for (int nt = 0; nt < NT; ++nt) o[nt][mm] = M::mma32(vop[kp & 1][mm], pb[nt], o[nt][mm]);
         }
       }
     }
@@ -431,11 +437,11 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
     // weight 2^(s - m) is therefore about 1 or more
     const float inv = vs / lt;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v[EPL];
+    for (int mm = 0; mm < EPL; ++mm) {
+      float v[4];
 #pragma unroll
-      for (int mm = 0; mm < EPL; ++mm) v[mm] = o[nt][mm][r] * inv;
-      store_out_n<EPL>(p.out, orow[nt] + EPL * (4 * grp + r), v, p.out_dtype);
+      for (int r = 0; r < 4; ++r) v[r] = o[nt][mm][r] * inv;
+      store_out_n<4>(p.out, orow[nt] + 16 * mm + 4 * grp, v, p.out_dtype);
     }
   }
 }
