@@ -23,6 +23,7 @@ def test_header_declares_the_path_entry_points():
     for n in ("pa_decode", "pa_decode_partition", "pa_decode_reduce", "pa_decode_workspace_size",
               "pa_decode_partition_size",
               "pa_decode_check", "pa_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
+              "pa_reshape_and_cache_scales", "pa_append_kv",
               "pa_prefill", "pa_prefill_check", "pa_prefill_slot_mapping", "pa_swap_blocks",
               "pa_bm_create", "pa_bm_destroy", "pa_bm_add", "pa_bm_append", "pa_bm_fork", "pa_bm_free",
               "pa_bm_table", "pa_bm_length", "pa_bm_free_blocks", "pa_bm_cached_blocks",
@@ -188,6 +189,27 @@ def test_cache_and_copy_validation(L):
     assert L.pa_slot_mapping(vp, vp, 0, 4, 16, vp, None) == 0
     assert L.pa_slot_mapping(0, vp, 4, 4, 16, vp, None) == 1
     assert L.pa_slot_mapping(vp, vp, 4, 0, 16, vp, None) == 2
+
+
+def test_append_kv_validation(L):
+    """pa_append_kv: the checks of pa_slot_mapping and of the cache write."""
+    vp = FAKE
+    P = binding
+
+    def call(B=4, mb=8, slots=vp, hkv=8, d=64, bs=16, nb=64, src=P.PA_F16, kv=P.PA_F16, ks=1.0,
+             vs=1.0, kss=None, vss=None, k_new=vp, tables=vp):
+        return L.pa_append_kv(k_new, vp, vp, vp, tables, vp, B, mb, slots, hkv, d, bs, nb, src, kv,
+                              ks, vs, kss, vss, None)
+
+    assert call(B=0) == 0 and call(B=0, k_new=0, tables=0) == 0     # nothing to do
+    assert call(k_new=0) == 1 and call(tables=0) == 1
+    assert call(B=-1) == 2 and call(mb=0) == 2 and call(bs=0) == 2 and call(nb=0) == 2
+    assert call(nb=1 << 28, bs=16) == 2                               # slots past int32
+    assert call(src=P.PA_F32) == 3                                    # f32 rows into an f16 cache
+    assert call(src=P.PA_F16, kv=P.PA_FP8_E4M3, ks=0.0) == 2          # pool scale must be positive
+    assert call(src=P.PA_F16, kv=P.PA_FP8_E4M3, kss=vp) == 1         # per-head scales come in pairs
+    assert call(kss=vp, vss=vp) == 3                                  # per-head scales: 8-bit caches only
+    assert call(hkv=1, d=4) == 3                                      # rows not whole 16-byte chunks
 
 
 # ---------------------------------------------------------------- prefill
