@@ -274,6 +274,10 @@ def bench_prefill(args, cfg):
     return 0
 
 
+# the library computes the balanced schedule's plan inside the attention
+# kernel up to this many sequences (a separate plan kernel beyond)
+INLINE_PLAN_MAX_B = 1024
+
 HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
 
 
@@ -574,7 +578,8 @@ def main(argv=None):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": nbytes, "avg_launch_ms": round(part_ms, 5),
                      "launch_scope": ("pa_decode_partition call: plan kernel, then the attention kernel"
-                                      if partition == 0 else "pa_decode_partition call: the attention kernel")},
+                                      if partition == 0 and cfg.B > INLINE_PLAN_MAX_B
+                                      else "pa_decode_partition call: the attention kernel")},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
