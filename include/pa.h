@@ -112,8 +112,7 @@ typedef struct pa_decode_args {
  *   D in {64, 128}; block_size in {8, 16, 32, 64};
  *   (q, kv) in {(F32,F32), (F16,F16), (BF16,BF16), and BF16 or F16 over
  *   FP8_E4M3 or FP8_E5M2}; out_dtype = q_dtype or PA_F32;
- *   G = Hq/Hkv from 1 to 16, except fp32 caches: G in {1, 2, 4, 8};
- *   not block_size 8 with an 8-bit cache, D = 64 and G <= 2.
+ *   G = Hq/Hkv from 1 to 16, except fp32 caches: G in {1, 2, 4, 8}.
  *   64-token blocks are read as two 32-token halves: the balanced schedule
  *   then splits work at half-block granularity (block ids times 2 must fit
  *   int32, as must B * max_blocks_per_seq * 2). */
@@ -289,8 +288,7 @@ typedef struct pa_prefill_args {
 } pa_prefill_args;
 
 /* Supported prefill combinations (others return PA_ERR_UNSUPPORTED):
- *   D in {64, 128}; block_size in {8, 16, 32, 64} (not 8 with an 8-bit
- *   cache at D = 64); G = Hq/Hkv from 1 to 16;
+ *   D in {64, 128}; block_size in {8, 16, 32, 64}; G = Hq/Hkv from 1 to 16;
  *   (q, kv) in {(F16,F16), (BF16,BF16), and BF16 or F16 over FP8_E4M3 or
  *   FP8_E5M2};
  *   out_dtype = q_dtype or PA_F32.  No workspace. */

@@ -182,8 +182,14 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
   constexpr int QB = Elem<Q>::bytes;
   constexpr int LPT = D / CE;    // lanes per token row
   constexpr int TPL = 64 / LPT;  // token rows per wave load
-  constexpr int NL = BS / TPL;   // rows per lane per block
-  static_assert(D % CE == 0 && 64 % LPT == 0 && BS % TPL == 0, "unsupported tile shape");
+  // A wave load of TPL rows spans UB blocks: 1, or 2 for 8-bit D = 64 rows
+  // (16 per load) in 8-token blocks.  Then each load goes out once per
+  // block, the other block's lanes out of range (they read zeros), and the
+  // results are merged.
+  constexpr int UB = TPL > BS ? TPL / BS : 1;
+  constexpr int NL = UB > 1 ? 1 : BS / TPL;  // rows per lane per unit of UB blocks
+  static_assert(D % CE == 0 && 64 % LPT == 0 && (UB > 1 ? TPL == UB * BS : BS % TPL == 0),
+                "unsupported tile shape");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -197,8 +203,9 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
 
   const uint32_t row_stride = static_cast<uint32_t>(p.Hkv) * D * KVB;  // bytes between token rows
   const uint32_t blk_bytes = row_stride * BS;
-  // this lane's chunk of row tg of a block, relative to the block's start
-  const int lane_off = static_cast<int>(g * D * KVB + c * 16 + tg * row_stride);
+  // this lane's chunk of row tg of a block (row tg % BS of block tg / BS
+  // when a load spans blocks), relative to that block's start
+  const int lane_off = static_cast<int>(g * D * KVB + c * 16 + (UB > 1 ? tg % BS : tg) * row_stride);
   const char* kpool = static_cast<const char*>(p.k_cache);
   const char* vpool = static_cast<const char*>(p.v_cache);
   // score scale in log2 units and V scale of this wave's KV head
@@ -209,8 +216,30 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
     Chunk k[NL], v[NL];
   };
 
-  // Loads of block id blk (nothing is read for blk < 0).
-  auto load = [&](const int (&id)[1], Buf& r) {
+  // Loads of the unit's blocks (nothing is read for an id < 0).
+  auto load = [&](const int (&id)[UB], Buf& r) {
+    if constexpr (UB > 1) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) r.k[0].w[w] = r.v[0].w[w] = 0u;
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int blk = id[u];
+        const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
+        const uint32_t n = blk < 0 ? 0u : blk_bytes;
+        const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + off, n);
+        const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + off, n);
+        const int o = tg / BS == u ? lane_off : 0x7fffff00;
+        Chunk a, b;
+        buffer_load<4>(kr, o, 0, a.w);
+        buffer_load<4>(vr, o, 0, b.w);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          r.k[0].w[w] |= a.w[w];
+          r.v[0].w[w] |= b.w[w];
+        }
+      }
+      return;
+    }
     const int blk = id[0];
     const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
     const uint32_t n = blk < 0 ? 0u : blk_bytes;
@@ -242,8 +271,15 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
 
     auto consume = [&](int j, unsigned ok, const Buf& r) {
       // valid rows of this block (only the last block of a sequence is
-      // partial; a block id outside the pool counts none)
-      const int valid = ok ? min(BS, span.L - j * BS) : 0;
+      // partial; a block id outside the pool counts none).  A unit of two
+      // blocks: this lane's row tg is row tg % BS of block j + tg / BS.
+      int valid;
+      if constexpr (UB > 1) {
+        const int u = tg / BS;
+        valid = ((ok >> u) & 1u) && (j + u) * BS + tg % BS < span.L ? TPL : 0;
+      } else {
+        valid = ok ? min(BS, span.L - j * BS) : 0;
+      }
       float s[NL][G];
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
@@ -289,7 +325,7 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
 
     const int32_t* table =
         p.block_tables + static_cast<size_t>(b) * (p.max_blocks_per_seq >> p.sub_shift);
-    walk_blocks<ST, 1, Buf>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
+    walk_blocks<ST, UB, Buf>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
 
     // merge the per-lane states of the TPL row groups that own the same
     // chunk; the butterfly leaves the merged state in every lane
@@ -366,11 +402,7 @@ bool by_group(const DecodeParams& p, F&& f) {
 template <int KV, int Q, int D, typename F>
 bool by_block(const DecodeParams& p, F&& f) {
   switch (p.block_size) {
-    case 8:
-      // a wave load of TPL rows must lie in one block: not so for 8-bit
-      // caches at D = 64 (16 rows per load)
-      if constexpr (8 % (64 * Ops<KV, Q>::CE / D) == 0) return by_group<KV, Q, D, 8>(p, f);
-      return false;
+    case 8: return by_group<KV, Q, D, 8>(p, f);
     case 16: return by_group<KV, Q, D, 16>(p, f);
     case 32: return by_group<KV, Q, D, 32>(p, f);
     default: return false;

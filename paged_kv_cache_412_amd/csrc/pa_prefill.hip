@@ -190,7 +190,11 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   // fills before the barrier that ends the iteration.  8-bit K/V are loaded
   // into registers and widened to the 16-bit operand type on their way to LDS.
   constexpr int TB = kKeys / BS > 0 ? kKeys / BS : 1;  // blocks per key tile
-  static_assert(WROWS <= BS && BS % WROWS == 0, "a wave load's rows in one block");
+  // blocks one wave load spans: 1, or 2 for 8-bit D = 64 rows (16 per load)
+  // in 8-token blocks, loaded once per block with the other block's lanes
+  // out of range (zeros) and the two results merged
+  constexpr int LB = WROWS > BS ? WROWS / BS : 1;
+  static_assert(LB == 1 ? BS % WROWS == 0 : (KVB == 1 && WROWS == LB * BS), "a wave load's rows");
   constexpr bool ONE_BLOCK = BS >= WR;                  // all of a wave's rows in one block
   static_assert(KVB != 2 || WROWS * ROWB == 1024, "one LDS fill per wave and pass");
   const int64_t row_stride = static_cast<int64_t>(p.Hkv) * D * KVB;
@@ -237,10 +241,21 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int row0 = wv * WR + ps * WROWS;          // first row of this wave load
-      if constexpr (!ONE_BLOCK) block_of(row0);
+      if constexpr (!ONE_BLOCK && LB == 1) block_of(row0);
       // rows past the last key read zeros (an offset past the end)
       const int voff = lane_row + ps * WROWS < n_keys - j * kKeys ? lane_off[ps] : 0x7fffff00;
-      if constexpr (KVB == 2) {
+      if constexpr (LB > 1) {
+        u32x4 ka = {0u, 0u, 0u, 0u}, va = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int h = 0; h < LB; ++h) {
+          block_of(row0 + h * BS);
+          const int o = srow / BS == h ? voff : 0x7fffff00;
+          ka |= __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, o, 0, 0));
+          va |= __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, o, 0, 0));
+        }
+        kst[ps] = ka;
+        vst[ps] = va;
+      } else if constexpr (KVB == 2) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             kr, (__attribute__((address_space(3))) void*)(lds[buf][0] + row0 * ROWB), 16, voff, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -461,14 +476,7 @@ template <int KV, int Q, int D, typename F>
 bool by_block(int32_t bs, int32_t G, F&& f) {
   if (G < 1 || G > 16) return false;
   switch (bs) {
-    case 8:
-      // the rows one wave stages per pass must lie in one block: 64 / (16-byte
-      // chunks per row) rows, 16 for 8-bit caches at D = 64
-      if constexpr (D * Elem<KV>::bytes >= 128) {
-        f(Tag<KV, Q, D, 8>{});
-        return true;
-      }
-      return false;
+    case 8: f(Tag<KV, Q, D, 8>{}); return true;
     case 16: f(Tag<KV, Q, D, 16>{}); return true;
     case 32: f(Tag<KV, Q, D, 32>{}); return true;
     case 64: f(Tag<KV, Q, D, 64>{}); return true;

@@ -112,9 +112,7 @@ def test_decode_check_block_sizes(L):
                     sc = 1.0 if kv == P.PA_F16 else 0.5
                     st = check(L, block_size=bs, D=D, Hq=2 * G, Hkv=2, q_dtype=P.PA_F16, kv_dtype=kv,
                                out_dtype=P.PA_F16, k_scale=sc, v_scale=sc)
-                    # the one gap: 8-bit caches at D = 64 in 8-token blocks on the vector ALU
-                    want = 3 if (bs == 8 and D == 64 and kv == P.PA_FP8_E4M3 and G <= 2) else 0
-                    assert st == want, (bs, D, G, kv)
+                    assert st == 0, (bs, D, G, kv)
     # partitions are whole blocks
     assert check(L, block_size=64, partition_size=64, max_blocks_per_seq=16) == 0
     assert check(L, block_size=64, partition_size=32) == 2
@@ -238,9 +236,7 @@ def test_prefill_check_accepts_supported_combinations(L):
         for out in (q, P.PA_F32):
             for D in (64, 128):
                 for bs in (8, 16, 32, 64):
-                    # rows a wave stages must lie in one block: not so for
-                    # 8-bit caches at D = 64 in 8-token blocks
-                    want = 3 if (bs == 8 and D == 64 and kv in (P.PA_FP8_E4M3, P.PA_FP8_E5M2)) else 0
+                    want = 0
                     for Hq in (2, 4, 8, 16):
                         assert pcheck(L, q_dtype=q, kv_dtype=kv, out_dtype=out, D=D, block_size=bs,
                                       Hq=Hq) == want, (q, kv, out, D, bs, Hq)

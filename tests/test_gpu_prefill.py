@@ -91,8 +91,6 @@ def test_prefill_small_all_rows(name):
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 16])
 def test_prefill_every_supported_shape(pair, D, bs, G):
     q, kv = pair
-    if bs == 8 and D == 64 and kv in ("e4m3", "e5m2"):
-        pytest.skip("not built: a wave stages 16 rows of an 8-bit D = 64 cache, more than a block")
     cfg = cfg_of("prefill70b", name=f"shape_{q}_{kv}_{D}_{bs}_{G}", B=2, Hq=2 * G, Hkv=2, D=D,
                  block_size=bs, kv_dtype=kv, q_dtype=q, out_dtype=q, src_dtype=q,
                  prefill=dict(new=(1, 150), ctx=(0, 90)))
