@@ -144,16 +144,23 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p
     for (int i = tid; i < cn; i += nt) w_lds[i] = fast_exp2(p.ws_m[row(c0 + i)] - M);
     __syncthreads();
     if (tid < p.D) {
+      // the loads of 16 rows go out together, then the same in-order chain
+      // of fused multiply-adds
+      constexpr int U = 16;
       int i = 0;
+      for (; i + U <= cn; i += U) {
+        float a[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) a[k] = p.ws_acc[row(c0 + i + k) * p.D + tid];
+#pragma unroll
+        for (int k = 0; k < U; ++k) A = __builtin_fmaf(a[k], w_lds[i + k], A);
+      }
       for (; i + 4 <= cn; i += 4) {
-        const float a0 = p.ws_acc[row(c0 + i) * p.D + tid];
-        const float a1 = p.ws_acc[row(c0 + i + 1) * p.D + tid];
-        const float a2 = p.ws_acc[row(c0 + i + 2) * p.D + tid];
-        const float a3 = p.ws_acc[row(c0 + i + 3) * p.D + tid];
-        A = __builtin_fmaf(a0, w_lds[i], A);
-        A = __builtin_fmaf(a1, w_lds[i + 1], A);
-        A = __builtin_fmaf(a2, w_lds[i + 2], A);
-        A = __builtin_fmaf(a3, w_lds[i + 3], A);
+        float a[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = p.ws_acc[row(c0 + i + k) * p.D + tid];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) A = __builtin_fmaf(a[k], w_lds[i + k], A);
       }
       for (; i < cn; ++i) A = __builtin_fmaf(p.ws_acc[row(c0 + i) * p.D + tid], w_lds[i], A);
     }

@@ -157,6 +157,12 @@ CONFIGS = {
     "prefill70b": Config("prefill70b", 8, B=16, Hq=64, Hkv=8, D=128, block_size=16, kv_dtype=BF16,
                          q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
                          prefill=dict(new=(1024, 1024), ctx=(0, 3072))),
+    "prefill70b_bs8": Config("prefill70b_bs8", 18, B=16, Hq=64, Hkv=8, D=128, block_size=8,
+                             kv_dtype=BF16, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
+                             prefill=dict(new=(1024, 1024), ctx=(0, 3072))),
+    "prefill70b_bs64": Config("prefill70b_bs64", 19, B=16, Hq=64, Hkv=8, D=128, block_size=64,
+                              kv_dtype=BF16, q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
+                              prefill=dict(new=(1024, 1024), ctx=(0, 3072))),
     "prefill_fp8": Config("prefill_fp8", 9, B=8, Hq=32, Hkv=8, D=128, block_size=16, kv_dtype=E4M3,
                           q_dtype=BF16, out_dtype=BF16, src_dtype=BF16,
                           prefill=dict(new=(2048, 2048), ctx=(0, 6144))),
