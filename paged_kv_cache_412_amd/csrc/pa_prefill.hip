@@ -74,13 +74,32 @@ __device__ __forceinline__ float vmax(float a, float b) { return __builtin_eleme
 // XCD-aware order: the hardware deals consecutive work-groups round-robin to
 // the 8 XCDs, each with its own L2.  Map hardware index i to a logical index
 // so that each XCD receives one contiguous run of logical work-groups: the
-// query tiles of one (sequence, KV head), which read the same K/V, then share
-// an L2.  A bijection on [0, n).
+// query tiles of one (sequence, KV head), which read the same K/V, then run
+// close together on one XCD and share its L2.  A bijection on [0, n).
 __device__ __forceinline__ int xcd_logical(int i, int n) {
   constexpr int X = 8;
   const int q = n / X, r = n % X;
   const int x = i % X, k = i / X;
   return x * q + min(x, r) + k;
+}
+
+// Inverse of xcd_logical: contiguous index c -> the round-robin index whose
+// logical image is c.  Applied to the (sequence, KV head) index, it deals
+// those pairs to the XCDs in turn, so every XCD's run mixes all sequences:
+// runs of whole sequences left the XCDs with unequal work when context
+// lengths differ (the kernel then waits for the slowest XCD).
+__device__ __forceinline__ int xcd_round_robin(int c, int n) {
+  constexpr int X = 8;
+  const int q = n / X, r = n % X;
+  int x, k;
+  if (c < r * (q + 1)) {
+    x = c / (q + 1);
+    k = c % (q + 1);
+  } else {
+    x = r + (c - r * (q + 1)) / q;
+    k = (c - r * (q + 1)) % q;
+  }
+  return k * X + x;
 }
 
 template <int KV, int Q, int D, int BS>
@@ -124,7 +143,8 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   // ---- which (sequence, KV head, query tile); heavy (late) tiles first
   const int logical = xcd_logical(blockIdx.x, p.total_groups);
   const int qt = p.q_tiles - 1 - logical % p.q_tiles;
-  const int bh = logical / p.q_tiles;
+  const int nbh = p.total_groups / p.q_tiles;
+  const int bh = xcd_round_robin(logical / p.q_tiles, nbh);
   const int kvh = bh % p.Hkv;
   const int b = bh / p.Hkv;
 
