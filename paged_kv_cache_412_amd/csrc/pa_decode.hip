@@ -18,27 +18,6 @@
 
 namespace pa {
 
-// Partitions whose weights one pass of the reduce stages in LDS.
-constexpr int kReduceChunk = 256;
-
-// Block-wide reduction (max or sum) of one value per thread; blockDim.x is a
-// multiple of 64 and at most 256.  Every thread receives the result.
-template <bool MAX>
-__device__ __forceinline__ float block_reduce(float v, float* lds4) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(v, off, 64);
-    v = MAX ? fmaxf(v, o) : v + o;
-  }
-  const int nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = lds4[0];
-  for (int w = 1; w < nw; ++w) v = MAX ? fmaxf(v, lds4[w]) : v + lds4[w];
-  return v;
-}
-
 // ------------------------------------------------------------------ plan
 
 // Balanced schedule, step 0: prefix[b] = sum over b' < b of the number of
@@ -74,34 +53,67 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeP
 
 // ------------------------------------------------------------------ reduce
 
-// One work-group of D threads per (query head, sequence); thread d owns
-// output element d.  The partials of the sequence are rows row(0..n-1): for
-// the fixed schedule its partitions, for the balanced schedule the
-// work-groups whose ranges overlap it.  The weights 2^(m_i - M) are computed
-// once per row and shared through LDS, so the per-element loop is one fused
-// multiply-add and one coalesced load per row.
-template <bool BALANCED>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p) {
-  __shared__ float w_lds[kReduceChunk];
-  __shared__ float red[4];
-  const int hq = blockIdx.x;
+// Waves of the reduce kernel per work-group; wave k of work-group x serves
+// query head 4x + k.
+constexpr int kReduceWaves = 4;
+
+// Maximum over the 64 lanes of a wave; every lane receives it.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+// Value of v in lane i (i wave-uniform).
+__device__ __forceinline__ float lane_value(float v, int i) {
+  return u2f(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(f2u(v)), i)));
+}
+
+// Combines the partials of one (query head, sequence): output elements
+// l + 64e (e < E = D / 64) belong to lane l.  The partials are rows
+// row(0..n-1): for the fixed schedule the sequence's partitions, for the
+// balanced schedule the work-groups whose ranges overlap it.
+//
+// WPH waves serve one head.  WPH = 1: wave k of work-group x serves query
+// head 4x + k and all its rows.  WPH = 4 (sequences split into many rows):
+// the work-group serves head x, and wave k takes rows [k n/4, (k+1) n/4).
+// Every wave holds the running max and sum of row i in lane i (for each
+// chunk of 64 rows), so the common maximum and the rescaled sum are wave
+// reductions; the weights 2^(m_i - M) stay in the lane of their row and
+// reach the others with v_readlane.  Each wave's weighted sum is one in-order
+// chain of fused multiply-adds over its rows, whose loads go out 16 rows at a
+// time (a short batch repeats its last row's loads and skips their FMAs, so
+// any batch is one round trip); with WPH = 4 the four sums are added in wave
+// order through LDS.
+template <bool BALANCED, int E, int WPH>
+__global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(const DecodeParams p) {
+  static_assert(WPH == 1 || WPH == kReduceWaves, "one wave or the whole work-group per head");
+  __shared__ float part[WPH == 1 ? 1 : kReduceWaves - 1][E * 64];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int hq = WPH == 1 ? blockIdx.x * kReduceWaves + wid : blockIdx.x;
   const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int nt = blockDim.x;
+  if (hq >= p.Hq) return;  // wave-uniform (WPH = 1 only: the grid covers Hq exactly otherwise)
   const size_t orow = static_cast<size_t>(b) * p.Hq + hq;
+  const bool writer = WPH == 1 || wid == 0;
 
   int n;                  // partial rows of this (sequence, head)
   size_t row0 = 0;        // fixed: row of partition 0; rows step by B*Hq
   int w0 = 0, hg = 0, wave = 0, q = 0;
-  int64_t F = 0;
   bool first_is_second_slot = false;
   if constexpr (BALANCED) {
     const int64_t pb = p.prefix[b], pn = p.prefix[b + 1];
     if (pn == pb) {  // no tokens: zeros (no work-group touched this sequence)
-      for (int d = tid; d < p.D; d += nt) store_out(p.out, orow * p.D + d, 0.f, p.out_dtype);
+      if (writer) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) store_out(p.out, orow * p.D + lane + 64 * e, 0.f, p.out_dtype);
+      }
       return;
     }
-    F = p.prefix[p.B];
+    const int64_t F = p.prefix[p.B];
     const int ng = balanced_groups(p, F);  // F >= 1 here
     w0 = balanced_owner(F, pb, ng);
     const int w1 = balanced_owner(F, pn - 1, ng);
@@ -120,52 +132,80 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p
     n = (L + p.partition_size - 1) / p.partition_size;
     row0 = ws_row(p, orow, 0);
   }
+  // every early return above is uniform over the work-group when WPH > 1
   auto row = [&](int i) -> size_t {
     if constexpr (BALANCED)
       return balanced_row(p, hg, w0 + i, (i == 0 && first_is_second_slot) ? 1 : 0, wave, q);
     else
       return row0 + static_cast<size_t>(i) * (static_cast<size_t>(p.B) * p.Hq);
   };
+  const int r0 = WPH == 1 ? 0 : wid * n / WPH;        // this wave's rows
+  const int r1 = WPH == 1 ? n : (wid + 1) * n / WPH;
 
-  float M = kMaxInit;
-  for (int i = tid; i < n; i += nt) M = fmaxf(M, p.ws_m[row(i)]);
-  M = block_reduce<true>(M, red);
-  float Ls = 0.f;
-  for (int i = tid; i < n; i += nt) {
-    const size_t r = row(i);
-    Ls += p.ws_l[r] * fast_exp2(p.ws_m[r] - M);
+  // rows 0..63 stay in their lanes; later chunks are read again below
+  float m0 = kMaxInit, l0 = 0.f;
+  if (lane < n) {
+    const size_t r = row(lane);
+    m0 = p.ws_m[r];
+    l0 = p.ws_l[r];
   }
-  Ls = block_reduce<false>(Ls, red);
+  float M = m0;
+  for (int i = lane + 64; i < n; i += 64) M = fmaxf(M, p.ws_m[row(i)]);
+  M = wave_max(M);
 
-  float A = 0.f;
-  for (int c0 = 0; c0 < n; c0 += kReduceChunk) {
-    const int cn = min(kReduceChunk, n - c0);
-    __syncthreads();
-    for (int i = tid; i < cn; i += nt) w_lds[i] = fast_exp2(p.ws_m[row(c0 + i)] - M);
-    __syncthreads();
-    if (tid < p.D) {
-      // the loads of 16 rows go out together, then the same in-order chain
-      // of fused multiply-adds
-      constexpr int U = 16;
-      int i = 0;
-      for (; i + U <= cn; i += U) {
-        float a[U];
+  float A[E];
 #pragma unroll
-        for (int k = 0; k < U; ++k) a[k] = p.ws_acc[row(c0 + i + k) * p.D + tid];
+  for (int e = 0; e < E; ++e) A[e] = 0.f;
+  float Ls = 0.f;  // this lane's rows' share of sum_i l_i 2^(m_i - M)
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int cn = min(64, n - c0);
+    float wl = 0.f;  // weight of row c0 + lane
+    if (c0 == 0) {
+      if (lane < cn) wl = fast_exp2(m0 - M);
+      Ls += l0 * wl;
+    } else if (lane < cn) {
+      const size_t r = row(c0 + lane);
+      wl = fast_exp2(p.ws_m[r] - M);
+      Ls += p.ws_l[r] * wl;
+    }
+    const int i_end = min(r1, c0 + cn) - c0;  // this wave's rows within the chunk
+    constexpr int U = 16;
+    for (int i = max(r0, c0) - c0; i < i_end; i += U) {
+      const int cnt = min(U, i_end - i);
+      float a[U][E];
 #pragma unroll
-        for (int k = 0; k < U; ++k) A = __builtin_fmaf(a[k], w_lds[i + k], A);
+      for (int k = 0; k < U; ++k) {
+        const float* src = p.ws_acc + row(c0 + i + min(k, cnt - 1)) * p.D + lane;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[k][e] = src[64 * e];
       }
-      for (; i + 4 <= cn; i += 4) {
-        float a[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) a[k] = p.ws_acc[row(c0 + i + k) * p.D + tid];
+      for (int k = 0; k < U; ++k) {
+        if (k < cnt) {
+          const float w = lane_value(wl, i + k);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) A = __builtin_fmaf(a[k], w_lds[i + k], A);
+          for (int e = 0; e < E; ++e) A[e] = __builtin_fmaf(a[k][e], w, A[e]);
+        }
       }
-      for (; i < cn; ++i) A = __builtin_fmaf(p.ws_acc[row(c0 + i) * p.D + tid], w_lds[i], A);
     }
   }
-  if (tid < p.D) store_out(p.out, orow * p.D + tid, Ls > 0.f ? A / Ls : 0.f, p.out_dtype);
+  Ls = group_sum<64>(Ls);
+  if constexpr (WPH > 1) {
+    if (wid > 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) part[wid - 1][lane + 64 * e] = A[e];
+    }
+    __syncthreads();
+    if (wid > 0) return;
+#pragma unroll
+    for (int w = 0; w < WPH - 1; ++w) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) A[e] += part[w][lane + 64 * e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    store_out(p.out, orow * p.D + lane + 64 * e, Ls > 0.f ? A[e] / Ls : 0.f, p.out_dtype);
 }
 
 // ------------------------------------------------------------------ host side
@@ -196,13 +236,33 @@ hipError_t launch_decode_partition(const DecodeParams& p, pa_dtype q_dtype, pa_d
   return launch_decode_valu(p, q_dtype, kv_dtype, stream, supported);
 }
 
-hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.Hq, p.B);
-  const int threads = (p.D + 63) / 64 * 64;
-  if (p.balanced)
-    hipLaunchKernelGGL(decode_reduce_kernel<true>, grid, dim3(threads), 0, stream, p);
+template <bool BALANCED, int E>
+static void launch_reduce_as(const DecodeParams& p, bool split, hipStream_t stream) {
+  const dim3 block(64 * kReduceWaves);
+  if (split)
+    hipLaunchKernelGGL((decode_reduce_kernel<BALANCED, E, kReduceWaves>), dim3(p.Hq, p.B), block,
+                       0, stream, p);
   else
-    hipLaunchKernelGGL(decode_reduce_kernel<false>, grid, dim3(threads), 0, stream, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<BALANCED, E, 1>),
+                       dim3((p.Hq + kReduceWaves - 1) / kReduceWaves, p.B), block, 0, stream, p);
+}
+
+hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {
+  if (p.D != 64 && p.D != 128) return hipErrorInvalidValue;
+  // Expected partial rows per sequence: balanced, about groups / B + 1 (a
+  // sequence's share of the work-groups plus the one it starts in); fixed,
+  // the partitions of the longest possible sequence.  Past 16 rows the
+  // work-group's four waves split one head's rows.
+  const int64_t rows = p.balanced ? static_cast<int64_t>(p.groups) / (p.B > 0 ? p.B : 1) + 1
+                                  : p.num_partitions;
+  const bool split = rows > 16;
+  if (p.balanced) {
+    if (p.D == 64) launch_reduce_as<true, 1>(p, split, stream);
+    else launch_reduce_as<true, 2>(p, split, stream);
+  } else {
+    if (p.D == 64) launch_reduce_as<false, 1>(p, split, stream);
+    else launch_reduce_as<false, 2>(p, split, stream);
+  }
   return hipGetLastError();
 }
 
