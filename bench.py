@@ -101,17 +101,33 @@ def prefill_bytes(wl) -> int:
     return kv + wl.T * c.Hq * c.D * (ELEM_BYTES[c.q_dtype] + ELEM_BYTES[c.out_dtype])
 
 
+def _counter_record(kernel: str, workload: str) -> dict:
+    """The committed PMC counter record of this kernel and workload, if it was
+    taken on the current kernel source; else {}."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path, encoding="utf-8") as f:
+        rec = json.load(f)
+    return rec if rec.get("kernel_hash") == kernel_hash(kernel) else {}
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed PMC counter runs, if they were taken
     on the current kernel source."""
-    path = os.path.join(TRAFFIC_DIR, f"traffic_{kernel}_{workload}.json")
-    if not os.path.exists(path):
+    return _counter_record(kernel, workload).get("hbm_bytes_per_launch")
+
+
+def measured_mfma(kernel: str, workload: str):
+    """Matrix-core counters per launch (busy percent of SIMD cycles, flops
+    issued, and those over the algorithmic flops) from committed PMC runs on
+    the current kernel source, or None."""
+    rec = _counter_record(kernel, workload)
+    if "mfma_util_pct" not in rec:
         return None
-    with open(path, encoding="utf-8") as f:
-        rec = json.load(f)
-    if rec.get("kernel_hash") != kernel_hash(kernel):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    return {"busy_pct": round(rec["mfma_util_pct"], 1),
+            "issued_flops": rec["mfma_flops_per_launch"],
+            "issued_over_algorithmic": round(rec["mfma_flops_per_launch"] / rec["algorithmic_flops"], 3)}
 
 
 def copy_calibration():
@@ -263,7 +279,8 @@ def bench_prefill(args, cfg):
         "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(kernel, cfg.name),
-                     "algorithmic_bytes": prefill_bytes(wl), "avg_launch_ms": round(attn_ms, 5)},
+                     "algorithmic_bytes": prefill_bytes(wl), "avg_launch_ms": round(attn_ms, 5),
+                     "mfma": measured_mfma(kernel, cfg.name)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -579,7 +596,8 @@ def main(argv=None):
                      "traffic": traffic, "algorithmic_bytes": nbytes, "avg_launch_ms": round(part_ms, 5),
                      "launch_scope": ("pa_decode_partition call: plan kernel, then the attention kernel"
                                       if partition == 0 and cfg.B > INLINE_PLAN_MAX_B
-                                      else "pa_decode_partition call: the attention kernel")},
+                                      else "pa_decode_partition call: the attention kernel"),
+                     "mfma": measured_mfma(kernel, cfg.name)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
