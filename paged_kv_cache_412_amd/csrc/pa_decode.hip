@@ -53,8 +53,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeP
 
 // ------------------------------------------------------------------ reduce
 
-// Waves of the reduce kernel per work-group; wave k of work-group x serves
-// query head 4x + k.
+// Waves of the reduce kernel per work-group (one head each, or all four on
+// one head's rows; see below).
 constexpr int kReduceWaves = 4;
 
 // Maximum over the 64 lanes of a wave; every lane receives it.
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(const 
   const int wid = threadIdx.x >> 6;
   const int hq = WPH == 1 ? blockIdx.x * kReduceWaves + wid : blockIdx.x;
   const int b = blockIdx.y;
-  if (hq >= p.Hq) return;  // wave-uniform (WPH = 1 only: the grid covers Hq exactly otherwise)
+  if (hq >= p.Hq) return;  // wave-uniform; only with WPH = 1 (grid x = Hq otherwise)
   const size_t orow = static_cast<size_t>(b) * p.Hq + hq;
   const bool writer = WPH == 1 || wid == 0;
 
