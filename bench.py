@@ -304,7 +304,6 @@ def bench_swap(args, cfg):
     two pa_swap_blocks calls.  Bytes move over the host link both ways."""
     import torch
 
-    from oracle import paged
     from paged_kv_cache_412_amd import binding, workloads
 
     print(f"[bench] building swap workload {cfg.name}", file=sys.stderr, flush=True)
@@ -379,6 +378,7 @@ def bench_swap(args, cfg):
                      "avg_launch_ms": {"evict": round(out_ms, 5), "restore": round(in_ms, 5)}},
     }
     if not args.no_cpu_baseline:
+        from oracle import paged
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         kd = parity_storage(wl.k_dev)
         kh = parity_storage(wl.k_host)
@@ -427,7 +427,6 @@ def replay(manager, ops, budget_s=None, on_add=None):
 def bench_stream(args, cfg):
     """Block-manager workloads: the library's native manager replays a
     seeded continuous-batching request stream (host code; no GPU kernel)."""
-    from oracle import prefix_cache as opc
     from paged_kv_cache_412_amd import binding, workloads
 
     print(f"[bench] building request stream {cfg.name}", file=sys.stderr, flush=True)
@@ -475,6 +474,7 @@ def bench_stream(args, cfg):
         "roofline": None,
     }
     if not args.no_cpu_baseline:
+        from oracle import prefix_cache as opc
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         o = opc.PrefixCache(NB, cfg.block_size, caching=True)
         done, odt, _ = replay(o, ops, budget_s=min(args.cpu_budget, 10.0))
