@@ -130,6 +130,52 @@ def measured_mfma(kernel: str, workload: str):
             "issued_over_algorithmic": round(rec["mfma_flops_per_launch"] / rec["algorithmic_flops"], 3)}
 
 
+def read_ceiling(args):
+    """The practical HBM read rate of a block gather on this part: a 4 GiB
+    pool read whole, piece by piece in a seeded random order, through
+    pa_read_blocks (the attention kernels' non-temporal 16-byte buffer
+    loads), for pieces of 1 to 32 KiB; beside it, torch's own device copy
+    (bytes read plus bytes written per second).  Prints one JSON line."""
+    import torch
+
+    from paged_kv_cache_412_amd import binding
+    total = 4 << 30
+    pool = torch.empty(total, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    reps = max(3, args.steps // 5)
+    res = {}
+    for kib in (1, 2, 4, 8, 16, 32):
+        piece = kib << 10
+        ids = torch.from_numpy(np.random.default_rng(412).permutation(total // piece).astype(np.int32)).cuda()
+        for _ in range(2):
+            binding.read_blocks(pool, piece, ids, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            binding.read_blocks(pool, piece, ids, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[f"{kib}KiB"] = round(total / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+    del pool
+    src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    print(json.dumps({"read_ceiling_gbs": res, "pool_bytes": total, "reps": reps,
+                      "torch_copy_gbs_read_plus_write": round(copy_gbs, 1),
+                      "peak_gbs": HBM_PEAK_GBS}), flush=True)
+    return 0
+
+
 def copy_calibration():
     """A plain device-to-device copy of CALIBRATION_BYTES, three times: the
     reference the PMC byte counters are scaled by."""
@@ -500,6 +546,8 @@ def main(argv=None):
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="measure the block-gather read ceiling and torch's copy rate, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy the PMC byte counters are scaled by")
     args = ap.parse_args(argv)
@@ -519,6 +567,8 @@ def main(argv=None):
         return 2
     if args.copy_calibration:
         return copy_calibration()
+    if args.read_ceiling:
+        return read_ceiling(args)
     if workloads.CONFIGS[args.workload].stream:
         return bench_stream(args, workloads.CONFIGS[args.workload])
     binding.lib()

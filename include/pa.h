@@ -395,6 +395,20 @@ int32_t pa_bm_length(const pa_block_manager* m, int32_t seq);
 int32_t pa_bm_free_blocks(const pa_block_manager* m);
 int32_t pa_bm_cached_blocks(const pa_block_manager* m);
 
+/* Measurement utility, not a step of the path (the pages define no such
+ * operation): reads pieces ids[0..n) of `pool` (num_pieces pieces of
+ * piece_bytes each, a multiple of 1024 up to 32768, pool 16-byte aligned,
+ * device memory) in that order, with the non-temporal 16-byte buffer loads
+ * of the attention kernels, and folds every loaded word into sink (uint32
+ * [sink_len], device), one word per work-group, so that no load is dead.
+ * Ids outside [0, num_pieces) read nothing.  Timed over pieces of a block's
+ * size in random order it gives the practical HBM read rate of a block
+ * gather: the ceiling the attention kernels are measured against beside the
+ * vendor peak.  Launches min(sink_len, 8 * compute units) work-groups. */
+pa_status pa_read_blocks(const void* pool, int32_t num_pieces, size_t piece_bytes,
+                         const int32_t* ids, int32_t n, uint32_t* sink, int32_t sink_len,
+                         void* stream);
+
 /* Static description of a status code. */
 const char* pa_status_str(pa_status s);
 

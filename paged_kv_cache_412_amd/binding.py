@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_workspace_size.restype = ctypes.c_size_t
     L.pa_decode_partition_size.argtypes = [argp]
     L.pa_decode_partition_size.restype = ctypes.c_int32
+    L.pa_read_blocks.argtypes = [vp, i32, ctypes.c_size_t, vp, i32, vp, i32, vp]
+    L.pa_read_blocks.restype = ctypes.c_int
     for name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce"):
         getattr(L, name).argtypes = [argp, vp]
         getattr(L, name).restype = ctypes.c_int
@@ -524,3 +526,16 @@ class BlockManager:
 
     def cached_blocks(self) -> int:
         return int(self._lib.pa_bm_cached_blocks(self._h))
+
+
+def read_blocks(pool, piece_bytes, ids, sink, stream=None):
+    """pa_read_blocks: read pieces ``ids`` of ``pool`` (a flat uint8 tensor of
+    whole pieces) into the fold ``sink`` (int32); a measurement utility."""
+    _require(pool, "pool", torch.uint8, 1)
+    _require(ids, "ids", torch.int32, 1)
+    _require(sink, "sink", torch.int32, 1)
+    if pool.numel() % piece_bytes:
+        raise ValueError("the pool must hold whole pieces")
+    _check(lib().pa_read_blocks(_ptr(pool), pool.numel() // piece_bytes, piece_bytes, _ptr(ids),
+                                ids.shape[0], _ptr(sink), sink.shape[0], _stream(stream)),
+           "pa_read_blocks")

@@ -323,3 +323,14 @@ def test_per_head_scales_validation(L):
     assert f(*args[:5], 0, *args[6:]) == 0                                         # T = 0
     assert f(*args[:5], -1, *args[6:]) == 2
     del k
+
+
+def test_read_blocks_rejections(L):
+    # the measurement utility: every case returns before anything is launched
+    def call(pool=FAKE, npieces=64, piece=16384, ids=FAKE + (1 << 28), n=8, sink=FAKE + (1 << 29), slen=16):
+        return L.pa_read_blocks(pool, npieces, piece, ids, n, sink, slen, None)
+    assert call(n=-1) == 2 and call(npieces=0) == 2 and call(slen=0) == 2
+    assert call(piece=512) == 2 and call(piece=1024 + 16) == 2 and call(piece=32768 + 1024) == 2
+    assert call(n=0, pool=None, ids=None, sink=None) == 0          # nothing to read
+    assert call(pool=None) == 1 and call(ids=None) == 1 and call(sink=None) == 1
+    assert call(pool=FAKE + 8) == 2                                 # misaligned
