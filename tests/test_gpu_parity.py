@@ -511,3 +511,23 @@ def test_slot_mapping_matches_the_oracle():
         binding.slot_mapping(torch.from_numpy(tables).cuda(), torch.from_numpy(pos).cuda(), bs, slots)
         torch.cuda.synchronize()
         assert np.array_equal(slots.cpu().numpy(), exp), bs
+
+
+@pytest.mark.parametrize("B", [1025, 3000])
+@pytest.mark.parametrize("pair,G,bs", [(("f16", "f16"), 1, 16), (("bf16", "bf16"), 8, 64),
+                                      (("bf16", "e4m3"), 4, 8), (("f32", "f32"), 2, 32)])
+@pytest.mark.parametrize("part", [0, 32])
+def test_batches_past_the_inline_plan(B, pair, G, bs, part):
+    """More than 1024 sequences: the balanced schedule's block-count prefix
+    sums come from the plan kernel (global memory) instead of each
+    work-group's own pass in LDS; the fixed schedule's grid spans them all."""
+    qd, kvd = pair
+    if part % bs:
+        part = bs
+    lens = tuple(int(x) for x in np.random.default_rng(B + G).integers(0, 70, B))
+    cfg = workloads.Config(f"bigB-{B}-{qd}-{kvd}-G{G}-bs{bs}", 9, B=B, Hq=2 * G, Hkv=2, D=64,
+                           block_size=bs, kv_dtype=kvd, q_dtype=qd, out_dtype="f32", src_dtype=qd,
+                           lens=lens)
+    wl, step, exp = run_step(cfg, partition_size=part, out_dtype="f32")
+    err = check_step(wl, step, exp, out_dtype="f32")
+    print(f"[ok] B={B} {qd}/{kvd} G={G} bs={bs} part={part} max abs err {err:.3e}", flush=True)
