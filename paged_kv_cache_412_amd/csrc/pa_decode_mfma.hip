@@ -267,12 +267,14 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
       for (int tt = 0; tt < TT; ++tt) {
         float pw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pw[i] = fast_exp2(sc[tt][i] - m_run);
-          l_part += pw[i];
-        }
+        for (int i = 0; i < 4; ++i) pw[i] = fast_exp2(sc[tt][i] - m_run);
         const uint32_t pa0 = M::pack2(pw[0], pw[1]);
         const uint32_t pa1 = M::pack2(pw[2], pw[3]);
+        // the running sum takes the weights as the weighted sum uses them,
+        // rounded to the operand type: the output is then an exact weighted
+        // mean of V rows (the fp32 weights would scale it by up to a
+        // half-ulp of that type)
+        l_part += M::pair_sum(pa0) + M::pair_sum(pa1);
         if (vmask[tt] != 0xffffu) {
           // zero the V rows past the end so that 0 * NaN cannot reach the sum
 #pragma unroll

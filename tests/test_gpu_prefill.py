@@ -134,11 +134,15 @@ def test_prefill_max_q_len_larger_than_needed():
     check(wl, step, exp)
 
 
-def test_prefill_full_size_sampled_rows():
-    """prefill70b at full size (16 x 1,024 new tokens after up to 3,072 cached
-    ones): sampled rows checked one by one against the oracle, each as a
-    one-row prefill over its sequence's first p + 1 tokens."""
-    cfg = C["prefill70b"]
+@pytest.mark.parametrize("name", ["prefill13b", "prefill70b", "prefill_fp8"])
+def test_prefill_full_size_sampled_rows(name):
+    """The prefill workloads at full size (prefill13b: 16 whole prompts of
+    512..4,096 tokens; prefill70b: 16 x 1,024 new tokens after up to 3,072
+    cached ones; prefill_fp8: 8 x 2,048 new tokens after up to 6,144 cached
+    ones over an e4m3 cache): the whole pools after the cache write, and
+    sampled rows checked one by one against the oracle, each as a one-row
+    prefill over its sequence's first p + 1 tokens."""
+    cfg = C[name]
     wl = workloads.make_prefill(cfg, device="cuda")
     pre = parity.snapshot(wl)
     step = PrefillStep(wl)
@@ -155,8 +159,10 @@ def test_prefill_full_size_sampled_rows():
     exp_slots = parity.prefill_slots(wl)
     assert np.array_equal(step.slots.cpu().numpy(), exp_slots)
     from oracle import paged
-    assert np.array_equal(k_after, paged.write_cache(pre.k_pool, pre.k_new, exp_slots, cfg.block_size))
-    assert np.array_equal(v_after, paged.write_cache(pre.v_pool, pre.v_new, exp_slots, cfg.block_size))
+    k_rows = parity.encode_rows(pre.k_new, cfg.src_dtype, cfg.kv_dtype, wl.k_scale)
+    v_rows = parity.encode_rows(pre.v_new, cfg.src_dtype, cfg.kv_dtype, wl.v_scale)
+    assert np.array_equal(k_after, paged.write_cache(pre.k_pool, k_rows, exp_slots, cfg.block_size))
+    assert np.array_equal(v_after, paged.write_cache(pre.v_pool, v_rows, exp_slots, cfg.block_size))
     width = max(len(r) for r in wl.tables)
     tab = workloads.pad_tables(wl.tables, width).astype(np.int64)
     q = parity.widen(pre.q, cfg.q_dtype)
@@ -166,11 +172,11 @@ def test_prefill_full_size_sampled_rows():
         p = int(wl.seq_lens[b]) - int(wl.news[b]) + i
         ref = paged.prefill(q[r:r + 1], k_after, v_after, tab[b:b + 1], np.array([p + 1]),
                             np.array([0, 1]), cfg.block_size, wl.scale,
-                            widen_k=lambda x: parity.widen(x, cfg.kv_dtype),
-                            widen_v=lambda x: parity.widen(x, cfg.kv_dtype))
+                            widen_k=lambda x: parity.widen(x, cfg.kv_dtype, wl.k_scale),
+                            widen_v=lambda x: parity.widen(x, cfg.kv_dtype, wl.v_scale))
         worst = max(worst, parity.assert_close(got[r:r + 1], ref, cfg.kv_dtype, cfg.out_dtype,
-                                               f"row {r}"))
-    print(f"[ok] full size sampled {len(picks)} rows, max abs err {worst:.3e}", flush=True)
+                                               f"{name} row {r}"))
+    print(f"[ok] {name} full size sampled {len(picks)} rows, max abs err {worst:.3e}", flush=True)
 
 
 def test_prefill_placement_invariance_and_determinism():
