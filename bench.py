@@ -69,14 +69,17 @@ def kv_bytes(wl) -> int:
 
 def decode_kernel_name(cfg) -> str:
     """The dominant kernel the library dispatches for this workload: the
-    prefill kernel for prefill workloads; for decode, the matrix-core
-    partition kernel for query groups of 4 or 8 over 16-bit or e4m3 caches,
-    the vector-ALU kernel otherwise."""
+    prefill kernel for prefill workloads; for decode, the library's rule
+    (include/pa.h, decode workspace layout): the matrix-core partition kernel
+    for query groups of 3 to 16 with a 16-bit query over a cache of the same
+    16-bit type or an 8-bit cache, the vector-ALU kernel otherwise."""
     if cfg.prefill:
         return "prefill_kernel"
     if cfg.swap:
         return "copy_blocks_kernel"
-    return "decode_mfma_kernel" if cfg.G in (4, 8) and cfg.kv_dtype != "f32" else "decode_valu_kernel"
+    pair = cfg.q_dtype == cfg.kv_dtype in ("f16", "bf16") or (
+        cfg.kv_dtype in ("e4m3", "e5m2") and cfg.q_dtype in ("f16", "bf16"))
+    return "decode_mfma_kernel" if 3 <= cfg.G <= 16 and pair else "decode_valu_kernel"
 
 
 def prefill_flops(wl) -> int:
@@ -544,6 +547,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b")
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--combine", choices=["auto", "in_launch", "reduce"], default="auto",
+                    help="who combines sequences split across work-groups (pa_decode_args.combine)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-ceiling", action="store_true",
@@ -579,7 +584,9 @@ def main(argv=None):
         return bench_swap(args, cfg)
     print(f"[bench] building workload {cfg.name}", file=sys.stderr, flush=True)
     wl = workloads.make(cfg, device="cuda")
-    step = DecodeStep(wl, partition_size=args.partition_size)
+    combine = {"auto": binding.PA_COMBINE_AUTO, "in_launch": binding.PA_COMBINE_IN_LAUNCH,
+               "reduce": binding.PA_COMBINE_REDUCE}[args.combine]
+    step = DecodeStep(wl, partition_size=args.partition_size, combine=combine)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         step.run()
@@ -636,7 +643,8 @@ def main(argv=None):
                    "seq_lens": (f"U[{cfg.len_range[0]},{cfg.len_range[1]}]" if cfg.len_range
                                 else "fixed"),
                    "total_tokens": int(np.sum(wl.seq_lens)), "pool_blocks": wl.num_blocks,
-                   "partition_size": partition, "cow_copies": len(step.copies)},
+                   "partition_size": partition, "combine": args.combine,
+                   "cow_copies": len(step.copies)},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_layers_per_s": round(cfg.B / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": nbytes,

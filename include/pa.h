@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 /* Element types.  The 8-bit cache formats (P1 "İlgili Teknikler": an 8-bit
  * KV cache, about half the memory of 16-bit) store a code c meaning
@@ -106,7 +106,18 @@ typedef struct pa_decode_args {
   const float* v_scales;       /* for an 8-bit cache: replace k_scale / v_scale, head */
                                /* g's codes meaning value * k_scales[g]; both or      */
                                /* neither; positive and finite (not checked)          */
+  int32_t combine;             /* who combines split sequences (PA_COMBINE_*)         */
 } pa_decode_args;
+
+/* Who combines the pieces of a sequence that several work-groups share
+ * (pa_decode_args.combine; Schedules below). */
+enum {
+  PA_COMBINE_AUTO = 0,      /* the library picks: IN_LAUNCH under the balanced   */
+                            /* schedule when its work-groups per KV-head group   */
+                            /* do not outnumber the sequences, else REDUCE       */
+  PA_COMBINE_IN_LAUNCH = 1, /* the partition launch itself: no reduce kernel     */
+  PA_COMBINE_REDUCE = 2     /* a reduce kernel after the partition launch        */
+};
 
 /* Supported decode combinations (others return PA_ERR_UNSUPPORTED):
  *   D in {64, 128}; block_size in {8, 16, 32, 64};
@@ -120,25 +131,62 @@ typedef struct pa_decode_args {
 /* Schedules.
  *   partition_size > 0 (fixed): one work-group per (KV heads, sequence,
  *     partition of partition_size tokens).  P = ceil(max_blocks_per_seq *
- *     block_size / partition_size) may not exceed 65535.  Workspace: fp32
- *     acc [P][B*Hq][D], then m [P][B*Hq] and l [P][B*Hq]; 4*B*Hq*P*(D+2)
- *     bytes, or none when P == 1.
- *   partition_size == 0 (balanced, the default): a plan kernel sums the
- *     sequences' block counts on the device, then one round of work-groups
- *     splits the concatenation of all sequences' blocks into equal ranges,
- *     so the work per work-group does not depend on the length mix.
- *     Workspace: int32 block prefix sums [B+1] padded to a multiple of 256
- *     bytes, then fp32 partials for rows = HG * W * 2 * NW * G:
- *     acc [rows][D], m [rows], l [rows].  NW = KV heads per work-group
- *     (the smallest power of two >= min(Hkv, 8) when G is 4 or 8 with a
- *     16-bit query over a 16-bit or e4m3 cache, else min(Hkv, 4) rounded up
- *     the same way), HG = ceil(Hkv / NW), W = max(1, floor(4096 / (HG*NW))).
+ *     block_size / partition_size) may not exceed 65535.
+ *   partition_size == 0 (balanced, the default): the sequences' block counts
+ *     are summed on the device (by every work-group itself up to 1024
+ *     sequences, else by a plan kernel first), then one round of
+ *     work-groups splits the concatenation of all sequences' blocks into
+ *     equal ranges, so the work per work-group does not depend on the
+ *     length mix.
+ *   Either way a sequence longer than one piece leaves fp32 partials (m, l
+ *   and the unnormalised V-weighted sum of each piece) in the workspace, to
+ *   be combined as M = max_p m_p,
+ *   out = sum_p e^(m_p-M) acc_p / sum_p e^(m_p-M) l_p:
+ *   - PA_COMBINE_IN_LAUNCH: the work-group that finishes the sequence's last
+ *     piece combines them in the same launch.  It counts the pieces'
+ *     arrivals on an int32 counter per (KV head, sequence) in the workspace;
+ *     no work-group ever waits for another.  The pieces' rows then pass
+ *     through device-coherent memory, and the combine runs at the end of the
+ *     launch, so this pays when few sequences are split (no reduce launch).
+ *   - PA_COMBINE_REDUCE: pa_decode_reduce's kernel combines them (and writes
+ *     zeros for empty sequences) in a launch of its own, which pays when
+ *     many sequences are split into many pieces.
+ *   pa_decode_partition runs the first launch, pa_decode_reduce the reduce
+ *   kernel when there is one (it enqueues nothing otherwise); pa_decode runs
+ *   both.
+ *
+ * Workspace layout (device memory, 16-byte aligned):
+ *   1. counters: int32 [Hkv][B], padded to a multiple of 256 bytes
+ *      (pa_decode_workspace_zero_bytes), used by PA_COMBINE_IN_LAUNCH.
+ *      They must be zero when a call starts, and every call that returns
+ *      PA_OK leaves them zero once its kernels have run.  So zero the workspace once after allocating it;
+ *      before reusing it for arguments with another B or Hkv (whose
+ *      counters would cover other bytes), zero the new counter bytes again.
+ *   2. balanced only: int32 block prefix sums [B+1], padded to a multiple of
+ *      256 bytes;
+ *   3. fp32 partial rows: acc [rows][D], then m [rows], then l [rows], with
+ *      rows = B*Hq*P (fixed; partition-major) or HG * W * 2 * NW * G
+ *      (balanced).  NW = KV heads per work-group (the smallest power of two
+ *      >= min(Hkv, 8) when the matrix-core kernel serves the call: G from 3
+ *      to 16 with a 16-bit query over a 16-bit or 8-bit cache; else the
+ *      smallest power of two >= min(Hkv, 4)), HG = ceil(Hkv / NW),
+ *      W = max(1, floor(4096 / (HG*NW))).
+ *   The fixed schedule with P == 1 splits nothing and needs no workspace.
+ *   The acc rows (rows * D * 4 bytes) must stay under 2 GiB (PA_ERR_SHAPE
+ *   otherwise; the balanced schedule's stay under 70 MB).
  * Workspace sizes depend only on these host-side sizes, never on device
- * contents.  Contents need not be initialised and are overwritten.
+ * contents.  Apart from the counters, contents need not be initialised.
+ * Two calls in flight at once (other streams) need separate workspaces.
  *
  * Bytes of workspace pa_decode needs for these arguments; 0 for invalid
  * arguments (and for a fixed schedule with P == 1). */
 size_t pa_decode_workspace_size(const pa_decode_args* a);
+
+/* Bytes at the start of the workspace (the arrival counters) that must hold
+ * zeros when a call with these arguments starts; every call leaves them
+ * zero.  0 for invalid arguments and when no workspace is needed.  Host
+ * only. */
+size_t pa_decode_workspace_zero_bytes(const pa_decode_args* a);
 
 /* Tokens per fixed split-K partition pa_decode will use for these arguments
  * (partition_size); 0 for the balanced schedule and for invalid arguments.
@@ -161,17 +209,18 @@ pa_status pa_decode_check(const pa_decode_args* a);
  * Equivalent to pa_decode_partition followed by pa_decode_reduce. */
 pa_status pa_decode(const pa_decode_args* a, void* stream);
 
-/* Split-K step 1 (with the plan kernel first under the balanced schedule):
- * each work-group computes, for each piece of a sequence it covers, the
- * piece's running max m, sum l and unnormalised V-weighted sum with an
- * online softmax.  Sequences covered by one work-group are finished here
- * (out written); others leave fp32 partials in the workspace. */
+/* Split-K step 1 (with the plan kernel first under the balanced schedule
+ * past 1024 sequences): each work-group computes, for each piece of a
+ * sequence it covers, the piece's running max m, sum l and unnormalised
+ * V-weighted sum with an online softmax.  Sequences covered by one
+ * work-group are finished here (out written); split ones too under
+ * PA_COMBINE_IN_LAUNCH, else they leave fp32 partials in the workspace. */
 pa_status pa_decode_partition(const pa_decode_args* a, void* stream);
 
-/* Split-K step 2: for sequences split between work-groups, combine the
- * partials: M = max_p m_p, out = sum_p e^(m_p-M) acc_p / sum_p e^(m_p-M) l_p;
- * under the balanced schedule it also writes zeros for sequences with
- * seq_lens 0.  Enqueues nothing for a fixed schedule with P == 1. */
+/* Split-K step 2 under PA_COMBINE_REDUCE: for sequences split between
+ * work-groups, combine the partials (Schedules above); under the balanced
+ * schedule it also writes zeros for sequences with seq_lens 0.  Enqueues
+ * nothing under PA_COMBINE_IN_LAUNCH or for a fixed schedule with P == 1. */
 pa_status pa_decode_reduce(const pa_decode_args* a, void* stream);
 
 /* Slot of each sequence's new token (P1 "Sayfalama Nasıl Çalışır", code

@@ -23,6 +23,8 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2 = 0, 1, 2, 3, 4
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
           4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH", 6: "PA_ERR_OUT_OF_BLOCKS"}
 PA_ERR_OUT_OF_BLOCKS = 6
+# who combines split sequences (pa_decode_args.combine)
+PA_COMBINE_AUTO, PA_COMBINE_IN_LAUNCH, PA_COMBINE_REDUCE = 0, 1, 2
 DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "e4m3": PA_FP8_E4M3, "e5m2": PA_FP8_E5M2}
 # uint8 pools are taken as e4m3 unless the caller names the format (kv_dtype)
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -52,7 +54,7 @@ class DecodeArgs(ctypes.Structure):
         ("v_scale", ctypes.c_float), ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
         ("out_dtype", ctypes.c_int), ("partition_size", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-        ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p), ("combine", ctypes.c_int32),
     ]
 
 
@@ -93,6 +95,8 @@ def lib() -> ctypes.CDLL:
     argp = ctypes.POINTER(DecodeArgs)
     L.pa_decode_workspace_size.argtypes = [argp]
     L.pa_decode_workspace_size.restype = ctypes.c_size_t
+    L.pa_decode_workspace_zero_bytes.argtypes = [argp]
+    L.pa_decode_workspace_zero_bytes.restype = ctypes.c_size_t
     L.pa_decode_partition_size.argtypes = [argp]
     L.pa_decode_partition_size.restype = ctypes.c_int32
     L.pa_read_blocks.argtypes = [vp, i32, ctypes.c_size_t, vp, i32, vp, i32, vp]
@@ -200,7 +204,7 @@ def _head_scales(args, k_scales, v_scales, Hkv):
 
 def decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0, v_scale=1.0,
                 partition_size=0, workspace=None, kv_dtype=None, k_scales=None,
-                v_scales=None) -> DecodeArgs:
+                v_scales=None, combine=PA_COMBINE_AUTO) -> DecodeArgs:
     """Build ``pa_decode_args`` from tensors (shapes per include/pa.h)."""
     for t, n, nd in ((out, "out", 3), (q, "q", 3), (k_cache, "k_cache", 4), (v_cache, "v_cache", 4)):
         _require(t, n, ndim=nd)
@@ -222,6 +226,7 @@ def decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale
     a.kv_dtype = _pa_dtype(k_cache, kv_dtype)
     a.out_dtype = _pa_dtype(out)
     a.partition_size = int(partition_size)
+    a.combine = int(combine)
     _head_scales(a, k_scales, v_scales, Hkv)
     if workspace is not None:
         _require(workspace, "workspace")
@@ -238,12 +243,20 @@ def partition_size(args: DecodeArgs) -> int:
     return int(lib().pa_decode_partition_size(ctypes.byref(args)))
 
 
+def workspace_zero_bytes(args: DecodeArgs) -> int:
+    """Bytes at the workspace's start that must be zero when a call starts."""
+    return int(lib().pa_decode_workspace_zero_bytes(ctypes.byref(args)))
+
+
 def alloc_workspace(args: DecodeArgs, device=None) -> torch.Tensor | None:
-    """A workspace tensor of the size ``pa_decode_workspace_size`` asks for (or None)."""
+    """A zero-filled workspace tensor of the size ``pa_decode_workspace_size``
+    asks for (or None).  Its arrival counters start at zero and every call
+    leaves them zero, so the tensor serves any number of calls with these
+    arguments' B and Hkv."""
     n = workspace_size(args)
     if n == 0:
         return None
-    ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
     args.workspace, args.workspace_bytes = ws.data_ptr(), n
     return ws
 
@@ -265,10 +278,11 @@ def decode_reduce_run(args: DecodeArgs, stream=None) -> None:
 
 
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0, v_scale=1.0,
-           partition_size=0, workspace=None, kv_dtype=None, stream=None, k_scales=None, v_scales=None):
+           partition_size=0, workspace=None, kv_dtype=None, stream=None, k_scales=None, v_scales=None,
+           combine=PA_COMBINE_AUTO):
     """pa_decode on tensors; allocates the workspace with torch when none is given."""
     a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale,
-                    partition_size, workspace, kv_dtype, k_scales, v_scales)
+                    partition_size, workspace, kv_dtype, k_scales, v_scales, combine)
     keep = None
     if workspace is None:
         keep = alloc_workspace(a, q.device)

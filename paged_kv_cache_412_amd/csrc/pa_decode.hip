@@ -8,7 +8,10 @@
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,
 // the same identity the FlashAttention-style tiling uses inside a partition
 // (P1 = Ultralytics glossary page "PagedAttention", section "İlgili
-// Teknikler").
+// Teknikler").  Either the partition kernels combine the partials themselves
+// (the last piece of a sequence to finish does it, pa_decode_common.h) or
+// the reduce kernel below does, in a launch of its own; the host picks per
+// call (DecodeParams::fused).
 
 #include <hip/hip_runtime.h>
 
@@ -56,16 +59,6 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeP
 // Waves of the reduce kernel per work-group (one head each, or all four on
 // one head's rows; see below).
 constexpr int kReduceWaves = 4;
-
-// Maximum over the 64 lanes of a wave; every lane receives it.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
-  v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
-  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
-  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
-}
 
 // Value of v in lane i (i wave-uniform).
 __device__ __forceinline__ float lane_value(float v, int i) {

@@ -10,7 +10,8 @@
 // scores (log2 units), the running sum l of 2^(s - m) and the unnormalised
 // V-weighted sum acc.  A segment covering the whole sequence writes
 // out = v_scale * acc / l directly; otherwise (m, l, v_scale * acc) go to a
-// partials row for the reduce kernel.
+// partials row, and the last segment of the sequence to finish combines the
+// rows (finish_splits below).
 //
 // Work decomposition.  A work-group holds one wave64 per KV head of a group
 // of up to NW consecutive KV heads (NW = 4 for the VALU kernel, 8 for the
@@ -28,6 +29,11 @@
 #include "pa_internal.h"
 
 namespace pa {
+
+// s_waitcnt immediate that waits for every outstanding vector memory
+// access, stores included (vmcnt = 0; expcnt and lgkmcnt left at their
+// maxima, so they do not wait): gfx9 encoding, vmcnt in bits 3:0 and 15:14.
+constexpr unsigned kWaitVmcnt0 = 0x0F70;
 
 // Running-max start value: finite, so that exp2(m_old - m_new) is 0 or 1
 // (never NaN) while a wave has seen no valid token; real scores are far above.
@@ -59,10 +65,10 @@ struct SegmentDest {
 // The balanced schedule's prefix sums, prefix[b] = blocks of sequences
 // before b and prefix[B] = all blocks.  With p.inline_plan every work-group
 // computes them into LDS (its threads take contiguous runs of sequences, a
-// wave scan and one pass over the wave totals; two barriers), and
-// work-group (0, 0) also stores them where the reduce kernel reads them;
-// otherwise the plan kernel has written them to p.prefix.  Every thread of
-// the work-group calls this, before any of them leaves.
+// wave scan and one pass over the wave totals; two barriers), and when a
+// reduce kernel follows, work-group (0, 0) also stores them where it reads
+// them; otherwise the plan kernel has written them to p.prefix.  Every
+// thread of the work-group calls this, before any of them leaves.
 struct PlanLds {
   int32_t prefix[kInlinePlanMaxB + 1];
   int32_t wave_sum[16];
@@ -93,7 +99,7 @@ __device__ __forceinline__ const int32_t* schedule_prefix(const DecodeParams& p,
   }
   if (t == T - 1) lds.prefix[p.B] = base + x;
   __syncthreads();
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  if (!p.fused && blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = t; i <= p.B; i += T) p.prefix[i] = lds.prefix[i];
   return lds.prefix;
 }
@@ -267,6 +273,40 @@ __device__ __forceinline__ void store_out_n(void* base, size_t i, const float* v
   }
 }
 
+// Partial rows of split sequences cross work-groups, which may run on
+// different XCDs, each with its own L2.  They are written and read with
+// device-scope 16-byte buffer accesses (cache policy sc1), which go to the
+// device-coherent level instead of a non-coherent L2 copy, so no cache-wide
+// write-back or invalidate is needed to pass them between XCDs.  The host
+// keeps each partial region under 2 GiB, so 32-bit byte offsets reach it.
+constexpr int kCoherent = 16;  // sc1: device scope
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
+}
+// N partial sums of row r from element d0 (16-byte stores), and the row's m
+// and l from the lane that holds element 0; cache policy CP.
+template <int CP, int N>
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rm,
+                                              __amdgpu_buffer_rsrc_t rl, uint32_t r, int D, int d0,
+                                              const float* v, float m, float l) {
+#pragma unroll
+  for (int k = 0; k < N; k += 4) {
+    const f32x4_t x = {v[k], v[k + 1], v[k + 2], v[k + 3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), ra, (r * D + d0 + k) * 4u, 0, CP);
+  }
+  if (d0 == 0) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, m), rm, r * 4u, 0, CP);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l), rl, r * 4u, 0, CP);
+  }
+}
+__device__ __forceinline__ f32x4_t load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t elem) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4u, 0, kCoherent));
+}
+__device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t r, uint32_t elem) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, elem * 4u, 0, kCoherent));
+}
+
 // Finish N elements [d0, d0+N) of query h of a segment: out (the segment
 // covers its sequence) or its partials row.  m, l: the query's final running
 // max and sum; acc: its unnormalised sums; vs: the V scale of its KV head.
@@ -279,14 +319,327 @@ __device__ __forceinline__ void store_segment(const DecodeParams& p, const Segme
     for (int k = 0; k < N; ++k) v[k] = l > 0.f ? (acc[k] / l) * vs : 0.f;
     store_out_n<N>(p.out, (dst.out_row + h) * p.D + d0, v, p.out_dtype);
   } else {
-    const size_t r = dst.part_row + h;
+    const uint32_t r = static_cast<uint32_t>(dst.part_row + h);
 #pragma unroll
     for (int k = 0; k < N; ++k) v[k] = acc[k] * vs;
-    store_f32_n<N>(p.ws_acc + r * p.D + d0, v);
-    if (d0 == 0) {
-      p.ws_m[r] = m;
-      p.ws_l[r] = l;
+    const __amdgpu_buffer_rsrc_t ra = partial_rsrc(p.ws_acc);
+    const __amdgpu_buffer_rsrc_t rm = partial_rsrc(p.ws_m);
+    const __amdgpu_buffer_rsrc_t rl = partial_rsrc(p.ws_l);
+    if (p.fused) {
+      // straight to the device-coherent level, where the wave that combines
+      // the sequence in this launch reads them
+      store_partial<kCoherent, N>(ra, rm, rl, r, p.D, d0, v, m, l);
+    } else {
+      // through the L2 as usual: the reduce kernel reads them after this launch
+      store_partial<0, N>(ra, rm, rl, r, p.D, d0, v, m, l);
     }
+  }
+}
+
+// ------------------------------------------------------------------ split sequences
+//
+// A sequence that several segments cover (partitions of it under the fixed
+// schedule; the work-groups whose block ranges overlap it under the balanced
+// one) leaves one partial row group per segment: for each of the G query
+// heads of a KV head, the segment's running max m_i (log2 units), running sum
+// l_i and unnormalised weighted sum acc_i (v_scale applied).  Softmax over
+// the whole sequence follows from rescaling every segment to the common
+// maximum, the identity the FlashAttention-style tiling uses inside a segment
+// (P1 = Ultralytics glossary page "PagedAttention", section "İlgili
+// Teknikler"):
+//   M = max_i m_i,  out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
+//
+// No separate launch combines them.  Each wave that wrote a partial row
+// group waits until its stores are complete and then counts its arrival on
+// the (KV head, sequence) counter in the workspace; the wave whose arrival
+// completes the count reads the others' rows, combines them and resets the
+// counter to zero.  The rows are written and read with device-scope accesses
+// (store_partial with sc1, load_coherent*), so what one XCD wrote is what another
+// reads without any cache-wide write-back or invalidate; the reads are
+// issued only after the arrival that completed the count has returned.  No
+// wave ever waits for another, and every call leaves every counter zero for
+// the next.
+
+// Maximum over the 64 lanes of a wave; every lane receives it.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+// Where the n partial row groups of one (sequence, KV head) are: row group i
+// starts at row split_row(i) (query 0; query q is the row after it by q).
+struct SplitRows {
+  int n;              // row groups (segments that cover the sequence)
+  int hg, w0, wave;   // balanced: head group, first work-group, wave
+  int first_second;   // balanced: the first work-group used its second slot
+  size_t row0, step;  // fixed: row of partition 0, rows between partitions
+};
+
+__device__ __forceinline__ size_t split_row(const DecodeParams& p, const SplitRows& s, int i) {
+  if (p.balanced) return balanced_row(p, s.hg, s.w0 + i, (i == 0 && s.first_second) ? 1 : 0, s.wave, 0);
+  return s.row0 + static_cast<size_t>(i) * s.step;
+}
+
+// Combine the partial row groups of one (sequence, KV head) for queries
+// q0 .. q0 + QB - 1 (those below G) into their output rows.  Pass 1: lane i
+// holds the (m, l) of row group i, so the common maximum and the rescaled
+// sum are wave reductions.  Pass 2: a query's D partial sums are D/4 lanes
+// of 16-byte loads, so one load instruction covers 64 / (D/4) row groups
+// (the lane's `sub`); LOADS 16-byte loads per lane go out at once per batch
+// of row groups (the first batch together with pass 1's loads), each lane
+// takes its row group's weight from the lane that holds it, and the
+// sub-groups' sums are added at the end.  The order of every sum
+// is fixed by the row groups' order, not by timing.  LOADS trades the
+// batches' round trips against registers: the combine runs after the block
+// walk, and a kernel whose walk needs few registers keeps it small so that
+// the combine does not set its register count.
+template <int D, int QB, int LOADS>
+__device__ __forceinline__ void combine_queries(const DecodeParams& p, const SplitRows& sr, int G,
+                                                int q0, size_t out_row, int lane) {
+  constexpr int QL = D / 4;                             // lanes per query row
+  constexpr int RPL = 64 / QL;                          // row groups per load instruction
+  constexpr int NB = LOADS / QB > 0 ? LOADS / QB : 1;   // load instructions per query and batch
+  constexpr int RB = RPL * NB;                          // row groups per batch
+  const int n = sr.n;
+  const int sub = lane / QL;
+  const int col = 4 * (lane % QL);
+  // every load is issued unconditionally, at a clamped row group and query
+  // (then discarded), so that a batch's loads go out back to back
+  int qc[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) qc[q] = min(q0 + q, G - 1);
+  auto valid = [&](int q) { return q0 + q < G; };
+
+  const __amdgpu_buffer_rsrc_t racc = partial_rsrc(p.ws_acc);
+  const __amdgpu_buffer_rsrc_t rm = partial_rsrc(p.ws_m);
+  const __amdgpu_buffer_rsrc_t rl = partial_rsrc(p.ws_l);
+  f32x4_t buf[NB][QB];
+  auto load_batch = [&](int r0, int c1) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int r = min(r0 + j * RPL + sub, c1 - 1);  // past the end: repeat the last row group
+      const uint32_t row = static_cast<uint32_t>(split_row(p, sr, r));
+#pragma unroll
+      for (int q = 0; q < QB; ++q) buf[j][q] = load_coherent4(racc, (row + qc[q]) * D + col);
+    }
+  };
+  // (m, l) of row group i = lane, and the first batch of partial sums
+  float m0[QB], l0[QB], M[QB];
+  {
+    const uint32_t r = static_cast<uint32_t>(split_row(p, sr, min(lane, n - 1)));
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      m0[q] = load_coherent1(rm, r + qc[q]);
+      l0[q] = load_coherent1(rl, r + qc[q]);
+    }
+  }
+  load_batch(0, min(n, 64));
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    if (lane >= n) {
+      m0[q] = kMaxInit;
+      l0[q] = 0.f;
+    }
+    M[q] = m0[q];
+  }
+  for (int i0 = 64; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t r = static_cast<uint32_t>(split_row(p, sr, min(i, n - 1)));
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const float mi = load_coherent1(rm, r + qc[q]);
+      if (i < n) M[q] = fmaxf(M[q], mi);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) M[q] = wave_max(M[q]);
+
+  f32x4_t A[QB];
+  float Ls[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    A[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    Ls[q] = 0.f;
+  }
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int c1 = min(n, c0 + 64);
+    float w[QB];  // weight of row group c0 + lane
+    if (c0 == 0) {
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        w[q] = lane < n ? fast_exp2(m0[q] - M[q]) : 0.f;
+        Ls[q] += l0[q] * w[q];
+      }
+    } else {
+      const int i = c0 + lane;
+      const uint32_t r = static_cast<uint32_t>(split_row(p, sr, min(i, n - 1)));
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const float mi = load_coherent1(rm, r + qc[q]);
+        const float li = load_coherent1(rl, r + qc[q]);
+        w[q] = i < n ? fast_exp2(mi - M[q]) : 0.f;
+        Ls[q] += i < n ? li * w[q] : 0.f;
+      }
+    }
+    for (int r0 = c0; r0 < c1; r0 += RB) {
+      if (r0 > 0) load_batch(r0, c1);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int r = r0 + j * RPL + sub;
+        const int src = min(r, c1 - 1) - c0;
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const float wr = __shfl(w[q], src, 64);
+          if (r < c1) A[q] += wr * buf[j][q];  // a repeated row group adds nothing, NaN included
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = QL; off < 64; off <<= 1) {
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) A[q][k] += __shfl_xor(A[q][k], off, 64);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) Ls[q] = group_sum<64>(Ls[q]);
+  if (sub == 0) {
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (valid(q)) {
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = Ls[q] > 0.f ? A[q][k] / Ls[q] : 0.f;
+        store_out_n<4>(p.out, (out_row + q0 + q) * D + col, v, p.out_dtype);
+      }
+    }
+  }
+}
+
+// All G queries of one (sequence, KV head), QB at a time.
+template <int D, int QB, int LOADS>
+__device__ __forceinline__ void combine_split(const DecodeParams& p, const SplitRows& sr, int G,
+                                              size_t out_row, int lane) {
+  for (int q0 = 0; q0 < G; q0 += QB) combine_queries<D, QB, LOADS>(p, sr, G, q0, out_row, lane);
+}
+
+// Where the partial row groups of split sequence b (KV head g of head
+// group hg, wave `wave`) are.
+__device__ __forceinline__ SplitRows split_rows(const DecodeParams& p, const int32_t* prefix, int b,
+                                                int hg, int wave, int G) {
+  SplitRows sr{};
+  if (p.balanced) {
+    const int64_t pb = prefix[b], pn = prefix[b + 1], F = prefix[p.B];
+    const int ng = balanced_groups(p, F);
+    sr.w0 = balanced_owner(F, pb, ng);
+    sr.n = balanced_owner(F, pn - 1, ng) - sr.w0 + 1;
+    sr.first_second = balanced_start(F, sr.w0, ng) != pb ? 1 : 0;
+    sr.hg = hg;
+    sr.wave = wave;
+  } else {
+    const int L = clamped_len(p, b);
+    sr.n = (L + p.partition_size - 1) / p.partition_size;
+    const int g = hg * p.heads_per_wg + wave;
+    sr.row0 = ws_row(p, static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G, 0);
+    sr.step = static_cast<size_t>(p.B) * p.Hq;
+  }
+  return sr;
+}
+
+// Balanced schedule: a sequence without tokens has no blocks, so no segment
+// covers it; work-group w writes the zero outputs of the empty sequences
+// b = w, w + groups, ... (queries of KV head g).
+template <int D>
+__device__ __forceinline__ void zero_empty_sequences(const DecodeParams& p, const int32_t* prefix,
+                                                     int g, int G, int lane) {
+  for (int b = blockIdx.y; b < p.B; b += p.groups) {
+    if (prefix[b + 1] != prefix[b]) continue;
+    const size_t e0 = (static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G) * D;
+    const float z[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = lane; i < G * D / 4; i += 64) store_out_n<4>(p.out, e0 + 4 * static_cast<size_t>(i), z, p.out_dtype);
+  }
+}
+
+// The largest b < B with prefix[b] <= x: for 0 <= x < prefix[B], the
+// (non-empty) sequence that holds block x.
+__device__ __forceinline__ int sequence_of_block(const int32_t* prefix, int B, int64_t x) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// What a wave does after its block walk: under the balanced schedule, zero
+// the empty sequences it is assigned; then, once its partial rows are
+// stored, count an arrival on the counter of each sequence it left partial
+// rows for, and combine the sequence's row groups if its arrival completed
+// the count (the counter then goes back to zero).  Those sequences follow from the schedule alone: under the balanced
+// schedule the ones holding the work-group's first and last blocks, unless
+// it covers them whole; under the fixed schedule its sequence, if longer
+// than one partition.  Nothing about them is kept through the walk, whose
+// registers are nearly all taken: the kernel's argument is read again from
+// the argument segment here, and the prefix sums from where they live.
+template <int D, int QB, int LOADS>
+__device__ __forceinline__ void finish_splits(PlanLds& lds, int lane) {
+  typedef const __attribute__((address_space(4))) DecodeParams KernArg;
+  KernArg* pk = (KernArg*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(pk));
+  DecodeParams p;
+  __builtin_memcpy(&p, (const void*)pk, sizeof(p));
+  if (!p.fused) return;  // the reduce kernel combines split sequences and zeroes empty ones
+  const int hg = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = hg * p.heads_per_wg + wave;
+  const int G = p.Hq / p.Hkv;
+  int split[2] = {-1, -1};
+  const int32_t* prefix = p.inline_plan ? lds.prefix : p.prefix;
+  if (p.balanced) {
+    zero_empty_sequences<D>(p, prefix, g, G, lane);
+    const int64_t F = prefix[p.B];
+    const int n = balanced_groups(p, F);
+    const int w = blockIdx.y;
+    if (w >= n) return;
+    const int64_t x0 = balanced_start(F, w, n), x1 = balanced_start(F, w + 1, n);
+    const int ba = sequence_of_block(prefix, p.B, x0);
+    const int bz = sequence_of_block(prefix, p.B, x1 - 1);
+    if (!(prefix[ba] == x0 && prefix[ba + 1] <= x1)) split[0] = ba;
+    if (bz != ba && prefix[bz + 1] > x1) split[1] = bz;
+  } else {
+    const int b = blockIdx.y;
+    const int L = clamped_len(p, b);
+    const int nblk = (L + p.block_size - 1) / p.block_size;
+    if (L > p.partition_size && static_cast<int64_t>(blockIdx.z) * (p.partition_size / p.block_size) < nblk)
+      split[0] = b;
+  }
+  if (split[0] < 0 && split[1] < 0) return;
+  // this wave's partial rows (device-scope stores) complete before its arrival counts
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int b = __builtin_amdgcn_readfirstlane(split[k]);
+    if (b < 0) continue;
+    const SplitRows sr = split_rows(p, prefix, b, hg, wave, G);
+    int32_t* cnt = p.counters + static_cast<size_t>(g) * p.B + b;
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readlane(old, 0);
+    if (old != sr.n - 1) continue;  // another segment of the sequence is still running
+    // every other segment's rows were complete before its arrival counted;
+    // they are read (device-scope loads) only after this arrival returned
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    combine_split<D, QB, LOADS>(p, sr, G, static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G, lane);
   }
 }
 

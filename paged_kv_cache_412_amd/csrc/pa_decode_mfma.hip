@@ -326,6 +326,7 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
       }
     }
   });
+  finish_splits<D, 4, (D == 128 ? 16 : 8)>(plan_lds, lane);  // 4 queries per combine pass
 }
 
 // ------------------------------------------------------------------ dispatch

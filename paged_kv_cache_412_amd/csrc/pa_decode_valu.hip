@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
       for (int e = 0; e < CE; ++e) acc[h][e] = 0.f;
     }
 
-    auto consume = [&](int j, unsigned ok, const Buf& r) {
+    auto consume = [&](int j, unsigned ok, Buf& r) {
       // valid rows of this block (only the last block of a sequence is
       // partial; a block id outside the pool counts none).  A unit of two
       // blocks: this lane's row tg is row tg % BS of block j + tg / BS.
@@ -286,9 +286,6 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
 #pragma unroll
         for (int h = 0; h < G; ++h) s[i][h] = group_sum<LPT>(O::dot(qr[h], r.k[i])) * qk;
       }
-      float vf[NL][CE];
-#pragma unroll
-      for (int i = 0; i < NL; ++i) O::to_f32(r.v[i], vf[i]);
       if (valid < BS) {
         // rows past the end are excluded outright: their K and V may hold
         // anything (NaN included), so they get weight 0 and a zeroed V row.
@@ -298,7 +295,7 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
 #pragma unroll
             for (int h = 0; h < G; ++h) s[i][h] = -__builtin_inff();
 #pragma unroll
-            for (int e = 0; e < CE; ++e) vf[i][e] = 0.f;
+            for (int w = 0; w < 4; ++w) r.v[i].w[w] = 0u;
           }
         }
       }
@@ -316,8 +313,10 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
         for (int i = 0; i < NL; ++i) {
           const float pw = fast_exp2(s[i][h] - mx);
           lh += pw;
+          float vf[CE];  // V row i in fp32, converted where it is used
+          O::to_f32(r.v[i], vf);
 #pragma unroll
-          for (int e = 0; e < CE; ++e) acc[h][e] = __builtin_fmaf(pw, vf[i][e], acc[h][e]);
+          for (int e = 0; e < CE; ++e) acc[h][e] = __builtin_fmaf(pw, vf[e], acc[h][e]);
         }
         l[h] = lh;
       }
@@ -351,6 +350,7 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
       for (int h = 0; h < G; ++h) store_segment<CE>(p, dst, h, c * CE, m[h], l[h], acc[h], vs);
     }
   });
+  finish_splits<D, (G < 4 ? G : 4), 4>(plan_lds, lane);
 }
 
 // ------------------------------------------------------------------ dispatch

@@ -10,19 +10,22 @@
 
 namespace pa {
 
-// Everything a decode-partition or reduce launch needs, resolved on the host.
+// Everything a decode-partition launch needs, resolved on the host.
 //
 // Two schedules split the work of a decode step among work-groups of
 // heads_per_wg waves (one KV head each):
 //  * fixed partitions (partition_size > 0 in the call): work-group
 //    (head group, sequence, partition) covers partition_size tokens of one
 //    sequence; partials rows are ws_row(hq, partition).
-//  * balanced (partition_size == 0): a plan kernel writes the prefix sums
-//    prefix[b] of the sequences' block counts; work-group (head group, w) of
-//    `groups` per head group takes blocks [w*F/groups, (w+1)*F/groups) of the
-//    concatenation of all sequences (F = prefix[B]).  It writes the output of
-//    every sequence it covers whole and partials only for the (at most two)
-//    sequences it covers in part; rows are balanced_row(...).
+//  * balanced (partition_size == 0): from the prefix sums prefix[b] of the
+//    sequences' block counts, work-group (head group, w) of `groups` per head
+//    group takes blocks [w*F/groups, (w+1)*F/groups) of the concatenation of
+//    all sequences (F = prefix[B]).  It writes the output of every sequence
+//    it covers whole and partials only for the (at most two) sequences it
+//    covers in part; rows are balanced_row(...).
+// Split sequences are combined either by the last of their segments to
+// finish, in the same launch (fused; arrival counters, pa_decode_common.h),
+// or by the reduce kernel launched after it.
 // Balanced schedule: up to this many sequences, the attention kernel's
 // work-groups compute the block-count prefix sums themselves (in LDS) instead
 // of a plan kernel launched before them.
@@ -38,7 +41,8 @@ struct DecodeParams {
   float* ws_acc;  // partial rows x D: unnormalised V-weighted sums (v_scale applied)
   float* ws_m;    // partial rows: running max (log2 units)
   float* ws_l;    // partial rows: running sum
-  int32_t* prefix;  // balanced: [B+1] block-count prefix sums
+  int32_t* prefix;  // balanced: [B+1] block-count prefix sums (plan kernel, B > kInlinePlanMaxB)
+  int32_t* counters;  // [Hkv][B] arrivals of a split sequence's segments; zero between calls
   // block_size, num_blocks and max_blocks_per_seq count the blocks the
   // kernels walk: 2^sub_shift of them make one block of the table (a block
   // is contiguous, so its halves are blocks of half the size); table rows
@@ -52,6 +56,7 @@ struct DecodeParams {
   int32_t head_groups;     // ceil(Hkv / heads_per_wg)
   int32_t groups;          // balanced: work-groups per head group
   int32_t inline_plan;     // balanced, B <= kInlinePlanMaxB: each work-group computes the plan
+  int32_t fused;           // 1: the partition kernels combine split sequences (no reduce launch)
   float qk_scale_log2;     // scale * k_scale * log2(e) (scale * log2(e) with per-head scales)
   float v_scale;
   const float* k_scales;   // per-head scales [Hkv] (device) or nullptr

@@ -5,13 +5,16 @@ A step, for a batch whose caches hold L-1 tokens each:
 1. the host block manager gives every sequence room for its new token (a new
    block when the last one is full, a copy-on-write when the last block is
    shared) -- done once, when the step is prepared;
-2. ``pa_slot_mapping``     slot of each new token from the block tables;
-3. ``pa_copy_blocks``      copy-on-write block copies (when there are any);
-4. ``pa_reshape_and_cache`` write the new K/V rows to their slots;
-5. ``pa_decode_partition`` split-K partitions of paged attention;
-6. ``pa_decode_reduce``    combine the partitions (long sequences only).
+2. ``pa_copy_blocks``      copy-on-write block copies (when there are any);
+3. ``pa_append_kv``        slot of each new token from the block tables and
+   the write of its K/V rows there, in one launch (equal to
+   ``pa_slot_mapping`` followed by ``pa_reshape_and_cache``);
+4. ``pa_decode_partition`` paged attention (sequences split across
+   work-groups combined in the same launch, or:)
+5. ``pa_decode_reduce``    the reduce launch that combines them, when the
+   library combines them in a launch of its own.
 
-Steps 2-6 run on the GPU and are what :meth:`DecodeStep.run` enqueues; they
+Steps 2-5 run on the GPU and are what :meth:`DecodeStep.run` enqueues; they
 are idempotent, so the same prepared step can be replayed for timing.
 """
 
@@ -26,7 +29,8 @@ from .workloads import TORCH_DTYPE, Workload, pad_tables, scale_args
 
 
 class DecodeStep:
-    def __init__(self, wl: Workload, partition_size: int = 0, out_dtype=None, device="cuda"):
+    def __init__(self, wl: Workload, partition_size: int = 0, out_dtype=None, device="cuda",
+                 combine=binding.PA_COMBINE_AUTO):
         cfg = wl.cfg
         self.wl = wl
         bs = cfg.block_size
@@ -49,7 +53,7 @@ class DecodeStep:
         self.args = binding.decode_args(self.out, wl.q, wl.k_pool, wl.v_pool, self.block_tables,
                                         self.seq_lens, wl.scale, self.k_scale, self.v_scale,
                                         partition_size, None, cfg.kv_dtype, self.k_scales,
-                                        self.v_scales)
+                                        self.v_scales, combine)
         self.workspace = binding.alloc_workspace(self.args, dev)
 
     # individual stages (each one C-ABI call)

@@ -21,7 +21,7 @@ def L():
 def test_header_declares_the_path_entry_points():
     names = set(binding.declared_functions())
     for n in ("pa_decode", "pa_decode_partition", "pa_decode_reduce", "pa_decode_workspace_size",
-              "pa_decode_partition_size",
+              "pa_decode_workspace_zero_bytes", "pa_decode_partition_size",
               "pa_decode_check", "pa_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
               "pa_reshape_and_cache_scales", "pa_append_kv",
               "pa_prefill", "pa_prefill_check", "pa_prefill_slot_mapping", "pa_swap_blocks",
@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.pa_abi_version() == 2
+    assert L.pa_abi_version() == 3
     for s in range(7):
         assert L.pa_status_str(s) and L.pa_status_str(s) != b"unknown status"
     assert L.pa_status_str(99) == b"unknown status"
@@ -123,26 +123,36 @@ def test_decode_check_block_sizes(L):
     assert check(L, block_size=32, B=40000, max_blocks_per_seq=30000) == 0
 
 
+def counter_bytes(B, Hkv):
+    """The arrival counters at the start of a workspace: int32 [Hkv][B],
+    padded to a multiple of 256 bytes."""
+    return -(-(4 * B * Hkv) // 256) * 256
+
+
 def test_workspace_size_formula_fixed_partitions(L):
+    # valid_args: B = 4, Hq = 8, Hkv = 8, D = 64
     a = valid_args(max_blocks_per_seq=64, partition_size=512)   # 1024 tokens -> 2 partitions
-    assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 2 * (64 + 2)
+    assert L.pa_decode_workspace_size(ctypes.byref(a)) == counter_bytes(4, 8) + 4 * 4 * 8 * 2 * (64 + 2)
+    assert L.pa_decode_workspace_zero_bytes(ctypes.byref(a)) == counter_bytes(4, 8)
     a = valid_args(max_blocks_per_seq=64, partition_size=256)   # 4 partitions
-    assert L.pa_decode_workspace_size(ctypes.byref(a)) == 4 * 4 * 8 * 4 * (64 + 2)
+    assert L.pa_decode_workspace_size(ctypes.byref(a)) == counter_bytes(4, 8) + 4 * 4 * 8 * 4 * (64 + 2)
     a = valid_args(max_blocks_per_seq=15, partition_size=256)   # 240 tokens: one partition
     assert L.pa_decode_workspace_size(ctypes.byref(a)) == 0
+    assert L.pa_decode_workspace_zero_bytes(ctypes.byref(a)) == 0
     assert L.pa_decode_workspace_size(ctypes.byref(valid_args(Hq=6, Hkv=4))) == 0
     assert L.pa_decode_workspace_size(None) == 0
+    assert L.pa_decode_workspace_zero_bytes(None) == 0
 
 
 def balanced_bytes(B, Hq, Hkv, D, nw):
-    """The balanced schedule's workspace: int32 prefix sums of B + 1 entries
-    (padded to 256 bytes), then fp32 partial rows (acc, m, l) for at most 4096
-    waves: head groups x work-groups per head group x 2 slots x KV heads per
-    work-group x G queries."""
+    """The balanced schedule's workspace: the arrival counters, int32 prefix
+    sums of B + 1 entries (padded to 256 bytes), then fp32 partial rows (acc,
+    m, l) for at most 4096 waves: head groups x work-groups per head group x
+    2 slots x KV heads per work-group x G queries."""
     hg = -(-Hkv // nw)
     groups_cap = max(1, 4096 // (hg * nw))
     rows = hg * groups_cap * 2 * nw * (Hq // Hkv)
-    return -(-(4 * (B + 1)) // 256) * 256 + 4 * rows * (D + 2)
+    return counter_bytes(B, Hkv) + -(-(4 * (B + 1)) // 256) * 256 + 4 * rows * (D + 2)
 
 
 @pytest.mark.parametrize("kw,nw", [
@@ -158,6 +168,7 @@ def test_workspace_size_formula_balanced(L, kw, nw):
     a = valid_args(**kw)
     want = balanced_bytes(a.B, a.Hq, a.Hkv, a.D, min(nw, 4 if a.Hq // a.Hkv <= 2 else 8))
     assert L.pa_decode_workspace_size(ctypes.byref(a)) == want
+    assert L.pa_decode_workspace_zero_bytes(ctypes.byref(a)) == counter_bytes(a.B, a.Hkv)
     assert L.pa_decode_partition_size(ctypes.byref(a)) == 0      # balanced: no fixed partition
 
 

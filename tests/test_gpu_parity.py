@@ -44,12 +44,13 @@ for _base in ("tiny", "llama13b", "llama70b", "long_fp8"):
 OTHER_BS = [f"{b}_bs{x}" for b in ("tiny", "llama13b", "llama70b", "long_fp8") for x in (8, 64)]
 
 
-def run_step(cfg, seqs=None, partition_size=0, out_dtype=None, q_sigma=1.0):
+def run_step(cfg, seqs=None, partition_size=0, out_dtype=None, q_sigma=1.0,
+             combine=binding.PA_COMBINE_AUTO):
     print(f"\n[case] {cfg.name} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} bs={cfg.block_size} "
-          f"kv={cfg.kv_dtype} part={partition_size} out={out_dtype}", flush=True)
+          f"kv={cfg.kv_dtype} part={partition_size} out={out_dtype} combine={combine}", flush=True)
     wl = workloads.make(cfg, device="cuda", q_sigma=q_sigma)
     pre = parity.snapshot(wl)
-    step = DecodeStep(wl, partition_size=partition_size, out_dtype=out_dtype)
+    step = DecodeStep(wl, partition_size=partition_size, out_dtype=out_dtype, combine=combine)
     step.run()
     torch.cuda.synchronize()
     exp = parity.oracle_step(wl, pre, seqs=seqs)
@@ -144,9 +145,11 @@ def test_balanced_schedule_extremes(name, shape):
 @pytest.mark.parametrize("name", ["tiny", "llama13b", "shared", "llama70b", "long_fp8"])
 @pytest.mark.parametrize("part", [0, 64])
 def test_workspace_contents_never_read_unwritten(name, part):
-    """A workspace full of NaN bytes: every partial the reduce reads must
-    have been written by this step's partition kernel (the balanced schedule
-    with fewer blocks than work-groups included)."""
+    """A workspace full of NaN bytes past its arrival counters: every partial
+    row the combine reads must have been written by this launch (the balanced
+    schedule with fewer blocks than work-groups included), and the counters
+    must be back at zero after every call, so that the next call on the same
+    workspace is right too."""
     cfg = SMALL[name]
     if part % cfg.block_size:
         part = cfg.block_size
@@ -154,12 +157,72 @@ def test_workspace_contents_never_read_unwritten(name, part):
     wl = workloads.make(cfg, device="cuda")
     pre = parity.snapshot(wl)
     step = DecodeStep(wl, partition_size=part, out_dtype="f32")
+    zb = binding.workspace_zero_bytes(step.args)
     if step.workspace is not None:
-        step.workspace.fill_(0xFF)
+        assert 0 < zb <= step.workspace.numel()
+        step.workspace[zb:].fill_(0xFF)
     step.run()
     torch.cuda.synchronize()
     exp = parity.oracle_step(wl, pre)
     check_step(wl, step, exp, out_dtype="f32")
+    if step.workspace is not None:
+        assert int(step.workspace[:zb].count_nonzero()) == 0, "arrival counters not reset"
+        step.workspace[zb:].fill_(0xFF)
+        step.out.fill_(float("nan"))
+        step.decode_partition()
+        step.decode_reduce()
+        torch.cuda.synchronize()
+        assert parity.assert_close(parity.gpu_out(step.out), exp.out, cfg.kv_dtype, "f32", name) >= 0
+        assert int(step.workspace[:zb].count_nonzero()) == 0
+
+
+COMBINES = {"in_launch": binding.PA_COMBINE_IN_LAUNCH, "reduce": binding.PA_COMBINE_REDUCE}
+
+
+@pytest.mark.parametrize("mode", list(COMBINES))
+@pytest.mark.parametrize("part", [0, 64])
+@pytest.mark.parametrize("name", ["tiny", "llama13b", "llama70b", "shared", "long_fp8", "long_fp8_bs32",
+                                  "long_e5m2_heads", "llama13b_bs8", "llama70b_bs64", "long_fp8_bs8"])
+def test_combine_modes(name, part, mode):
+    """Both ways of combining split sequences on the same inputs: by the
+    last piece to finish inside the partition launch, and by the reduce
+    launch, under both schedules, with a workspace that holds NaN bytes past
+    its arrival counters; the counters are back at zero afterwards."""
+    cfg = SMALL[name]
+    if part % cfg.block_size:
+        part = cfg.block_size
+    print(f"\n[case] combine={mode} {name} part={part}", flush=True)
+    wl = workloads.make(cfg, device="cuda")
+    pre = parity.snapshot(wl)
+    step = DecodeStep(wl, partition_size=part, out_dtype="f32", combine=COMBINES[mode])
+    zb = binding.workspace_zero_bytes(step.args)
+    if step.workspace is not None:
+        step.workspace[zb:].fill_(0xFF)
+    step.run()
+    torch.cuda.synchronize()
+    exp = parity.oracle_step(wl, pre)
+    err = check_step(wl, step, exp, out_dtype="f32")
+    if step.workspace is not None:
+        assert int(step.workspace[:zb].count_nonzero()) == 0, "arrival counters not reset"
+    print(f"[ok] {name} part={part} combine={mode} max abs err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("mode", list(COMBINES))
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "long_fp8", "llama13b_bs64", "long_fp8_bs8"])
+@pytest.mark.parametrize("shape", ["one_long", "many_short"])
+def test_combine_modes_extremes(name, shape, mode):
+    """One sequence split over every work-group (as many pieces as there are
+    work-groups, more than one wave's worth of row groups), and hundreds of
+    short sequences, empty ones included, under both combine modes."""
+    base = SMALL[name]
+    if shape == "one_long":
+        cfg = replace(base, B=1, lens=(20001,), len_range=(), pool_blocks=0)
+    else:
+        lens = tuple(int(x) for x in np.random.default_rng(5).integers(0, 40, 300))
+        cfg = replace(base, B=300, lens=lens, len_range=(), pool_blocks=0)
+    wl, step, exp = run_step(cfg, out_dtype="f32", combine=COMBINES[mode])
+    err = check_step(wl, step, exp, out_dtype="f32")
+    print(f"[ok] {name} {shape} combine={mode} max abs err {err:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["llama13b", "llama70b", "long_fp8"])
