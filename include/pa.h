@@ -223,6 +223,22 @@ pa_status pa_decode_partition(const pa_decode_args* a, void* stream);
  * nothing under PA_COMBINE_IN_LAUNCH or for a fixed schedule with P == 1. */
 pa_status pa_decode_reduce(const pa_decode_args* a, void* stream);
 
+/* pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * arguments and the result are those of pa_decode; workspace and
+ * workspace_bytes are ignored.  Instead the library uses a fixed array of
+ * 32 MiB per GPU, in its own code object, held until the process ends: its
+ * first 256 KiB hold the arrival counters (so B * Hkv may not exceed 65536),
+ * the rest the prefix sums and partial rows that pa_decode_workspace_size
+ * would count for this launch.  Arguments that need more return
+ * PA_ERR_WORKSPACE, with nothing enqueued.  The call allocates and frees
+ * nothing; the first call on a GPU also enqueues one small kernel that
+ * clears the counters.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, or two threads) race and give
+ * wrong results; calls ordered on one stream are safe.  PA_ERR_LAUNCH if the
+ * HIP runtime cannot give the array's address. */
+pa_status pa_decode_no_alloc(const pa_decode_args* a, void* stream);
+
 /* Slot of each sequence's new token (P1 "Sayfalama Nasıl Çalışır", code
  * sketch: position pos goes to block table[pos / bs] at offset pos % bs):
  *   slots[b] = block_tables[b][positions[b] / block_size] * block_size

@@ -101,7 +101,7 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_partition_size.restype = ctypes.c_int32
     L.pa_read_blocks.argtypes = [vp, i32, ctypes.c_size_t, vp, i32, vp, i32, vp]
     L.pa_read_blocks.restype = ctypes.c_int
-    for name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce"):
+    for name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce", "pa_decode_no_alloc"):
         getattr(L, name).argtypes = [argp, vp]
         getattr(L, name).restype = ctypes.c_int
     L.pa_decode_check.argtypes = [argp]
@@ -288,6 +288,16 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0,
         keep = alloc_workspace(a, q.device)
     decode_run(a, stream)
     return out, keep
+
+
+def decode_no_alloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0,
+                    v_scale=1.0, partition_size=0, kv_dtype=None, stream=None, k_scales=None,
+                    v_scales=None, combine=PA_COMBINE_AUTO):
+    """pa_decode_no_alloc on tensors: the library's own fixed workspace, nothing allocated."""
+    a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale,
+                    partition_size, None, kv_dtype, k_scales, v_scales, combine)
+    _check(lib().pa_decode_no_alloc(ctypes.byref(a), _stream(stream)), "pa_decode_no_alloc")
+    return out
 
 
 def slot_mapping(block_tables, positions, block_size, slots, stream=None):

@@ -21,7 +21,7 @@ def L():
 def test_header_declares_the_path_entry_points():
     names = set(binding.declared_functions())
     for n in ("pa_decode", "pa_decode_partition", "pa_decode_reduce", "pa_decode_workspace_size",
-              "pa_decode_workspace_zero_bytes", "pa_decode_partition_size",
+              "pa_decode_workspace_zero_bytes", "pa_decode_partition_size", "pa_decode_no_alloc",
               "pa_decode_check", "pa_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
               "pa_reshape_and_cache_scales", "pa_append_kv",
               "pa_prefill", "pa_prefill_check", "pa_prefill_slot_mapping", "pa_swap_blocks",
@@ -176,6 +176,16 @@ def test_partition_size_query(L):
     a = valid_args(partition_size=64)
     assert L.pa_decode_partition_size(ctypes.byref(a)) == 64
     assert L.pa_decode_partition_size(ctypes.byref(valid_args(Hq=6, Hkv=4))) == 0
+
+
+def test_no_alloc_rejects_before_any_launch(L):
+    """pa_decode_no_alloc validates like pa_decode (no workspace needed) and
+    refuses what its fixed array cannot hold; no HIP call is reached."""
+    assert L.pa_decode_no_alloc(ctypes.byref(valid_args(D=96)), None) == 3
+    assert L.pa_decode_no_alloc(None, None) == 1
+    too_many = valid_args(B=2048, Hq=40, Hkv=40, workspace=0, workspace_bytes=0)   # B*Hkv > 65536
+    assert L.pa_decode_no_alloc(ctypes.byref(too_many), None) == 4
+    assert L.pa_decode_no_alloc(ctypes.byref(valid_args(combine=3)), None) == 2
 
 
 def test_decode_with_bad_args_enqueues_nothing(L):
