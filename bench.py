@@ -2,7 +2,8 @@
 
 One step = the whole hot path over one batch: slot mapping, copy-on-write
 block copies (when the workload shares blocks), the cache write of one new
-token per sequence, the split-K decode partitions and their reduce.  With a
+token per sequence, the split-K decode partitions and the combine of split
+sequences (in the partition launch or a reduce launch, ``--combine``).  With a
 prefill workload (``--workload prefill13b | prefill70b | prefill_fp8``) a
 step is the prefill path instead: slot mapping of every new token, the cache
 write, and causal paged attention, reported in algorithmic TFLOP/s against
@@ -13,7 +14,10 @@ exactly ``--steps`` steps between a synchronise and two HIP events.
 Printed: one JSON line with the metric (effective KV GB/s: bytes of the valid
 tokens' K and V, sum_b L_b * 2 * Hkv * D * elem, per step time), the roofline
 of the dominant kernel (the decode partition kernel, timed with HIP events on
-the stream it runs on) and the CPU oracle timed on a bounded sample.
+the stream it runs on), the per-step time as the median of 5 batches beside
+the contract's single timed batch, the GPU, ROCm release and host, and the
+CPU oracle timed on a bounded sample twice (every affinity core, one
+thread) with the GPU output's max abs error against the oracle on it.
 """
 
 from __future__ import annotations
@@ -193,12 +197,49 @@ def copy_calibration():
     return 0
 
 
-def cpu_baseline(wl, step, budget_s: float):
+def host_facts() -> dict:
+    """Where the CPU baseline ran: affinity cores, os.cpu_count(), the CPU
+    model, NumPy's BLAS backend and its default thread count."""
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "cpu_model": model, "numpy_blas": blas}
+
+
+def cpu_legs(run_leg, budget_s: float) -> dict:
+    """The oracle timed twice on the host: with every core this process may
+    run on as BLAS threads, then with one.  run_leg(threads, budget) returns
+    the leg's result dict; the all-core leg is the reported value."""
+    host = host_facts()
+    n = host["affinity_cores"]
+    many = run_leg(n, budget_s)
+    one = run_leg(1, budget_s)
+    out = dict(many)
+    out["cores"] = n
+    out["single_thread"] = {k: one[k] for k in ("value", "seconds", "sample") if k in one}
+    out["host"] = host
+    return out
+
+
+def cpu_baseline(wl, step, budget_s: float, check=None):
     """The oracle as it stands, on host copies of the pools, over as many
-    sequences as fit in ``budget_s`` seconds (at least one)."""
+    sequences as fit in ``budget_s`` seconds (at least one), with every
+    affinity core and with one BLAS thread.  ``check`` receives the oracle's
+    output for the sequences it computed (max abs error of the GPU's)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import paged
+    from paged_kv_cache_412_amd.workloads import ELEM_BYTES
     from tests import parity
 
     cfg = wl.cfg
@@ -207,29 +248,35 @@ def cpu_baseline(wl, step, budget_s: float):
     q = parity.widen(parity.storage(wl.q), cfg.q_dtype)
     tab = step.tables_np
     order = np.random.default_rng(0).permutation(cfg.B)
-    done, nbytes = [], 0
-    from paged_kv_cache_412_amd.workloads import ELEM_BYTES
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for b in order:
-            paged.decode(q, k, v, tab, wl.seq_lens, cfg.block_size, wl.scale, seqs=[int(b)],
-                         widen_k=lambda x: parity.widen(x, cfg.kv_dtype, wl.k_scale),
-                         widen_v=lambda x: parity.widen(x, cfg.kv_dtype, wl.v_scale))
-            done.append(int(b))
-            nbytes += int(wl.seq_lens[b]) * 2 * cfg.Hkv * cfg.D * ELEM_BYTES[cfg.kv_dtype]
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} of {cfg.B} sequences (all {cfg.Hq} heads), {dt:.1f} s, "
-                      f"fp64 NumPy, BLAS limited to 1 thread",
-            "seconds": round(dt, 3), "seq_layers_per_s": round(len(done) / dt, 3)}
+
+    def leg(threads, budget):
+        done, nbytes = [], 0
+        outs = []
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            for b in order:
+                o = paged.decode(q, k, v, tab, wl.seq_lens, cfg.block_size, wl.scale, seqs=[int(b)],
+                                 widen_k=lambda x: parity.widen(x, cfg.kv_dtype, wl.k_scale),
+                                 widen_v=lambda x: parity.widen(x, cfg.kv_dtype, wl.v_scale))
+                outs.append(o[int(b)])
+                done.append(int(b))
+                nbytes += int(wl.seq_lens[b]) * 2 * cfg.Hkv * cfg.D * ELEM_BYTES[cfg.kv_dtype]
+                if time.perf_counter() - t0 >= budget:
+                    break
+            dt = time.perf_counter() - t0
+        if check is not None and threads != 1:
+            check(done, np.stack(outs))
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+                "sample": f"{len(done)} of {cfg.B} sequences (all {cfg.Hq} heads), {dt:.1f} s, "
+                          f"fp64 NumPy, BLAS limited to {threads} thread(s)",
+                "seconds": round(dt, 3), "seq_layers_per_s": round(len(done) / dt, 3)}
+    return cpu_legs(leg, budget_s)
 
 
-def cpu_baseline_prefill(wl, step, budget_s: float):
+def cpu_baseline_prefill(wl, step, budget_s: float, check=None):
     """The oracle as it stands over a bounded sample of new tokens: each
     sampled token's attention as a one-row prefill over its sequence's first
-    p + 1 tokens, all query heads."""
+    p + 1 tokens, all query heads; every affinity core, then one thread."""
     from threadpoolctl import threadpool_limits
 
     from oracle import paged
@@ -242,24 +289,86 @@ def cpu_baseline_prefill(wl, step, budget_s: float):
     tab = step.tables_np.astype(np.int64)
     rows = np.random.default_rng(0).permutation(wl.T)
     owner = np.searchsorted(wl.q_starts, rows, side="right") - 1
-    done, flops = 0, 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for r, b in zip(rows, owner):
-            pos = int(wl.seq_lens[b]) - int(wl.news[b]) + int(r - wl.q_starts[b])
-            paged.prefill(q[r:r + 1], k, v, tab[b:b + 1], np.array([pos + 1]), np.array([0, 1]),
-                          cfg.block_size, wl.scale,
-                          widen_k=lambda x: parity.widen(x, cfg.kv_dtype, wl.k_scale),
-                          widen_v=lambda x: parity.widen(x, cfg.kv_dtype, wl.v_scale))
-            done += 1
-            flops += 4 * cfg.D * cfg.Hq * (pos + 1)
-            if time.perf_counter() - t0 >= budget_s:
+
+    def leg(threads, budget):
+        done, flops = [], 0
+        outs = []
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            for r, b in zip(rows, owner):
+                pos = int(wl.seq_lens[b]) - int(wl.news[b]) + int(r - wl.q_starts[b])
+                o = paged.prefill(q[r:r + 1], k, v, tab[b:b + 1], np.array([pos + 1]), np.array([0, 1]),
+                                  cfg.block_size, wl.scale,
+                                  widen_k=lambda x: parity.widen(x, cfg.kv_dtype, wl.k_scale),
+                                  widen_v=lambda x: parity.widen(x, cfg.kv_dtype, wl.v_scale))
+                done.append(int(r))
+                outs.append(o[0])
+                flops += 4 * cfg.D * cfg.Hq * (pos + 1)
+                if time.perf_counter() - t0 >= budget:
+                    break
+            dt = time.perf_counter() - t0
+        if check is not None and threads != 1:
+            check(done, np.stack(outs))
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+                "sample": f"{len(done)} of {wl.T} new tokens (all {cfg.Hq} heads), {dt:.1f} s, "
+                          f"fp64 NumPy, BLAS limited to {threads} thread(s)",
+                "seconds": round(dt, 3)}
+    return cpu_legs(leg, budget_s)
+
+
+def gpu_facts() -> dict:
+    """The GPU and the ROCm release the numbers come from."""
+    import torch
+    ver = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                ver = f.read().strip()
                 break
-        dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {wl.T} new tokens (all {cfg.Hq} heads), {dt:.1f} s, "
-                      f"fp64 NumPy, BLAS limited to 1 thread",
-            "seconds": round(dt, 3)}
+        except OSError:
+            continue
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu_name": torch.cuda.get_device_name(0), "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm_version": ver,
+            "hip_runtime": torch.version.hip}
+
+
+def median_batches(run_step, stream, batches=5, steps=100) -> dict:
+    """Per-step time as the median of `batches` batches of `steps` back-to-back
+    steps (events on the stream around each batch)."""
+    import torch
+    ms = []
+    for _ in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            run_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / steps)
+    return {"median_ms_per_step": round(float(np.median(ms)), 5),
+            "batches_ms_per_step": [round(x, 5) for x in ms], "steps_per_batch": steps}
+
+
+def error_check(gpu_out, kv_dtype, out_dtype):
+    """A `check` callback for the CPU legs: max abs error of the GPU output
+    (first axis: sequences or new-token rows) against the oracle on the
+    sampled rows, and whether every element is
+    within the parity tolerance (that of the KV dtype plus half an ulp of
+    the output dtype)."""
+    from tests import parity
+    result = {}
+
+    def check(rows, ref):
+        g = parity.gpu_out(gpu_out)[rows]
+        err = np.abs(g - ref)
+        p, emin = parity.OUT_FORMAT[out_dtype]
+        from oracle import numerics
+        bound = parity.TOL[kv_dtype] + numerics.half_ulp(ref, p, emin)
+        result.update({"value": float(np.max(err)), "within_tolerance": bool(np.all(err <= bound)),
+                       "tolerance": parity.TOL[kv_dtype], "rows": len(rows)})
+    return check, result
 
 
 def bench_prefill(args, cfg):
@@ -297,6 +406,7 @@ def bench_prefill(args, cfg):
     torch.cuda.synchronize()
     stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, s in enumerate(stages)}
+    batches = median_batches(step.run, stream, steps=20)
     flops = prefill_flops(wl)
     tflops = flops / (ms_step * 1e-3) / 1e12
     attn_ms = stage_ms["attention"]
@@ -325,6 +435,8 @@ def bench_prefill(args, cfg):
         "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
         "flops_per_step": flops,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "median_of_batches": dict(batches, tflops=round(flops / (batches["median_ms_per_step"] * 1e-3) / 1e12, 2)),
+        "system": gpu_facts(),
         "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(kernel, cfg.name),
@@ -333,7 +445,9 @@ def bench_prefill(args, cfg):
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline_prefill(wl, step, args.cpu_budget)
+        check, err = error_check(step.out, cfg.kv_dtype, cfg.out_dtype)
+        out["cpu_baseline"] = cpu_baseline_prefill(wl, step, args.cpu_budget, check)
+        out["max_abs_err_vs_oracle"] = err
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -549,7 +663,8 @@ def main(argv=None):
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--combine", choices=["auto", "in_launch", "reduce"], default="auto",
                     help="who combines sequences split across work-groups (pa_decode_args.combine)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle work per CPU leg (all cores, then one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="measure the block-gather read ceiling and torch's copy rate, then exit")
@@ -617,6 +732,7 @@ def main(argv=None):
     stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, s in enumerate(stages)}
 
+    batches = median_batches(step.run, stream)
     nbytes = kv_bytes(wl)
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     part_ms = stage_ms["decode_partition"]
@@ -649,6 +765,8 @@ def main(argv=None):
         "seq_layers_per_s": round(cfg.B / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": nbytes,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "median_of_batches": dict(batches, gbs=round(nbytes / (batches["median_ms_per_step"] * 1e-3) / 1e9, 2)),
+        "system": gpu_facts(),
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": nbytes, "avg_launch_ms": round(part_ms, 5),
@@ -659,7 +777,9 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, step, args.cpu_budget)
+        check, err = error_check(step.out, cfg.kv_dtype, cfg.out_dtype)
+        out["cpu_baseline"] = cpu_baseline(wl, step, args.cpu_budget, check)
+        out["max_abs_err_vs_oracle"] = err
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
