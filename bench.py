@@ -406,7 +406,7 @@ def bench_prefill(args, cfg):
     torch.cuda.synchronize()
     stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, s in enumerate(stages)}
-    batches = median_batches(step.run, stream, steps=20)
+    batches = median_batches(step.run, stream, args.batches, steps=20) if args.batches else None
     flops = prefill_flops(wl)
     tflops = flops / (ms_step * 1e-3) / 1e12
     attn_ms = stage_ms["attention"]
@@ -435,7 +435,8 @@ def bench_prefill(args, cfg):
         "tokens_per_s": round(wl.T / (ms_step * 1e-3), 1),
         "flops_per_step": flops,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
-        "median_of_batches": dict(batches, tflops=round(flops / (batches["median_ms_per_step"] * 1e-3) / 1e12, 2)),
+        "median_of_batches": (dict(batches, tflops=round(flops / (batches["median_ms_per_step"] * 1e-3) / 1e12, 2))
+                              if batches else None),
         "system": gpu_facts(),
         "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -666,6 +667,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=8.0,
                     help="seconds of oracle work per CPU leg (all cores, then one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--batches", type=int, default=5,
+                    help="extra batches of 100 steps for the median step time (0: none)")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="measure the block-gather read ceiling and torch's copy rate, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -732,7 +735,7 @@ def main(argv=None):
     stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, s in enumerate(stages)}
 
-    batches = median_batches(step.run, stream)
+    batches = median_batches(step.run, stream, args.batches) if args.batches else None
     nbytes = kv_bytes(wl)
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     part_ms = stage_ms["decode_partition"]
@@ -765,7 +768,8 @@ def main(argv=None):
         "seq_layers_per_s": round(cfg.B / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": nbytes,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
-        "median_of_batches": dict(batches, gbs=round(nbytes / (batches["median_ms_per_step"] * 1e-3) / 1e9, 2)),
+        "median_of_batches": (dict(batches, gbs=round(nbytes / (batches["median_ms_per_step"] * 1e-3) / 1e9, 2))
+                              if batches else None),
         "system": gpu_facts(),
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

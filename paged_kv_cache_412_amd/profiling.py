@@ -14,6 +14,11 @@ Three steps, run from the repository root:
     ``MfmaUtil`` (matrix-core busy cycles over active cycles times SIMDs, in
     percent) and ``MfmaFlops`` (matrix-core operations issued, 512 flops per
     MOP), for the kernels that run on the matrix cores.
+``python -m paged_kv_cache_412_amd.profiling vmem --workload W --out DIR``
+    (GPU) one ``rocprofv3 --pmc`` pass per vector-memory counter
+    (VMEM_COUNTERS): address-unit busy and stall cycles, vector-L1 stalls,
+    vector-memory read instructions, waves, and the GPU busy cycles they are
+    shares of.
 ``python -m paged_kv_cache_412_amd.profiling summarize --workload W --dir DIR``
     (any machine) reads those CSVs and writes
     ``profiles/<kernel>_<workload>.md`` (per-kernel durations; HBM bytes per
@@ -47,7 +52,7 @@ PMC_STEPS, PMC_WARMUP = 3, 1
 
 def _bench_cmd(workload: str, steps: int, warmup: int, extra=()) -> list:
     return [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--steps",
-            str(steps), "--warmup", str(warmup), "--no-cpu-baseline", *extra]
+            str(steps), "--warmup", str(warmup), "--no-cpu-baseline", "--batches", "0", *extra]
 
 
 def _run(cmd: list, limit: int) -> None:
@@ -80,6 +85,23 @@ def mfma(workload: str, out: str) -> None:
               "--", *_bench_cmd(workload, PMC_STEPS, PMC_WARMUP)], 180)
 
 
+# The vector-memory path of the decode kernels: how busy the per-CU address
+# unit (TA) is, how often the vector L1 (TCP, "TC" to the TA) holds it up,
+# and how many vector-memory read instructions carry the bytes.  One counter
+# per pass.  GRBM_GUI_ACTIVE (GPU busy cycles of the dispatch) normalises the
+# others: TA_BUSY_avr is already a mean over the TA instances, the *_sum
+# counters add up one instance per compute unit.
+VMEM_COUNTERS = ("GRBM_GUI_ACTIVE", "TA_BUSY_avr", "TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+                 "TA_DATA_STALLED_BY_TC_CYCLES_sum", "TCP_PENDING_STALL_CYCLES_sum",
+                 "TCP_TCR_TCP_STALL_CYCLES_sum", "SQ_INSTS_VMEM_RD", "SQ_WAVES")
+
+
+def vmem(workload: str, out: str) -> None:
+    for counter in VMEM_COUNTERS:
+        _run([ROCPROF, "--pmc", counter, "-f", "csv", "-d", out, "-o", f"pmc_{counter}_{workload}",
+              "--", *_bench_cmd(workload, PMC_STEPS, PMC_WARMUP)], 180)
+
+
 def _find(d: str, pattern: str):
     hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
     return hits[-1] if hits else None
@@ -99,6 +121,19 @@ def _counter_per_dispatch(path: str, counter: str) -> dict:
     for (name, _), v in per.items():
         out.setdefault(name, []).append(v)
     return out
+
+
+def _gpu_shape(agent_info: str):
+    """(XCD count, compute-unit count) of the GPU agent in a rocprofv3
+    agent-info CSV; (8, 256) when the file is missing."""
+    try:
+        with open(agent_info, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Agent_Type", "").upper().endswith("GPU"):
+                    return int(row["Num_Xcc"]), int(row["Cu_Count"])
+    except (OSError, KeyError, ValueError):
+        pass
+    return 8, 256
 
 
 def _short(name: str) -> str:
@@ -245,6 +280,36 @@ def summarize(workload: str, d: str) -> None:
         if rate_us:
             lines.append(f"| issued matrix-core TFLOP/s at the timed launches' mean duration | "
                          f"{issued / (rate_us * 1e-6) / 1e12:.1f} |")
+    vm = {c: _find(d, f"pmc_{c}_{workload}_counter_collection.csv") for c in VMEM_COUNTERS}
+    if all(vm.values()):
+        val = {c: kernel_avg(vm[c], c)[0] for c in VMEM_COUNTERS}
+        xcc, cus = _gpu_shape(vm["GRBM_GUI_ACTIVE"].replace("_counter_collection.csv", "_agent_info.csv"))
+        # GRBM_GUI_ACTIVE adds one busy-cycle count per XCD: the dispatch's
+        # own length in cycles is that over the XCD count.
+        cyc = val["GRBM_GUI_ACTIVE"] / xcc
+        rec["vmem"] = val
+        lines += ["", "## Vector-memory path (rocprofv3 --pmc, one counter per pass)", "", "```",
+                  f"python -m paged_kv_cache_412_amd.profiling vmem --workload {workload} --out gpurun_out/prof",
+                  "  # = rocprofv3 --pmc <counter> -f csv ... -- python3 bench.py --workload "
+                  f"{workload} --steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline --batches 0",
+                  "  #   for each of: " + ", ".join(VMEM_COUNTERS), "```", "",
+                  f"Per `{kernel}` dispatch (mean over the run's dispatches).  GRBM_GUI_ACTIVE is summed "
+                  f"over the {xcc} XCDs; shares are of the dispatch's length in cycles (that sum over "
+                  f"{xcc}), and of that length times {cus} compute units for the summed counters.", "",
+                  "| counter | per dispatch | share |", "|---|---|---|",
+                  f"| GRBM_GUI_ACTIVE (cycles, all XCDs) | {val['GRBM_GUI_ACTIVE']:.4g} | "
+                  f"{cyc:.4g} cycles per XCD |",
+                  f"| TA_BUSY_avr: address unit busy | {val['TA_BUSY_avr']:.4g} | "
+                  f"{100 * val['TA_BUSY_avr'] / cyc:.1f} % |"]
+        for c, what in (("TA_ADDR_STALLED_BY_TC_CYCLES_sum", "address unit stalled by the vector L1 (addresses)"),
+                        ("TA_DATA_STALLED_BY_TC_CYCLES_sum", "address unit stalled by the vector L1 (data)"),
+                        ("TCP_PENDING_STALL_CYCLES_sum", "vector L1 stalled on pending misses"),
+                        ("TCP_TCR_TCP_STALL_CYCLES_sum", "vector L1 stalled by the L2 request path")):
+            lines.append(f"| {c}: {what} | {val[c]:.4g} | {100 * val[c] / (cus * cyc):.1f} % |")
+        insts = val["SQ_INSTS_VMEM_RD"]
+        lines += [f"| SQ_INSTS_VMEM_RD: vector-memory read instructions | {insts:.4g} | "
+                  f"{kvb / insts:.0f} algorithmic bytes per instruction |",
+                  f"| SQ_WAVES | {val['SQ_WAVES']:.4g} | |"]
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{kernel}_{workload}.md"), "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
@@ -294,7 +359,7 @@ def bench_prefill_flops(cfg) -> int:
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("step", choices=["trace", "pmc", "mfma", "summarize"])
+    ap.add_argument("step", choices=["trace", "pmc", "mfma", "vmem", "summarize"])
     ap.add_argument("--workload", default="llama13b")
     ap.add_argument("--out", default="gpurun_out/prof")
     ap.add_argument("--dir", default="gpurun_out/prof")
@@ -305,6 +370,8 @@ def main(argv=None) -> int:
         pmc(a.workload, a.out)
     elif a.step == "mfma":
         mfma(a.workload, a.out)
+    elif a.step == "vmem":
+        vmem(a.workload, a.out)
     else:
         summarize(a.workload, a.dir)
     return 0
