@@ -162,66 +162,104 @@ __device__ __forceinline__ void for_each_segment(const DecodeParams& p, const in
   }
 }
 
-// Walk blocks jbeg..jend-1 of a partition in units of UB consecutive blocks,
+// Walk blocks jbeg..jend-1 of a segment in units of UB consecutive blocks,
 // with ST register sets in rotation: the loads of the next ST-1 units are in
-// flight while a unit is consumed.  Block ids come 64 at a time, one per lane,
-// from a single vector load, and each unit takes its ids with v_readlane, so
-// no scalar load sits between two units.
+// flight while a unit is consumed.  A unit's block-table entries are fetched
+// ST units before its loads are issued, by one small vector load per unit
+// (lanes 0..UB-1) through the same in-order memory queue as the K/V loads: the
+// stream never stops to read the table, and the ids reach the scalar unit by
+// v_readlane, so no scalar load sits between two units.  Only the entries of
+// the segment's first ST-1 units are waited for as soon as they are fetched.
 //
 // `load(ids, buf)` issues the loads of the unit's UB block ids into buf,
 // through buffer resources that are empty for ids < 0: ids outside the pool
-// and the look-ahead past the partition's end load nothing but still issue
-// the same instructions.  Every path through the loop therefore has the same
-// loads in flight, and the compiler's wait counts stay exact (a load issued on
-// one path only would force it to wait for all loads, the look-ahead
-// included).  `consume(j0, ok, buf)` folds logical blocks j0..j0+UB-1 into the
-// running state; bit u of ok is clear for a block that counts no valid token
-// (an id outside the pool, or past the partition's end).
+// and the look-ahead past the segment's end load nothing but still issue
+// the same instructions, as does the table fetch past the segment's end.
+// Every path through the loop therefore has the same loads in flight, and the
+// compiler's wait counts stay exact (a load issued on one path only would
+// force it to wait for all loads, the look-ahead included).
+// `consume(j0, ok, buf)` folds logical blocks j0..j0+UB-1 into the running
+// state; bit u of ok is clear for a block that counts no valid token (an id
+// outside the pool, or past the segment's end).
 // Logical block j is sub-block j % 2^sub of table entry j / 2^sub; its id
 // is entry * 2^sub + j % 2^sub (blocks of the pool seen as 2^sub smaller ones).
-template <int ST, int UB, typename Buf, typename Load, typename Consume>
+//
+// SYNC > 0 (a power of two): every SYNC units the waves of the work-group meet
+// at a barrier.  The waves walk the same blocks (one KV head each), and
+// without it the oldest waves win the memory-issue arbitration and run ahead:
+// the blocks in flight then spread over more of the pool, and the last waves
+// finish alone.  Every wave of the work-group must walk the same segments
+// (waves that have exited are not waited for).
+template <int ST, int UB, int SYNC, typename Buf, typename Load, typename Consume>
 __device__ __forceinline__ void walk_blocks(const int32_t* table, const PartitionSpan& s,
                                             int num_blocks, int sub, int lane, Load&& load,
                                             Consume&& consume) {
-  for (int base = s.jbeg; base < s.jend; base += 64) {
-    const int cnt = min(64, s.jend - base);
-    int ids = -1;
-    if (lane < cnt) {
-      const int j = base + lane;
-      const int e = table[j >> sub];
-      // entries outside the pool (num_blocks >> sub table blocks) count none
-      ids = static_cast<unsigned>(e) < static_cast<unsigned>(num_blocks >> sub)
-                ? (e << sub) | (j & ((1 << sub) - 1))
-                : -1;
-    }
-    const int units = (cnt + UB - 1) / UB;
-    // ids of unit k (k uniform; 64 is a multiple of UB, so a unit never
-    // straddles two 64-block chunks)
-    auto unit_ids = [&](int k, int (&out)[UB]) {
+  // The span and the table row are the same in every lane, but they come
+  // from loads through a generic pointer (the schedule's prefix sums), which
+  // the compiler cannot prove uniform: without these the block ids would be
+  // per-lane values and every buffer load a loop over distinct resources.
+  const int jbeg = __builtin_amdgcn_readfirstlane(s.jbeg);
+  const int jend = __builtin_amdgcn_readfirstlane(s.jend);
+  const int32_t* const row = uniform_ptr(table);
+  if (jend <= jbeg) return;
+  const int units = (jend - jbeg + UB - 1) / UB;
+  // the table entries the segment names; a fetch at or past them reads nothing
+  const uint32_t tbytes = static_cast<uint32_t>(((jend - 1) >> sub) + 1) * 4u;
+  const __amdgpu_buffer_rsrc_t trs = block_rsrc(row, tbytes);
+  const unsigned pool_entries = static_cast<unsigned>(num_blocks >> sub);
+  const int submask = (1 << sub) - 1;
+  // A fetch reads the table entries of logical blocks jbeg + first + l in
+  // lanes l < n (entry (jbeg + first) / 2^sub + l: consecutive entries, as
+  // many as the blocks span); the other lanes point past the resource.
+  auto fetch = [&](int first, int n) -> int {
+    const int e0 = (jbeg + first) >> sub;
+    const int off = lane < n ? (e0 + lane) * 4 : static_cast<int>(tbytes);
+    return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(trs, off, 0, 0));
+  };
+  // ids of unit k from entries fetched from logical block jbeg + first (k,
+  // first uniform); returns the unit's ok bits
+  auto ids_of = [&](int k, int e, int first, int (&id)[UB]) -> unsigned {
+    const int e0 = (jbeg + first) >> sub;
+    unsigned ok = 0;
 #pragma unroll
-      for (int u = 0; u < UB; ++u) out[u] = k < 64 / UB ? __builtin_amdgcn_readlane(ids, k * UB + u) : -1;
-    };
-    Buf buf[ST];
+    for (int u = 0; u < UB; ++u) {
+      const int j = jbeg + k * UB + u;
+      const int x = __builtin_amdgcn_readlane(e, (j >> sub) - e0);
+      const bool valid = j < jend && static_cast<unsigned>(x) < pool_entries;
+      id[u] = valid ? (x << sub) | (j & submask) : -1;
+      ok |= (valid ? 1u : 0u) << u;
+    }
+    return ok;
+  };
+  Buf buf[ST];
+  unsigned ok[ST];
+  int tv[ST];  // at unit ii, slot ii % ST: the entries of unit ii + ST - 1
+  {
+    const int e = fetch(0, (ST - 1) * UB);
 #pragma unroll
     for (int u = 0; u < ST - 1; ++u) {
       int id[UB];
-      unit_ids(u, id);
+      ok[u] = ids_of(u, e, 0, id);
       load(id, buf[u]);
     }
-    for (int i = 0; i < units; i += ST) {
 #pragma unroll
-      for (int u = 0; u < ST; ++u) {
-        const int ii = i + u;
-        if (ii >= units) break;
-        int nid[UB], cid[UB];
-        unit_ids(ii + ST - 1, nid);
-        load(nid, buf[(u + ST - 1) % ST]);
-        unit_ids(ii, cid);
-        unsigned ok = 0;
+    for (int u = 0; u < ST; ++u) tv[u] = fetch((u + ST - 1) * UB, UB);
+  }
+  static_assert(SYNC == 0 || ((SYNC & (SYNC - 1)) == 0 && SYNC % ST == 0), "barrier interval");
+  for (int i = 0; i < units; i += ST) {
+    if constexpr (SYNC > 0) {
+      if ((i & (SYNC - 1)) == 0) __builtin_amdgcn_s_barrier();
+    }
 #pragma unroll
-        for (int b = 0; b < UB; ++b) ok |= (cid[b] >= 0 ? 1u : 0u) << b;
-        consume(base + ii * UB, ok, buf[u]);
-      }
+    for (int u = 0; u < ST; ++u) {
+      const int ii = i + u;
+      if (ii >= units) break;
+      const int nu = (u + ST - 1) % ST;
+      int id[UB];
+      ok[nu] = ids_of(ii + ST - 1, tv[u], (ii + ST - 1) * UB, id);
+      tv[u] = fetch((ii + 2 * ST - 1) * UB, UB);
+      load(id, buf[nu]);
+      consume(jbeg + ii * UB, ok[u], buf[u]);
     }
   }
 }
@@ -281,8 +319,12 @@ __device__ __forceinline__ void store_out_n(void* base, size_t i, const float* v
 // keeps each partial region under 2 GiB, so 32-bit byte offsets reach it.
 constexpr int kCoherent = 16;  // sc1: device scope
 
+// (The workspace pointers are kernel arguments, but the combine after the
+// walk reads them back from the kernel-argument segment through a copy that
+// the compiler cannot prove uniform.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(uniform_ptr(base)), 0, 0x7fffffff,
+                                           0x00020000);
 }
 // N partial sums of row r from element d0 (16-byte stores), and the row's m
 // and l from the lane that holds element 0; cache policy CP.

@@ -307,7 +307,9 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
 
     const int32_t* table =
         p.block_tables + static_cast<size_t>(b) * (p.max_blocks_per_seq >> p.sub_shift);
-    walk_blocks<ST, UB, Raw>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
+    // waves meet every 8 units (8-bit caches) or 4 (16-bit), the intervals
+    // that measured fastest for each
+    walk_blocks<ST, UB, (FP8 ? 8 : 4), Raw>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
 
     // l of query lo summed over the four lane groups; every lane then fetches
     // m and l of the queries whose accumulators it holds (4*grp + i)

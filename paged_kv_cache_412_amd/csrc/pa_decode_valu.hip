@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kValuHeads * 64) void decode_valu_kernel(const Deco
 
     const int32_t* table =
         p.block_tables + static_cast<size_t>(b) * (p.max_blocks_per_seq >> p.sub_shift);
-    walk_blocks<ST, UB, Buf>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
+    walk_blocks<ST, UB, 0, Buf>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
 
     // merge the per-lane states of the TPL row groups that own the same
     // chunk; the butterfly leaves the merged state in every lane

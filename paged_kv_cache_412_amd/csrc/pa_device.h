@@ -49,6 +49,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base, u
                                            0x00020000);
 }
 
+// A pointer that is the same in every lane, made provably so (v_readfirstlane
+// of both halves; free when it already sits in scalar registers).  Buffer
+// resources need one: built from a value the compiler takes as per-lane,
+// every buffer access becomes a loop over the distinct resources.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t u = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u >> 32)));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Cache-policy bits of a buffer load: non-temporal (the pools are read once
 // per decode step; L2 and the MALL are left to the block tables and queries).
 constexpr int kLoadNT = 2;
