@@ -162,63 +162,49 @@ __device__ __forceinline__ void for_each_segment(const DecodeParams& p, const in
   }
 }
 
-// Walk blocks jbeg..jend-1 of a segment in units of UB consecutive blocks,
-// with ST register sets in rotation: the loads of the next ST-1 units are in
-// flight while a unit is consumed.  A unit's block-table entries are fetched
-// ST units before its loads are issued, by one small vector load per unit
-// (lanes 0..UB-1) through the same in-order memory queue as the K/V loads: the
-// stream never stops to read the table, and the ids reach the scalar unit by
-// v_readlane, so no scalar load sits between two units.  Only the entries of
-// the segment's first ST-1 units are waited for as soon as they are fetched.
-//
-// `load(ids, buf)` issues the loads of the unit's UB block ids into buf,
-// through buffer resources that are empty for ids < 0: ids outside the pool
-// and the look-ahead past the segment's end load nothing but still issue
-// the same instructions, as does the table fetch past the segment's end.
-// Every path through the loop therefore has the same loads in flight, and the
-// compiler's wait counts stay exact (a load issued on one path only would
-// force it to wait for all loads, the look-ahead included).
-// `consume(j0, ok, buf)` folds logical blocks j0..j0+UB-1 into the running
-// state; bit u of ok is clear for a block that counts no valid token (an id
-// outside the pool, or past the segment's end).
-// Logical block j is sub-block j % 2^sub of table entry j / 2^sub; its id
-// is entry * 2^sub + j % 2^sub (blocks of the pool seen as 2^sub smaller ones).
-//
-// SYNC > 0 (a power of two): every SYNC units the waves of the work-group meet
-// at a barrier.  The waves walk the same blocks (one KV head each), and
-// without it the oldest waves win the memory-issue arbitration and run ahead:
-// the blocks in flight then spread over more of the pool, and the last waves
-// finish alone.  Every wave of the work-group must walk the same segments
-// (waves that have exited are not waited for).
-template <int ST, int UB, int SYNC, typename Buf, typename Load, typename Consume>
-__device__ __forceinline__ void walk_blocks(const int32_t* table, const PartitionSpan& s,
-                                            int num_blocks, int sub, int lane, Load&& load,
-                                            Consume&& consume) {
+// The block-table side of a walk over blocks jbeg..jend-1 of a segment, in
+// units of UB consecutive blocks.  Logical block j is sub-block j % 2^sub of
+// table entry j / 2^sub; its id is entry * 2^sub + j % 2^sub (blocks of the
+// pool seen as 2^sub smaller ones).  Entries are fetched by small vector
+// loads through the same in-order memory queue as the K/V loads and reach
+// the scalar unit by v_readlane, so no scalar load sits between two units.
+template <int UB>
+struct TableCursor {
+  int jbeg, jend, sub, lane, submask;
+  unsigned pool_entries;
+  uint32_t tbytes;
+  __amdgpu_buffer_rsrc_t trs;
+
   // The span and the table row are the same in every lane, but they come
   // from loads through a generic pointer (the schedule's prefix sums), which
-  // the compiler cannot prove uniform: without these the block ids would be
-  // per-lane values and every buffer load a loop over distinct resources.
-  const int jbeg = __builtin_amdgcn_readfirstlane(s.jbeg);
-  const int jend = __builtin_amdgcn_readfirstlane(s.jend);
-  const int32_t* const row = uniform_ptr(table);
-  if (jend <= jbeg) return;
-  const int units = (jend - jbeg + UB - 1) / UB;
-  // the table entries the segment names; a fetch at or past them reads nothing
-  const uint32_t tbytes = static_cast<uint32_t>(((jend - 1) >> sub) + 1) * 4u;
-  const __amdgpu_buffer_rsrc_t trs = block_rsrc(row, tbytes);
-  const unsigned pool_entries = static_cast<unsigned>(num_blocks >> sub);
-  const int submask = (1 << sub) - 1;
-  // A fetch reads the table entries of logical blocks jbeg + first + l in
-  // lanes l < n (entry (jbeg + first) / 2^sub + l: consecutive entries, as
-  // many as the blocks span); the other lanes point past the resource.
-  auto fetch = [&](int first, int n) -> int {
+  // the compiler cannot prove uniform: without the v_readfirstlane the block
+  // ids would be per-lane values and every buffer load a loop over distinct
+  // resources.
+  __device__ __forceinline__ TableCursor(const int32_t* table, const PartitionSpan& s,
+                                         int num_blocks, int sub_, int lane_)
+      : jbeg(__builtin_amdgcn_readfirstlane(s.jbeg)),
+        jend(__builtin_amdgcn_readfirstlane(s.jend)),
+        sub(sub_),
+        lane(lane_),
+        submask((1 << sub_) - 1),
+        pool_entries(static_cast<unsigned>(num_blocks >> sub_)) {
+    // the table entries the segment names; a fetch at or past them reads nothing
+    tbytes = jend > jbeg ? static_cast<uint32_t>(((jend - 1) >> sub) + 1) * 4u : 0u;
+    trs = block_rsrc(uniform_ptr(table), tbytes);
+  }
+  __device__ __forceinline__ int units() const { return jend > jbeg ? (jend - jbeg + UB - 1) / UB : 0; }
+  // the table entries of logical blocks jbeg + first + l in lanes l < n
+  // (entry (jbeg + first) / 2^sub + l: consecutive entries, as many as the
+  // blocks span); the other lanes point past the resource
+  __device__ __forceinline__ int fetch(int first, int n) const {
     const int e0 = (jbeg + first) >> sub;
     const int off = lane < n ? (e0 + lane) * 4 : static_cast<int>(tbytes);
     return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(trs, off, 0, 0));
-  };
-  // ids of unit k from entries fetched from logical block jbeg + first (k,
-  // first uniform); returns the unit's ok bits
-  auto ids_of = [&](int k, int e, int first, int (&id)[UB]) -> unsigned {
+  }
+  // ids of unit k from entries e fetched from logical block jbeg + first (k,
+  // first uniform); returns the unit's ok bits: bit u is clear for a block
+  // that counts no valid token (an id outside the pool, or past the end)
+  __device__ __forceinline__ unsigned ids_of(int k, int e, int first, int (&id)[UB]) const {
     const int e0 = (jbeg + first) >> sub;
     unsigned ok = 0;
 #pragma unroll
@@ -230,20 +216,51 @@ __device__ __forceinline__ void walk_blocks(const int32_t* table, const Partitio
       ok |= (valid ? 1u : 0u) << u;
     }
     return ok;
-  };
+  }
+};
+
+// Walk a segment with ST register sets in rotation: the loads of the next
+// ST-1 units are in flight while a unit is consumed.  A unit's table entries
+// are fetched ST units before its loads are issued (one small load per unit,
+// lanes 0..UB-1), so the stream never stops to read the table; only the
+// entries of the segment's first ST-1 units are waited for at once.
+//
+// `load(ids, buf)` issues the loads of the unit's UB block ids into buf,
+// through buffer resources that are empty for ids < 0: ids outside the pool
+// and the look-ahead past the segment's end load nothing but still issue
+// the same instructions, as does the table fetch past the segment's end.
+// Every path through the loop therefore has the same loads in flight, and the
+// compiler's wait counts stay exact (a load issued on one path only would
+// force it to wait for all loads, the look-ahead included).
+// `consume(j0, ok, buf)` folds logical blocks j0..j0+UB-1 into the running
+// state, with the unit's ok bits.
+//
+// SYNC > 0 (a power of two): every SYNC units the waves of the work-group meet
+// at a barrier.  The waves walk the same blocks (one KV head each), and
+// without it the oldest waves win the memory-issue arbitration and run ahead:
+// the blocks in flight then spread over more of the pool, and the last waves
+// finish alone.  Every wave of the work-group must walk the same segments
+// (waves that have exited are not waited for).
+template <int ST, int UB, int SYNC, typename Buf, typename Load, typename Consume>
+__device__ __forceinline__ void walk_blocks(const int32_t* table, const PartitionSpan& s,
+                                            int num_blocks, int sub, int lane, Load&& load,
+                                            Consume&& consume) {
+  const TableCursor<UB> tc(table, s, num_blocks, sub, lane);
+  const int units = tc.units();
+  if (units == 0) return;
   Buf buf[ST];
   unsigned ok[ST];
   int tv[ST];  // at unit ii, slot ii % ST: the entries of unit ii + ST - 1
   {
-    const int e = fetch(0, (ST - 1) * UB);
+    const int e = tc.fetch(0, (ST - 1) * UB);
 #pragma unroll
     for (int u = 0; u < ST - 1; ++u) {
       int id[UB];
-      ok[u] = ids_of(u, e, 0, id);
+      ok[u] = tc.ids_of(u, e, 0, id);
       load(id, buf[u]);
     }
 #pragma unroll
-    for (int u = 0; u < ST; ++u) tv[u] = fetch((u + ST - 1) * UB, UB);
+    for (int u = 0; u < ST; ++u) tv[u] = tc.fetch((u + ST - 1) * UB, UB);
   }
   static_assert(SYNC == 0 || ((SYNC & (SYNC - 1)) == 0 && SYNC % ST == 0), "barrier interval");
   for (int i = 0; i < units; i += ST) {
@@ -256,12 +273,100 @@ __device__ __forceinline__ void walk_blocks(const int32_t* table, const Partitio
       if (ii >= units) break;
       const int nu = (u + ST - 1) % ST;
       int id[UB];
-      ok[nu] = ids_of(ii + ST - 1, tv[u], (ii + ST - 1) * UB, id);
-      tv[u] = fetch((ii + 2 * ST - 1) * UB, UB);
+      ok[nu] = tc.ids_of(ii + ST - 1, tv[u], (ii + ST - 1) * UB, id);
+      tv[u] = tc.fetch((ii + 2 * ST - 1) * UB, UB);
       load(id, buf[nu]);
-      consume(jbeg + ii * UB, ok[u], buf[u]);
+      consume(tc.jbeg + ii * UB, ok[u], buf[u]);
     }
   }
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of the wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
+// the other counters at their no-wait values).
+constexpr unsigned wait_vmcnt(int n) {
+  return 0x0F70u | static_cast<unsigned>(n & 15) | (static_cast<unsigned>((n >> 4) & 3) << 14);
+}
+
+// Walk a segment with the work-group's waves loading each unit together into
+// NS LDS stages: NS-1 units are in flight while one is consumed.
+// `issue(ids, stage)` starts this wave's DW loads of the unit into stage
+// `stage`; `read(stage, buf)` copies this wave's operands of the unit into
+// registers; `consume(j0, ok, buf)` folds them in.
+//
+// Per unit, each wave waits for its own loads of it and then meets the others
+// at a barrier: after it the unit is whole in LDS, and every wave is done
+// with the unit before, whose stage the next loads then overwrite.  The unit
+// is read out before those loads are issued: the compiler cannot tell the
+// stages apart and would otherwise wait for the new loads before the reads.
+// The wait is explicit, so the vector-memory operations of every unit must
+// be the same: each unit (the first NS-1 in the prologue included) issues one
+// table fetch and then its DW loads, also past the segment's end (empty
+// loads), so that the unit's loads are followed by exactly (NS-2)(DW+1)
+// operations when they are waited for.  The table entries a unit's loads use
+// are fetched two units earlier (a fetch is then followed by 2DW+1
+// operations when it is read, and the compiler's own wait for it leaves the
+// stage loads in flight).  The walk ends with all its loads complete.  Every
+// wave of the work-group must walk the same segments and issue its share.
+template <int UB, int NS, int DW, typename Buf, typename Issue, typename Read, typename Consume>
+__device__ __forceinline__ void walk_blocks_coop(const int32_t* table, const PartitionSpan& s,
+                                                 int num_blocks, int sub, int lane, Issue&& issue,
+                                                 Read&& read, Consume&& consume) {
+  static_assert(NS >= 2 && NS * UB <= 32 && NS * UB <= 64, "stages");
+  const TableCursor<UB> tc(table, s, num_blocks, sub, lane);
+  const int units = tc.units();
+  if (units == 0) return;
+  __syncthreads();  // every wave is past its reads of the stages (a previous segment)
+  const int e = tc.fetch(0, NS * UB);  // units 0 .. NS-1, waited for at once
+  int tv[2];                           // entries for the unit issued at iteration ii, slot ii % 2 ...
+  int tfirst[2];                       // ... fetched from logical block jbeg + tfirst
+  unsigned okq = 0;                    // ok bits of the NS-1 units in flight, oldest lowest
+  if constexpr (NS == 2) {
+    tv[0] = e;
+    tfirst[0] = 0;
+  }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u) {  // the issues of iterations u - NS + 1
+    const int f = tc.fetch((u + 2) * UB, UB);
+    if (u == NS - 3) {
+      tv[0] = f;
+      tfirst[0] = (u + 2) * UB;
+    }
+    if (u == NS - 2) {
+      tv[1] = f;
+      tfirst[1] = (u + 2) * UB;
+    }
+    int id[UB];
+    okq |= tc.ids_of(u, e, 0, id) << (u * UB);
+    asm volatile("" ::: "memory");  // the fetch goes out before the unit's loads
+    issue(id, u);
+  }
+  for (int i = 0; i < units; i += 2) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int ii = i + s2;
+      if (ii >= units) break;
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt((NS - 2) * (DW + 1)));  // this wave's loads of unit ii
+      // A bare barrier: __syncthreads() would add a release fence, which
+      // waits for every load into LDS this wave has in flight, the later
+      // stages' included.  The empty asm keeps the compiler from moving the
+      // reads of the stage above it.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      Buf buf;
+      read(ii % NS, buf);
+      int id[UB];
+      const unsigned okn = tc.ids_of(ii + NS - 1, tv[s2], tfirst[s2], id);
+      tv[s2] = tc.fetch((ii + NS + 1) * UB, UB);
+      tfirst[s2] = (ii + NS + 1) * UB;
+      asm volatile("" ::: "memory");  // the fetch goes out before the unit's loads
+      issue(id, (ii + NS - 1) % NS);
+      const unsigned ok = okq & ((1u << UB) - 1u);
+      okq = (okq >> UB) | (okn << (UB * (NS - 2)));  // units ii+1 .. ii+NS-1 remain
+      consume(tc.jbeg + ii * UB, ok, buf);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // no load into a stage outlives the walk
 }
 
 // Vector stores.  Every lane's run of N outputs goes out in 16-byte (or, for

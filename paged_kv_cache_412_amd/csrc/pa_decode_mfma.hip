@@ -50,7 +50,14 @@ namespace pa {
 // KV heads (waves) per work-group
 constexpr int kMfmaHeads = 8;
 
-template <int KV, int Q, int D, int BS, int ST>
+// COOP (8-bit caches, D = 128, blocks of 16 or 32 tokens, every KV head of
+// the work-group present): the
+// work-group loads each unit together, every token row's slice of the group's
+// eight heads (1 KiB, contiguous) by one 64-lane load straight into LDS, and
+// each wave then reads its head's K and V from there.  The pool is then read
+// in whole 1 KiB pieces instead of one head's 128 bytes per row, which the
+// memory system serves faster.
+template <int KV, int Q, int D, int BS, int ST, bool COOP>
 __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const DecodeParams p) {
   using M = Mfma<Q>;
   constexpr bool FP8 = is_fp8(KV);
@@ -62,8 +69,11 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   // of one buffer resource per block
   constexpr bool SPLIT = BS < 16;
   constexpr int TPB = SPLIT ? 1 : BS / 16;      // 16-token tiles per block (or per 16/BS blocks)
-  constexpr int UB = 32 / BS;                   // blocks per pipeline unit (32 tokens)
-  constexpr int TT = 2;                         // 16-token tiles per unit
+  // tokens per pipeline unit: 32 (two 16-token tiles), or one tile per LDS
+  // stage when cooperative loads walk 16-token blocks (four stages fit)
+  constexpr int UT = (COOP && BS == 16) ? 16 : 32;
+  constexpr int UB = UT / BS;                   // blocks per pipeline unit
+  constexpr int TT = UT / 16;                   // 16-token tiles per unit
   constexpr int KW = D / 8;                     // dwords of 16-bit K per lane per tile
   constexpr int KR = FP8 ? D / 16 : D / 8;      // dwords of stored K per lane per tile
   constexpr int VW = EPL / 2;                   // dwords of 16-bit V per lane per row
@@ -72,6 +82,16 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
   const int G = p.Hq / p.Hkv;  // 3..16: the query group padded to the MFMA's 16 rows
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(!COOP || (FP8 && D == 128 && BS >= 16), "cooperative loads: 8-bit caches, D = 128");
+  // cooperative stages: the unit's token rows of K, then of V, each row the
+  // group's 1 KiB slice padded by 16 bytes (rows 16 bytes apart in the banks);
+  // wave w loads rows kRpw*w .. kRpw*w + kRpw - 1 of both
+  constexpr int kRows = UT;
+  constexpr int kRpw = kRows / kMfmaHeads;
+  constexpr int kPitch = kMfmaHeads * D * KVB + 16;
+  constexpr int kStageBytes = 2 * kRows * kPitch;
+  constexpr int kLdsStages = kRows == 16 ? 4 : 2;  // 133 KiB of LDS either way
+  __shared__ __attribute__((aligned(16))) unsigned char coop_lds[COOP ? kLdsStages * kStageBytes : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -307,9 +327,81 @@ __global__ __launch_bounds__(kMfmaHeads * 64) void decode_mfma_kernel(const Deco
 
     const int32_t* table =
         p.block_tables + static_cast<size_t>(b) * (p.max_blocks_per_seq >> p.sub_shift);
-    // waves meet every 8 units (8-bit caches) or 4 (16-bit), the intervals
-    // that measured fastest for each
-    walk_blocks<ST, UB, (FP8 ? 8 : 4), Raw>(table, span, p.num_blocks, p.sub_shift, lane, load, consume);
+    if constexpr (COOP) {
+      // wave w loads its unit rows (one block: a unit is one block here) of K
+      // and of V, each row the slice of the group's heads, into the stage;
+      // the whole unit is there after the walk's barrier
+      static_assert(!COOP || UB == 1, "a cooperative unit is one block");
+      const int grp_off = hg * kMfmaHeads * D * KVB;
+      auto issue = [&](const int (&id)[UB], int stage) {
+        unsigned char* st = coop_lds + stage * kStageBytes;
+        const int blk = id[0];
+        const size_t off = static_cast<size_t>(blk < 0 ? 0 : blk) * blk_bytes;
+        const uint32_t n = blk < 0 ? 0u : blk_bytes;
+        const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + off, n);
+        const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + off, n);
+#pragma unroll
+        for (int q = 0; q < kRpw; ++q) {
+          const int r = kRpw * wave + q;
+          const int vo = r * static_cast<int>(row_stride) + grp_off + lane * 16;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              kr, (__attribute__((address_space(3))) void*)(st + r * kPitch), 16, vo, 0, 0, kLoadNT);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              vr, (__attribute__((address_space(3))) void*)(st + (kRows + r) * kPitch), 16, vo, 0, 0,
+              kLoadNT);
+        }
+      };
+      // this wave's head from the stage, in the register layout of the
+      // direct loads: K bytes [32*grp, +32) of row lo of each tile, V bytes
+      // [8*lo, +8) of rows 4*grp + e.  The reads are one asm block per tile
+      // that waits for them itself: as plain loads the compiler would first
+      // wait for every load into LDS in flight (it cannot tell the stages
+      // apart), which would leave no stage loading during the arithmetic.
+      static_assert(!COOP || EPL == 8, "8-byte V runs");
+      const uint32_t lds0 = static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)coop_lds));
+      auto read = [&](int stage, Raw& r) {
+        const uint32_t st = lds0 + static_cast<uint32_t>(stage * kStageBytes);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const uint32_t ka = st + (16 * tt + lo) * kPitch + wave * D + grp * (D / 4);
+          const uint32_t va = st + (kRows + 16 * tt + 4 * grp) * kPitch + wave * D + EPL * lo;
+          u32x4 k0, k1;
+          u32x2 v0, v1, v2, v3;
+          asm volatile(
+              "ds_read_b128 %0, %6\n"
+              "ds_read_b128 %1, %6 offset:16\n"
+              "ds_read_b64 %2, %7\n"
+              "ds_read_b64 %3, %7 offset:%8\n"
+              "ds_read_b64 %4, %7 offset:%9\n"
+              "ds_read_b64 %5, %7 offset:%10\n"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(k0), "=&v"(k1), "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+              : "v"(ka), "v"(va), "n"(kPitch), "n"(2 * kPitch), "n"(3 * kPitch)
+              : "memory");
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            r.k[tt][i] = k0[i];
+            r.k[tt][4 + i] = k1[i];
+          }
+          r.v[tt][0][0] = v0[0];
+          r.v[tt][0][1] = v0[1];
+          r.v[tt][1][0] = v1[0];
+          r.v[tt][1][1] = v1[1];
+          r.v[tt][2][0] = v2[0];
+          r.v[tt][2][1] = v2[1];
+          r.v[tt][3][0] = v3[0];
+          r.v[tt][3][1] = v3[1];
+        }
+      };
+      walk_blocks_coop<UB, kLdsStages, 2 * kRpw, Raw>(table, span, p.num_blocks, p.sub_shift, lane, issue,
+                                                   read, consume);
+    } else {
+      // waves meet every 8 units (8-bit caches) or 4 (16-bit), the intervals
+      // that measured fastest for each
+      walk_blocks<ST, UB, (FP8 ? 8 : 4), Raw>(table, span, p.num_blocks, p.sub_shift, lane, load,
+                                                consume);
+    }
 
     // l of query lo summed over the four lane groups; every lane then fetches
     // m and l of the queries whose accumulators it holds (4*grp + i)
@@ -338,16 +430,32 @@ namespace {
 // register sets in the load pipeline (units in flight per wave, plus one)
 constexpr int kStages = 2;
 
+// Cooperative loads need every wave of a work-group to load its share, so
+// every KV head of the group present: the head count a multiple of eight.
+bool use_coop(const DecodeParams& p, int kv, int d) {
+  return is_fp8(kv) && d == 128 && p.heads_per_wg == kMfmaHeads && p.Hkv % kMfmaHeads == 0;
+}
+
 template <int KV_, int Q_, int D_, int BS_>
 struct Tag {
   static constexpr int KV = KV_, Q = Q_, D = D_, BS = BS_;
-  static const void* kernel() {
-    return reinterpret_cast<const void*>(&decode_mfma_kernel<KV, Q, D, BS, kStages>);
+  // instances that have the mode (a unit of 8-token blocks spans four blocks,
+  // which the per-wave row assignment does not cover)
+  static constexpr bool kCoop = is_fp8(KV) && D == 128 && BS >= 16;
+  template <bool C>
+  static const void* fn() {
+    return reinterpret_cast<const void*>(&decode_mfma_kernel<KV, Q, D, BS, kStages, C>);
+  }
+  static const void* kernel(const DecodeParams& p) {
+    if constexpr (kCoop) {
+      if (use_coop(p, KV, D)) return fn<true>();
+    }
+    return fn<false>();
   }
   static hipError_t launch(const DecodeParams& p, hipStream_t s) {
     const dim3 grid = p.balanced ? dim3(p.head_groups, p.groups, 1)
                                  : dim3(p.head_groups, p.B, p.num_partitions);
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, D, BS, kStages>), grid,
+    hipLaunchKernelGGL(reinterpret_cast<void (*)(DecodeParams)>(const_cast<void*>(kernel(p))), grid,
                        dim3(p.heads_per_wg * 64), 0, s, p);
     return hipGetLastError();
   }
@@ -402,7 +510,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, pa_dtype q_dtype, pa_dtype 
 
 int32_t decode_mfma_groups_per_cu(const DecodeParams& p, pa_dtype q_dtype, pa_dtype kv_dtype) {
   const void* fn = nullptr;
-  if (!dispatch(p, q_dtype, kv_dtype, [&](auto t) { fn = decltype(t)::kernel(); })) return 0;
+  if (!dispatch(p, q_dtype, kv_dtype, [&](auto t) { fn = decltype(t)::kernel(p); })) return 0;
   return groups_per_cu(fn, p.heads_per_wg * 64);
 }
 
