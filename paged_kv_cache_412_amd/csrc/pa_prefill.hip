@@ -102,7 +102,9 @@ __device__ __forceinline__ int xcd_round_robin(int c, int n) {
   return k * X + x;
 }
 
-template <int KV, int Q, int D, int BS>
+// MHA: the instance for one query head per KV head (G = 1) with 16-bit K/V;
+// it differs only in how the transposing V reads are issued (see read_v).
+template <int KV, int Q, int D, int BS, bool MHA>
 __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(const PrefillParams p) {
   using M = Mfma<Q>;
   constexpr int KVB = Elem<KV>::bytes;
@@ -344,15 +346,65 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
 #pragma unroll
   for (int mm = 0; mm < EPL; ++mm)
     vtr[mm] = lds_off(4 * grp + (lo >> 2), 2 * mm + ((lo >> 1) & 1)) + ((lo & 1) << 3);
+  // The transposing reads of one 32-key step.  Through the builtin the
+  // compiler cannot tell which LDS buffer they read, and with 16-bit K/V
+  // (filled straight into LDS) it first waits for the next tile's fills.
+  // Without grouping every work-group reads K/V of its own, the fills come
+  // from memory, and that wait costs more than the reads' latency: the MHA
+  // instance issues them as one asm block that waits for them itself.  With
+  // grouping the fills are mostly L2 hits, and the builtin reads, issued a
+  // step ahead of their products, keep their latency hidden.
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  static_assert(!MHA || (KVB == 2 && (EPL == 8 || EPL == 4)), "MHA instance: 16-bit K/V");
   auto read_v = [&](const uint8_t* Vt, int kp, u32x4 (&va)[EPL]) {
+    if constexpr (MHA) {
+      const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                                (__attribute__((address_space(3))) const uint8_t*)Vt)) +
+                            32 * kp * ROWB;
+      u32x2 y[2 * EPL];
+      if constexpr (EPL == 8) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %16 offset:%24\n"
+            "ds_read_b64_tr_b16 %2, %17\n ds_read_b64_tr_b16 %3, %17 offset:%24\n"
+            "ds_read_b64_tr_b16 %4, %18\n ds_read_b64_tr_b16 %5, %18 offset:%24\n"
+            "ds_read_b64_tr_b16 %6, %19\n ds_read_b64_tr_b16 %7, %19 offset:%24\n"
+            "ds_read_b64_tr_b16 %8, %20\n ds_read_b64_tr_b16 %9, %20 offset:%24\n"
+            "ds_read_b64_tr_b16 %10, %21\n ds_read_b64_tr_b16 %11, %21 offset:%24\n"
+            "ds_read_b64_tr_b16 %12, %22\n ds_read_b64_tr_b16 %13, %22 offset:%24\n"
+            "ds_read_b64_tr_b16 %14, %23\n ds_read_b64_tr_b16 %15, %23 offset:%24\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]),
+              "=&v"(y[6]), "=&v"(y[7]), "=&v"(y[8]), "=&v"(y[9]), "=&v"(y[10]), "=&v"(y[11]),
+              "=&v"(y[12]), "=&v"(y[13]), "=&v"(y[14]), "=&v"(y[15])
+            : "v"(base + vtr[0]), "v"(base + vtr[1]), "v"(base + vtr[2]), "v"(base + vtr[3]),
+              "v"(base + vtr[4]), "v"(base + vtr[5]), "v"(base + vtr[6]), "v"(base + vtr[7]),
+              "n"(16 * ROWB)
+            : "memory");
+      } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n ds_read_b64_tr_b16 %1, %8 offset:%12\n"
+            "ds_read_b64_tr_b16 %2, %9\n ds_read_b64_tr_b16 %3, %9 offset:%12\n"
+            "ds_read_b64_tr_b16 %4, %10\n ds_read_b64_tr_b16 %5, %10 offset:%12\n"
+            "ds_read_b64_tr_b16 %6, %11\n ds_read_b64_tr_b16 %7, %11 offset:%12\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]),
+              "=&v"(y[6]), "=&v"(y[7])
+            : "v"(base + vtr[0]), "v"(base + vtr[1]), "v"(base + vtr[2]), "v"(base + vtr[3]),
+              "n"(16 * ROWB)
+            : "memory");
+      }
 #pragma unroll
-    for (int mm = 0; mm < EPL; ++mm) {
-      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + 32 * kp * ROWB));
-      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + (32 * kp + 16) * ROWB));
-      const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
-      va[mm] = u32x4{y0[0], y0[1], y1[0], y1[1]};
+      for (int mm = 0; mm < EPL; ++mm)
+        va[mm] = u32x4{y[2 * mm][0], y[2 * mm][1], y[2 * mm + 1][0], y[2 * mm + 1][1]};
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < EPL; ++mm) {
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + 32 * kp * ROWB));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + (32 * kp + 16) * ROWB));
+        const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
+        va[mm] = u32x4{y0[0], y0[1], y1[0], y1[1]};
+      }
     }
   };
 
@@ -486,7 +538,14 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
 template <int KV_, int Q_, int D_, int BS_>
 struct Tag {
   static hipError_t launch(const PrefillParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((prefill_kernel<KV_, Q_, D_, BS_>), dim3(p.total_groups), dim3(kWaves * 64), 0,
+    if constexpr (Elem<KV_>::bytes == 2) {
+      if (p.Hq == p.Hkv) {
+        hipLaunchKernelGGL((prefill_kernel<KV_, Q_, D_, BS_, true>), dim3(p.total_groups),
+                           dim3(kWaves * 64), 0, s, p);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((prefill_kernel<KV_, Q_, D_, BS_, false>), dim3(p.total_groups), dim3(kWaves * 64), 0,
                        s, p);
     return hipGetLastError();
   }
