@@ -129,12 +129,17 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE];  // [buffer][K, V]
 
   // LDS placement of 16-byte chunk c of key row r: XOR-swizzled so that the
-  // reads of one chunk column of 16 rows (K operands), the transposing reads
-  // of two adjacent chunks of 4 consecutive rows (V operands: the rows'
-  // swizzles differ in bits 1-2) and the staging writes (whole rows) each
-  // touch distinct banks.
+  // reads of one chunk column of 16 rows (K operands: 16 distinct chunks)
+  // and the transposing reads of two adjacent chunks of 8 consecutive rows
+  // (V operands, two 16-lane groups at once: the rows' swizzles differ above
+  // bit 0, so the pairs land on distinct chunks) touch distinct banks; the
+  // staging fills write whole rows.  With 256-byte rows a row spans every
+  // bank, so rows r and r + 4 must not share a chunk pair: the first
+  // swizzle, 2(r mod 4) + (r div 4) mod 2, gave them the same one, and a
+  // third of the LDS's active cycles were bank conflicts.
   auto swz = [](int r) {
-    return ((r & 3) << 1) | ((r >> 2) & 1) | (CH == 16 ? (r & 8) : 0);
+    if constexpr (CH == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+    return ((r & 3) << 1) | ((r >> 2) & 1);
   };
   auto lds_off = [&](int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); };
 

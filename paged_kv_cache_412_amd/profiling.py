@@ -21,6 +21,9 @@ Three steps, run from the repository root:
     (VMEM_COUNTERS): address-unit busy and stall cycles, vector-L1 stalls,
     vector-memory read instructions, waves, and the GPU busy cycles they are
     shares of.
+``python -m paged_kv_cache_412_amd.profiling pipe --workload W --out DIR``
+    (GPU) one ``rocprofv3 --pmc`` pass per counter of PIPE_COUNTERS: where
+    the waves' time goes (waiting, LDS issue and bank conflicts, VALU).
 ``python -m paged_kv_cache_412_amd.profiling summarize --workload W --dir DIR``
     (any machine) reads those CSVs and writes
     ``profiles/<kernel>_<workload>.md`` (per-kernel durations; HBM bytes per
@@ -106,6 +109,20 @@ VMEM_COUNTERS = ("GRBM_GUI_ACTIVE", "TA_BUSY_avr", "TA_ADDR_STALLED_BY_TC_CYCLES
 
 def vmem(workload: str, out: str) -> None:
     for counter in VMEM_COUNTERS:
+        _run([ROCPROF, "--pmc", counter, "-f", "csv", "-d", out, "-o", f"pmc_{counter}_{workload}",
+              "--", *_bench_cmd(workload, PMC_STEPS, PMC_WARMUP)], 180)
+
+
+# Where the waves' time goes (one counter per pass): wave cycles and the
+# share of them spent waiting (for anything; for an LDS instruction to
+# issue), LDS instruction issue and bank-conflict cycles against the LDS's
+# active cycles, and the derived LDS and VALU utilisations.
+PIPE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
+                 "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "LdsUtil", "VALUBusy")
+
+
+def pipe(workload: str, out: str) -> None:
+    for counter in PIPE_COUNTERS:
         _run([ROCPROF, "--pmc", counter, "-f", "csv", "-d", out, "-o", f"pmc_{counter}_{workload}",
               "--", *_bench_cmd(workload, PMC_STEPS, PMC_WARMUP)], 180)
 
@@ -318,6 +335,30 @@ def summarize(workload: str, d: str) -> None:
         lines += [f"| SQ_INSTS_VMEM_RD: vector-memory read instructions | {insts:.4g} | "
                   f"{kvb / insts:.0f} algorithmic bytes per instruction |",
                   f"| SQ_WAVES | {val['SQ_WAVES']:.4g} | |"]
+    pp = {c: _find(d, f"pmc_{c}_{workload}_counter_collection.csv") for c in PIPE_COUNTERS}
+    if all(pp.values()):
+        val = {c: kernel_avg(pp[c], c)[0] for c in PIPE_COUNTERS}
+        rec["pipe"] = val
+        wc = val["SQ_WAVE_CYCLES"]
+        lds = val["SQ_LDS_IDX_ACTIVE"]
+        lines += ["", "## Where the waves' time goes (rocprofv3 --pmc, one counter per pass)", "", "```",
+                  f"python -m paged_kv_cache_412_amd.profiling pipe --workload {workload} --out gpurun_out/prof",
+                  "  # = rocprofv3 --pmc <counter> -f csv ... -- python3 bench.py --workload "
+                  f"{workload} --steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline --batches 0",
+                  "  #   for each of: " + ", ".join(PIPE_COUNTERS), "```", "",
+                  f"Per `{kernel}` dispatch (mean over the run's dispatches).", "",
+                  "| counter | per dispatch | share |", "|---|---|---|",
+                  f"| SQ_WAVE_CYCLES: wave-cycles | {wc:.4g} | |",
+                  f"| SQ_WAIT_ANY: wave-cycles waiting for anything | {val['SQ_WAIT_ANY']:.4g} | "
+                  f"{100 * val['SQ_WAIT_ANY'] / wc:.1f} % of wave-cycles |",
+                  f"| SQ_WAIT_INST_LDS: wave-cycles waiting to issue an LDS instruction | "
+                  f"{val['SQ_WAIT_INST_LDS']:.4g} | {100 * val['SQ_WAIT_INST_LDS'] / wc:.1f} % of wave-cycles |",
+                  f"| SQ_ACTIVE_INST_LDS: cycles issuing LDS instructions | {val['SQ_ACTIVE_INST_LDS']:.4g} | |",
+                  f"| SQ_LDS_IDX_ACTIVE: LDS active cycles | {lds:.4g} | |",
+                  f"| SQ_LDS_BANK_CONFLICT: LDS bank-conflict cycles | {val['SQ_LDS_BANK_CONFLICT']:.4g} | "
+                  f"{100 * val['SQ_LDS_BANK_CONFLICT'] / lds:.1f} % of LDS active cycles |",
+                  f"| LdsUtil (derived, %) | {val['LdsUtil']:.3g} | |",
+                  f"| VALUBusy (derived, %) | {val['VALUBusy']:.3g} | |"]
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{kernel}_{workload}.md"), "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
@@ -367,7 +408,7 @@ def bench_prefill_flops(cfg) -> int:
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("step", choices=["trace", "pmc", "calibration", "mfma", "vmem", "summarize"])
+    ap.add_argument("step", choices=["trace", "pmc", "calibration", "mfma", "vmem", "pipe", "summarize"])
     ap.add_argument("--no-calibration", action="store_true",
                     help="pmc: skip the calibration copy (taken once by the calibration step)")
     ap.add_argument("--workload", default="llama13b")
@@ -384,6 +425,8 @@ def main(argv=None) -> int:
         mfma(a.workload, a.out)
     elif a.step == "vmem":
         vmem(a.workload, a.out)
+    elif a.step == "pipe":
+        pipe(a.workload, a.out)
     else:
         summarize(a.workload, a.dir)
     return 0
