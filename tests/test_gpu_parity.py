@@ -662,3 +662,70 @@ def test_batches_past_the_inline_plan(B, pair, G, bs, part):
     wl, step, exp = run_step(cfg, partition_size=part, out_dtype="f32")
     err = check_step(wl, step, exp, out_dtype="f32")
     print(f"[ok] B={B} {qd}/{kvd} G={G} bs={bs} part={part} max abs err {err:.3e}", flush=True)
+
+
+# The work-group-cooperative 8-bit path (whole token-row slices of K and V
+# loaded by all eight waves straight into LDS) serves D = 128 8-bit caches
+# whose KV heads fill whole work-groups of eight; the reduced shapes above
+# have two KV heads and take the per-wave path, so these cover it at sizes
+# the oracle finishes in seconds.
+COOP = {
+    "coop_e4m3": replace(C["long_fp8"], name="coop_e4m3", B=3, len_range=(300, 3000)),
+    "coop_e4m3_bs32": replace(C["long_fp8_bs32"], name="coop_e4m3_bs32", B=3, len_range=(300, 3000)),
+    "coop_e4m3_bs64": replace(C["long_fp8"], name="coop_e4m3_bs64", B=3, block_size=64,
+                              len_range=(300, 3000)),
+    "coop_e5m2_heads": replace(C["long_e5m2"], name="coop_e5m2_heads", B=3, head_scales=True,
+                               len_range=(300, 3000)),
+    "coop_e4m3_16heads": replace(C["long_fp8"], name="coop_e4m3_16heads", B=2, Hq=64, Hkv=16,
+                                 len_range=(300, 2000)),
+}
+
+
+@pytest.mark.parametrize("name", list(COOP))
+def test_cooperative_path_edge_lengths(name):
+    """Empty, single-token, block-edge and partition-edge lengths through the
+    cooperative path, every output against the oracle."""
+    base = COOP[name]
+    bs = base.block_size
+    lens = (0, 1, bs - 1, bs, bs + 1, 2 * bs + 3, 511, 512, 513, 1537)
+    cfg = replace(base, B=len(lens), lens=lens, len_range=(), pool_blocks=0)
+    wl, step, exp = run_step(cfg, out_dtype="f32")
+    err = check_step(wl, step, exp, out_dtype="f32")
+    out = parity.gpu_out(step.out)
+    assert np.array_equal(out[0], np.zeros_like(out[0])), "L = 0 must give zeros"
+    print(f"[ok] {name} edge lengths max abs err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("mode", list(COMBINES))
+@pytest.mark.parametrize("part", [0, 64, 512])
+@pytest.mark.parametrize("name", list(COOP))
+def test_cooperative_path_schedules_and_combines(name, part, mode):
+    """Both schedules (balanced, and fixed partitions of several sizes) and
+    both combine modes through the cooperative path, with NaN bytes in the
+    workspace past its arrival counters."""
+    cfg = COOP[name]
+    if part % cfg.block_size:
+        part = cfg.block_size
+    print(f"\n[case] cooperative {name} part={part} combine={mode}", flush=True)
+    wl = workloads.make(cfg, device="cuda")
+    pre = parity.snapshot(wl)
+    step = DecodeStep(wl, partition_size=part, out_dtype="f32", combine=COMBINES[mode])
+    zb = binding.workspace_zero_bytes(step.args)
+    if step.workspace is not None:
+        step.workspace[zb:].fill_(0xFF)
+    step.run()
+    torch.cuda.synchronize()
+    exp = parity.oracle_step(wl, pre)
+    err = check_step(wl, step, exp, out_dtype="f32")
+    if step.workspace is not None:
+        assert int(step.workspace[:zb].count_nonzero()) == 0, "arrival counters not reset"
+    print(f"[ok] {name} part={part} combine={mode} max abs err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["coop_e4m3", "coop_e4m3_bs64"])
+def test_cooperative_path_one_long_sequence(name):
+    """One sequence split over every work-group through the cooperative path."""
+    cfg = replace(COOP[name], B=1, lens=(20001,), len_range=(), pool_blocks=0)
+    wl, step, exp = run_step(cfg, out_dtype="f32")
+    err = check_step(wl, step, exp, out_dtype="f32")
+    print(f"[ok] {name} one long max abs err {err:.3e}", flush=True)
