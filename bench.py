@@ -659,7 +659,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps before the timed ones: with 10, the first timed decode "
+                         "steps still run below the steady rate (long 8-bit contexts 10 %% slower)")
     ap.add_argument("--workload", default="llama13b")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--combine", choices=["auto", "in_launch", "reduce"], default="auto",

@@ -103,7 +103,8 @@ __device__ __forceinline__ int xcd_round_robin(int c, int n) {
 }
 
 // MHA: the instance for one query head per KV head (G = 1) with 16-bit K/V;
-// it differs only in how the transposing V reads are issued (see read_v).
+// it differs in how the transposing V reads are issued (read_v_all) and in
+// how the weighted sum's products are ordered against the weights.
 template <int KV, int Q, int D, int BS, bool MHA>
 __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(const PrefillParams p) {
   using M = Mfma<Q>;
@@ -351,65 +352,88 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
 #pragma unroll
   for (int mm = 0; mm < EPL; ++mm)
     vtr[mm] = lds_off(4 * grp + (lo >> 2), 2 * mm + ((lo >> 1) & 1)) + ((lo & 1) << 3);
-  // The transposing reads of one 32-key step.  Through the builtin the
+  // The transposing reads of the value rows.  Through the builtin the
   // compiler cannot tell which LDS buffer they read, and with 16-bit K/V
   // (filled straight into LDS) it first waits for the next tile's fills.
   // Without grouping every work-group reads K/V of its own, the fills come
   // from memory, and that wait costs more than the reads' latency: the MHA
-  // instance issues them as one asm block that waits for them itself.  With
-  // grouping the fills are mostly L2 hits, and the builtin reads, issued a
-  // step ahead of their products, keep their latency hidden.
+  // instance issues the whole tile's reads as one asm block that waits for
+  // them itself.  With grouping the fills are mostly L2 hits, and the builtin
+  // reads of each 32-key step, issued a step ahead of its products, keep
+  // their latency hidden.
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   static_assert(!MHA || (KVB == 2 && (EPL == 8 || EPL == 4)), "MHA instance: 16-bit K/V");
-  auto read_v = [&](const uint8_t* Vt, int kp, u32x4 (&va)[EPL]) {
-    if constexpr (MHA) {
-      const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-                                (__attribute__((address_space(3))) const uint8_t*)Vt)) +
-                            32 * kp * ROWB;
-      u32x2 y[2 * EPL];
-      if constexpr (EPL == 8) {
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %16 offset:%24\n"
-            "ds_read_b64_tr_b16 %2, %17\n ds_read_b64_tr_b16 %3, %17 offset:%24\n"
-            "ds_read_b64_tr_b16 %4, %18\n ds_read_b64_tr_b16 %5, %18 offset:%24\n"
-            "ds_read_b64_tr_b16 %6, %19\n ds_read_b64_tr_b16 %7, %19 offset:%24\n"
-            "ds_read_b64_tr_b16 %8, %20\n ds_read_b64_tr_b16 %9, %20 offset:%24\n"
-            "ds_read_b64_tr_b16 %10, %21\n ds_read_b64_tr_b16 %11, %21 offset:%24\n"
-            "ds_read_b64_tr_b16 %12, %22\n ds_read_b64_tr_b16 %13, %22 offset:%24\n"
-            "ds_read_b64_tr_b16 %14, %23\n ds_read_b64_tr_b16 %15, %23 offset:%24\n"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]),
-              "=&v"(y[6]), "=&v"(y[7]), "=&v"(y[8]), "=&v"(y[9]), "=&v"(y[10]), "=&v"(y[11]),
-              "=&v"(y[12]), "=&v"(y[13]), "=&v"(y[14]), "=&v"(y[15])
-            : "v"(base + vtr[0]), "v"(base + vtr[1]), "v"(base + vtr[2]), "v"(base + vtr[3]),
-              "v"(base + vtr[4]), "v"(base + vtr[5]), "v"(base + vtr[6]), "v"(base + vtr[7]),
-              "n"(16 * ROWB)
-            : "memory");
-      } else {
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %8\n ds_read_b64_tr_b16 %1, %8 offset:%12\n"
-            "ds_read_b64_tr_b16 %2, %9\n ds_read_b64_tr_b16 %3, %9 offset:%12\n"
-            "ds_read_b64_tr_b16 %4, %10\n ds_read_b64_tr_b16 %5, %10 offset:%12\n"
-            "ds_read_b64_tr_b16 %6, %11\n ds_read_b64_tr_b16 %7, %11 offset:%12\n"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]),
-              "=&v"(y[6]), "=&v"(y[7])
-            : "v"(base + vtr[0]), "v"(base + vtr[1]), "v"(base + vtr[2]), "v"(base + vtr[3]),
-              "n"(16 * ROWB)
-            : "memory");
-      }
-#pragma unroll
-      for (int mm = 0; mm < EPL; ++mm)
-        va[mm] = u32x4{y[2 * mm][0], y[2 * mm][1], y[2 * mm + 1][0], y[2 * mm + 1][1]};
+  // MHA: both 32-key steps' value operands in one block, issued right after
+  // the score products (the wait at its end then overlaps their execution
+  // instead of stalling between the two steps' products)
+  auto read_v_all = [&](const uint8_t* Vt, u32x4 (&va)[KP][EPL]) {
+    static_assert(KP == 2, "two 32-key steps per tile");
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) const uint8_t*)Vt));
+    // y[4*mm + q]: head dims 16*mm.. of key rows 16*q + 4*grp .. + 3
+    u32x2 y[4 * EPL];
+    if constexpr (EPL == 8) {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %32\n ds_read_b64_tr_b16 %1, %32 offset:%40\n"
+          "ds_read_b64_tr_b16 %2, %32 offset:%41\n ds_read_b64_tr_b16 %3, %32 offset:%42\n"
+          "ds_read_b64_tr_b16 %4, %33\n ds_read_b64_tr_b16 %5, %33 offset:%40\n"
+          "ds_read_b64_tr_b16 %6, %33 offset:%41\n ds_read_b64_tr_b16 %7, %33 offset:%42\n"
+          "ds_read_b64_tr_b16 %8, %34\n ds_read_b64_tr_b16 %9, %34 offset:%40\n"
+          "ds_read_b64_tr_b16 %10, %34 offset:%41\n ds_read_b64_tr_b16 %11, %34 offset:%42\n"
+          "ds_read_b64_tr_b16 %12, %35\n ds_read_b64_tr_b16 %13, %35 offset:%40\n"
+          "ds_read_b64_tr_b16 %14, %35 offset:%41\n ds_read_b64_tr_b16 %15, %35 offset:%42\n"
+          "ds_read_b64_tr_b16 %16, %36\n ds_read_b64_tr_b16 %17, %36 offset:%40\n"
+          "ds_read_b64_tr_b16 %18, %36 offset:%41\n ds_read_b64_tr_b16 %19, %36 offset:%42\n"
+          "ds_read_b64_tr_b16 %20, %37\n ds_read_b64_tr_b16 %21, %37 offset:%40\n"
+          "ds_read_b64_tr_b16 %22, %37 offset:%41\n ds_read_b64_tr_b16 %23, %37 offset:%42\n"
+          "ds_read_b64_tr_b16 %24, %38\n ds_read_b64_tr_b16 %25, %38 offset:%40\n"
+          "ds_read_b64_tr_b16 %26, %38 offset:%41\n ds_read_b64_tr_b16 %27, %38 offset:%42\n"
+          "ds_read_b64_tr_b16 %28, %39\n ds_read_b64_tr_b16 %29, %39 offset:%40\n"
+          "ds_read_b64_tr_b16 %30, %39 offset:%41\n ds_read_b64_tr_b16 %31, %39 offset:%42\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]),
+            "=&v"(y[6]), "=&v"(y[7]), "=&v"(y[8]), "=&v"(y[9]), "=&v"(y[10]), "=&v"(y[11]),
+            "=&v"(y[12]), "=&v"(y[13]), "=&v"(y[14]), "=&v"(y[15]), "=&v"(y[16]), "=&v"(y[17]),
+            "=&v"(y[18]), "=&v"(y[19]), "=&v"(y[20]), "=&v"(y[21]), "=&v"(y[22]), "=&v"(y[23]),
+            "=&v"(y[24]), "=&v"(y[25]), "=&v"(y[26]), "=&v"(y[27]), "=&v"(y[28]), "=&v"(y[29]),
+            "=&v"(y[30]), "=&v"(y[31])
+          : "v"(base + vtr[0]), "v"(base + vtr[1]), "v"(base + vtr[2]), "v"(base + vtr[3]),
+            "v"(base + vtr[4]), "v"(base + vtr[5]), "v"(base + vtr[6]), "v"(base + vtr[7]),
+            "n"(16 * ROWB), "n"(32 * ROWB), "n"(48 * ROWB)
+          : "memory");
     } else {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %16 offset:%20\n"
+          "ds_read_b64_tr_b16 %2, %16 offset:%21\n ds_read_b64_tr_b16 %3, %16 offset:%22\n"
+          "ds_read_b64_tr_b16 %4, %17\n ds_read_b64_tr_b16 %5, %17 offset:%20\n"
+          "ds_read_b64_tr_b16 %6, %17 offset:%21\n ds_read_b64_tr_b16 %7, %17 offset:%22\n"
+          "ds_read_b64_tr_b16 %8, %18\n ds_read_b64_tr_b16 %9, %18 offset:%20\n"
+          "ds_read_b64_tr_b16 %10, %18 offset:%21\n ds_read_b64_tr_b16 %11, %18 offset:%22\n"
+          "ds_read_b64_tr_b16 %12, %19\n ds_read_b64_tr_b16 %13, %19 offset:%20\n"
+          "ds_read_b64_tr_b16 %14, %19 offset:%21\n ds_read_b64_tr_b16 %15, %19 offset:%22\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]),
+            "=&v"(y[6]), "=&v"(y[7]), "=&v"(y[8]), "=&v"(y[9]), "=&v"(y[10]), "=&v"(y[11]),
+            "=&v"(y[12]), "=&v"(y[13]), "=&v"(y[14]), "=&v"(y[15])
+          : "v"(base + vtr[0]), "v"(base + vtr[1]), "v"(base + vtr[2]), "v"(base + vtr[3]),
+            "n"(16 * ROWB), "n"(32 * ROWB), "n"(48 * ROWB)
+          : "memory");
+    }
 #pragma unroll
-      for (int mm = 0; mm < EPL; ++mm) {
-        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + 32 * kp * ROWB));
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + (32 * kp + 16) * ROWB));
-        const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
-        va[mm] = u32x4{y0[0], y0[1], y1[0], y1[1]};
-      }
+    for (int mm = 0; mm < EPL; ++mm) {
+      va[0][mm] = u32x4{y[4 * mm][0], y[4 * mm][1], y[4 * mm + 1][0], y[4 * mm + 1][1]};
+      va[1][mm] = u32x4{y[4 * mm + 2][0], y[4 * mm + 2][1], y[4 * mm + 3][0], y[4 * mm + 3][1]};
+    }
+  };
+  // other instances: one 32-key step's value operands through the builtin
+  auto read_v = [&](const uint8_t* Vt, int kp, u32x4 (&va)[EPL]) {
+#pragma unroll
+    for (int mm = 0; mm < EPL; ++mm) {
+      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + 32 * kp * ROWB));
+      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + vtr[mm] + (32 * kp + 16) * ROWB));
+      const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
+      va[mm] = u32x4{y0[0], y0[1], y1[0], y1[1]};
     }
   };
 
@@ -443,8 +467,9 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
       }
       // the first value rows, read now so that their LDS latency hides
       // behind the softmax
-      u32x4 vop[2][EPL];
-      read_v(Vt, 0, vop[0]);
+      u32x4 vop[KP][EPL];
+      if constexpr (MHA) read_v_all(Vt, vop);
+      else read_v(Vt, 0, vop[0]);
       // mask keys after each query's position (only near the diagonal)
       if (k0 + kKeys - 1 > pmin) {
 #pragma unroll
@@ -487,12 +512,11 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
           for (int mm = 0; mm < EPL; ++mm) o[nt][mm] *= alpha;
         }
       }
-      // weighted sum, 32 keys at a time
-#pragma unroll
-      for (int kp = 0; kp < KP; ++kp) {
-        // weights, packed as the B operand: slots e < 4 are keys 4*grp + e of
-        // the first 16-key tile, e >= 4 the same of the second
-        u32x4 pb[NT];
+      // weighted sum, 32 keys at a time.  Weights of 32-key step kp, packed
+      // as the B operand: slots e < 4 are keys 4*grp + e of the first 16-key
+      // tile, e >= 4 the same of the second
+      u32x4 pb[KP][NT];
+      auto weights = [&](int kp) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           float w[2][4];
@@ -501,18 +525,45 @@ __global__ __launch_bounds__(kWaves * 64, kMinGroupsPerCU) void prefill_kernel(c
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               w[h][r] = fast_exp2(__builtin_fmaf(s[2 * kp + h][nt][r], c, -m[nt]));
-          pb[nt] = u32x4{M::pack2(w[0][0], w[0][1]), M::pack2(w[0][2], w[0][3]),
-                         M::pack2(w[1][0], w[1][1]), M::pack2(w[1][2], w[1][3])};
-          // the sum takes the weights as rounded for the matrix cores, so the
-          // result is an exact weighted mean of V rows under those weights
-          l[nt] = M::mma32(ones, pb[nt], l[nt]);
+          pb[kp][nt] = u32x4{M::pack2(w[0][0], w[0][1]), M::pack2(w[0][2], w[0][3]),
+                             M::pack2(w[1][0], w[1][1]), M::pack2(w[1][2], w[1][3])};
         }
-        // the next step's value operands go out before this step's products
-        if (kp + 1 < KP) read_v(Vt, kp + 1, vop[(kp + 1) & 1]);
+      };
+      // the running sum takes the weights as rounded for the matrix cores, so
+      // the result is an exact weighted mean of V rows under those weights
+      auto products = [&](int kp) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) l[nt] = M::mma32(ones, pb[kp][nt], l[nt]);
 #pragma unroll
         for (int mm = 0; mm < EPL; ++mm) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[nt][mm] = M::mma32(vop[kp & 1][mm], pb[nt], o[nt][mm]);
+          for (int nt = 0; nt < NT; ++nt) o[nt][mm] = M::mma32(vop[kp][mm], pb[kp][nt], o[nt][mm]);
+        }
+      };
+      if constexpr (MHA) {
+        // The second step's weights are computed while the first step's
+        // products run: one product, then two vector ops, in turn, so that
+        // the matrix cores and the vector ALUs work at the same time within
+        // the wave (left to itself the compiler computes every weight first).
+        constexpr int MPK = NT * (EPL + 1);  // products per step
+        weights(0);
+        __builtin_amdgcn_sched_barrier(0);
+        products(0);
+        weights(1);
+#pragma unroll
+        for (int i = 0; i < MPK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix product
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two vector ops
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        products(1);
+      } else {
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp) {
+          weights(kp);
+          // the next step's value operands go out before this step's products
+          if (kp + 1 < KP) read_v(Vt, kp + 1, vop[kp + 1]);
+          products(kp);
         }
       }
     }

@@ -22,8 +22,10 @@ Three steps, run from the repository root:
     vector-memory read instructions, waves, and the GPU busy cycles they are
     shares of.
 ``python -m paged_kv_cache_412_amd.profiling pipe --workload W --out DIR``
-    (GPU) one ``rocprofv3 --pmc`` pass per counter of PIPE_COUNTERS: where
-    the waves' time goes (waiting, LDS issue and bank conflicts, VALU).
+    (GPU) one ``rocprofv3 --pmc`` pass per counter of PIPE_COUNTERS and
+    ISSUE_COUNTERS: where the waves' time goes (issuing, waiting for an issue
+    slot or on a dependency, LDS issue and bank conflicts, VALU), and how
+    often vector instructions issue while the matrix cores are busy.
 ``python -m paged_kv_cache_412_amd.profiling summarize --workload W --dir DIR``
     (any machine) reads those CSVs and writes
     ``profiles/<kernel>_<workload>.md`` (per-kernel durations; HBM bytes per
@@ -51,7 +53,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROFILES = os.path.join(ROOT, "profiles")
 ROCPROF = "rocprofv3"
-STEPS, WARMUP = 50, 10          # bench.py's defaults: the profiled run is the bench run
+STEPS, WARMUP = 50, 200         # bench.py's defaults: the profiled run is the bench run
 PMC_STEPS, PMC_WARMUP = 3, 1
 
 
@@ -121,8 +123,18 @@ PIPE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE
                  "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "LdsUtil", "VALUBusy")
 
 
+# Issue and co-execution (one counter per pass, same step): the wave-cycles
+# spent issuing, waiting for an issue slot and (SQ_WAIT_ANY above) waiting
+# on a dependency, which add up to SQ_WAVE_CYCLES; the matrix cores' busy
+# cycles, and those in which a vector instruction issued beside them; the
+# instruction mix; and the dispatch's length in cycles for the clock.
+ISSUE_COUNTERS = ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_VALU_MFMA_BUSY_CYCLES",
+                  "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                  "SQ_INSTS_VALU_TRANS_F32", "GRBM_GUI_ACTIVE")
+
+
 def pipe(workload: str, out: str) -> None:
-    for counter in PIPE_COUNTERS:
+    for counter in PIPE_COUNTERS + ISSUE_COUNTERS:
         _run([ROCPROF, "--pmc", counter, "-f", "csv", "-d", out, "-o", f"pmc_{counter}_{workload}",
               "--", *_bench_cmd(workload, PMC_STEPS, PMC_WARMUP)], 180)
 
@@ -359,6 +371,35 @@ def summarize(workload: str, d: str) -> None:
                   f"{100 * val['SQ_LDS_BANK_CONFLICT'] / lds:.1f} % of LDS active cycles |",
                   f"| LdsUtil (derived, %) | {val['LdsUtil']:.3g} | |",
                   f"| VALUBusy (derived, %) | {val['VALUBusy']:.3g} | |"]
+        ip = {c: _find(d, f"pmc_{c}_{workload}_counter_collection.csv") for c in ISSUE_COUNTERS}
+        if all(ip.values()):
+            iv = {c: kernel_avg(ip[c], c)[0] for c in ISSUE_COUNTERS}
+            rec["issue"] = iv
+            xcc, cus = _gpu_shape(ip["GRBM_GUI_ACTIVE"].replace("_counter_collection.csv", "_agent_info.csv"))
+            cyc = iv["GRBM_GUI_ACTIVE"] / xcc  # the dispatch's length in cycles
+            simds = 4 * cus
+            busy = iv["SQ_VALU_MFMA_BUSY_CYCLES"]
+            lines += ["",
+                      f"Issue and co-execution (same step, one counter per pass: "
+                      f"{', '.join(ISSUE_COUNTERS)}).  The first three rows split the wave-cycles.", "",
+                      "| counter | per dispatch | share |", "|---|---|---|",
+                      f"| SQ_ACTIVE_INST_ANY: wave-cycles issuing | {iv['SQ_ACTIVE_INST_ANY']:.4g} | "
+                      f"{100 * iv['SQ_ACTIVE_INST_ANY'] / wc:.1f} % of wave-cycles |",
+                      f"| SQ_WAIT_INST_ANY: wave-cycles waiting for an issue slot | {iv['SQ_WAIT_INST_ANY']:.4g} | "
+                      f"{100 * iv['SQ_WAIT_INST_ANY'] / wc:.1f} % of wave-cycles |",
+                      f"| SQ_WAIT_ANY (above): wave-cycles waiting on a dependency | {val['SQ_WAIT_ANY']:.4g} | "
+                      f"{100 * val['SQ_WAIT_ANY'] / wc:.1f} % of wave-cycles |",
+                      f"| GRBM_GUI_ACTIVE (cycles, all {xcc} XCDs) | {iv['GRBM_GUI_ACTIVE']:.4g} | "
+                      f"{cyc:.4g} cycles per XCD |",
+                      f"| SQ_VALU_MFMA_BUSY_CYCLES: matrix-core busy cycles, all {simds} SIMDs | {busy:.4g} | "
+                      f"{100 * busy / (simds * cyc):.1f} % of SIMD cycles |",
+                      f"| SQ_VALU_MFMA_COEXEC_CYCLES: busy with a vector instruction issued beside | "
+                      f"{iv['SQ_VALU_MFMA_COEXEC_CYCLES']:.4g} | "
+                      f"{100 * iv['SQ_VALU_MFMA_COEXEC_CYCLES'] / busy:.1f} % of matrix-core busy cycles |",
+                      f"| SQ_INSTS_MFMA: matrix instructions | {iv['SQ_INSTS_MFMA']:.4g} | "
+                      f"{busy / iv['SQ_INSTS_MFMA']:.1f} busy cycles each |",
+                      f"| SQ_INSTS_VALU: vector instructions (matrix ones included) | {iv['SQ_INSTS_VALU']:.4g} | |",
+                      f"| SQ_INSTS_VALU_TRANS_F32: fp32 transcendentals | {iv['SQ_INSTS_VALU_TRANS_F32']:.4g} | |"]
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{kernel}_{workload}.md"), "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")

@@ -46,7 +46,7 @@ def runs(tmp_path, monkeypatch):
     out = tmp_path / "profiles"
     monkeypatch.setattr(profiling, "PROFILES", str(out))
     w = "llama70b"
-    # kernel trace: 10 warm-up launches at 700 us, then the 50 timed ones at 640 us
+    # kernel trace: the warm-up launches at 700 us, then the 50 timed ones at 640 us
     S, W = profiling.STEPS, profiling.WARMUP
     durs = [700.0] * W + [640.0] * S
     rows, t = [], 1_000_000
@@ -72,6 +72,18 @@ def runs(tmp_path, monkeypatch):
     alg = profiling.bench_decode_flops(workloads.CONFIGS[w])
     counters(d / f"pmc_MfmaUtil_{w}_counter_collection.csv", "MfmaUtil", [6.0, 7.0, 8.0])
     counters(d / f"pmc_MfmaFlops_{w}_counter_collection.csv", "MfmaFlops", [2.0 * alg] * 3)
+    # where the time goes: 1000 wave-cycles split 350 issuing / 400 waiting
+    # for a slot / 250 on a dependency; 8 XCDs of 1000 cycles; the matrix
+    # cores of 1024 SIMDs busy 40 %, a quarter of that beside vector issue
+    pipe = {"SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_ANY": 250.0, "SQ_WAIT_INST_LDS": 30.0,
+            "SQ_ACTIVE_INST_LDS": 40.0, "SQ_LDS_IDX_ACTIVE": 200.0, "SQ_LDS_BANK_CONFLICT": 20.0,
+            "LdsUtil": 19.0, "VALUBusy": 40.0, "SQ_ACTIVE_INST_ANY": 350.0, "SQ_WAIT_INST_ANY": 400.0,
+            "GRBM_GUI_ACTIVE": 8000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 409600.0,
+            "SQ_VALU_MFMA_COEXEC_CYCLES": 102400.0, "SQ_INSTS_MFMA": 25600.0, "SQ_INSTS_VALU": 1.0e5,
+            "SQ_INSTS_VALU_TRANS_F32": 1.0e4}
+    assert set(pipe) == set(profiling.PIPE_COUNTERS + profiling.ISSUE_COUNTERS)
+    for name, v in pipe.items():
+        counters(d / f"pmc_{name}_{w}_counter_collection.csv", name, [v] * 3, split=4)
     profiling.summarize(w, str(d))
     rec = json.loads((out / f"traffic_decode_mfma_kernel_{w}.json").read_text())
     md = (out / f"decode_mfma_kernel_{w}.md").read_text()
@@ -116,3 +128,18 @@ def test_bench_reads_back_the_record(runs, monkeypatch, tmp_path):
     p.write_text(json.dumps(stale))
     assert bench.measured_traffic("decode_mfma_kernel", "llama70b") is None
     assert bench.measured_mfma("decode_mfma_kernel", "llama70b") is None
+
+
+def test_summary_pipe_and_issue_counters(runs):
+    rec, md, _ = runs
+    assert rec["pipe"]["SQ_WAVE_CYCLES"] == pytest.approx(1000.0)   # instances summed per dispatch
+    assert "| 10.0 % of LDS active cycles |" in md                  # bank conflicts 20 of 200
+    shares = [float(x) for x in
+              [md.split(f"| {c}")[1].split("|")[2].split("%")[0] for c in
+               ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY (above)")]]
+    assert shares == [35.0, 40.0, 25.0] and sum(shares) == pytest.approx(100.0)
+    assert "| 1000 cycles per XCD |" in md
+    assert "| 40.0 % of SIMD cycles |" in md
+    assert "| 25.0 % of matrix-core busy cycles |" in md
+    assert "| 16.0 busy cycles each |" in md
+    assert rec["issue"]["SQ_INSTS_VALU_TRANS_F32"] == pytest.approx(1.0e4)
