@@ -23,6 +23,7 @@ thread) with the GPU output's max abs error against the oracle on it.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -328,9 +329,23 @@ def gpu_facts() -> dict:
         except OSError:
             continue
     props = torch.cuda.get_device_properties(0)
-    return {"gpu_name": torch.cuda.get_device_name(0), "gcn_arch": getattr(props, "gcnArchName", None),
-            "compute_units": props.multi_processor_count, "rocm_version": ver,
-            "hip_runtime": torch.version.hip}
+    name = torch.cuda.get_device_name(0)
+    # without libdrm's marketing-name table the runtime reports no name; the
+    # kernel driver's sysfs entries still carry the product name, the PCI
+    # device id and the VBIOS part number
+    sysfs = {}
+    for card in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        for key in ("product_name", "device", "vbios_version"):
+            try:
+                with open(os.path.join(card, key)) as f:
+                    sysfs.setdefault(key, f.read().strip())
+            except OSError:
+                pass
+        if sysfs:
+            break
+    return {"gpu_name": name or sysfs.get("product_name", ""), "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "pci_device_id": sysfs.get("device"),
+            "vbios": sysfs.get("vbios_version"), "rocm_version": ver, "hip_runtime": torch.version.hip}
 
 
 def median_batches(run_step, stream, batches=5, steps=100) -> dict:
