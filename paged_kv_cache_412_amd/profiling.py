@@ -192,12 +192,12 @@ def summarize(workload: str, d: str) -> None:
     lines = [f"# {kernel} -- {workload}", "",
              "Kernel durations from `rocprofv3 --kernel-trace --stats` around the bench.py run (no CPU baseline).",
              "", "Commands (repository root, MI355X):", "", "```",
-             f"python -m paged_kv_cache_412_amd.profiling trace --workload {workload} --out gpurun_out/prof",
-             "  # = " + " ".join([ROCPROF, "--kernel-trace", "--stats", "-f", "csv", "-d", "gpurun_out/prof",
+             f"python -m paged_kv_cache_412_amd.profiling trace --workload {workload} --out rocprof_out",
+             "  # = " + " ".join([ROCPROF, "--kernel-trace", "--stats", "-f", "csv", "-d", "rocprof_out",
                                    "-o", f"trace_{workload}", "--", "python3", "bench.py", "--workload",
                                    workload, "--steps", str(STEPS), "--warmup", str(WARMUP),
                                    "--no-cpu-baseline"]),
-             f"python -m paged_kv_cache_412_amd.profiling summarize --workload {workload} --dir gpurun_out/prof",
+             f"python -m paged_kv_cache_412_amd.profiling summarize --workload {workload} --dir rocprof_out",
              "```", "", "| kernel | calls | average us | total us | % |", "|---|---|---|---|---|"]
     avg_us = None
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
@@ -283,7 +283,7 @@ def summarize(workload: str, d: str) -> None:
                     "calibration_write_kib": cw_kib, "fetch_factor": kf, "write_factor": kw,
                     "hbm_bytes_per_launch": hbm, "dispatches": [nf, nw]})
         lines += ["", "## HBM traffic (rocprofv3 --pmc, one counter per pass)", "", "```",
-                  f"python -m paged_kv_cache_412_amd.profiling pmc --workload {workload} --out gpurun_out/prof",
+                  f"python -m paged_kv_cache_412_amd.profiling pmc --workload {workload} --out rocprof_out",
                   "  # = rocprofv3 --pmc FETCH_SIZE -f csv ... -- python3 bench.py --workload "
                   f"{workload} --steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline",
                   "  #   rocprofv3 --pmc FETCH_SIZE -f csv ... -- python3 bench.py --copy-calibration",
@@ -304,7 +304,7 @@ def summarize(workload: str, d: str) -> None:
         alg = bench_prefill_flops(cfg) if cfg.prefill else bench_decode_flops(cfg)
         rec.update({"mfma_util_pct": u, "mfma_flops_per_launch": issued, "algorithmic_flops": alg})
         lines += ["", "## Matrix-core activity (rocprofv3 --pmc, one derived counter per pass)", "", "```",
-                  f"python -m paged_kv_cache_412_amd.profiling mfma --workload {workload} --out gpurun_out/prof",
+                  f"python -m paged_kv_cache_412_amd.profiling mfma --workload {workload} --out rocprof_out",
                   "  # = rocprofv3 --pmc MfmaUtil -f csv ... -- python3 bench.py --workload "
                   f"{workload} --steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline",
                   "  #   and the same with MfmaFlops", "```", "",
@@ -326,7 +326,7 @@ def summarize(workload: str, d: str) -> None:
         cyc = val["GRBM_GUI_ACTIVE"] / xcc
         rec["vmem"] = val
         lines += ["", "## Vector-memory path (rocprofv3 --pmc, one counter per pass)", "", "```",
-                  f"python -m paged_kv_cache_412_amd.profiling vmem --workload {workload} --out gpurun_out/prof",
+                  f"python -m paged_kv_cache_412_amd.profiling vmem --workload {workload} --out rocprof_out",
                   "  # = rocprofv3 --pmc <counter> -f csv ... -- python3 bench.py --workload "
                   f"{workload} --steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline --batches 0",
                   "  #   for each of: " + ", ".join(VMEM_COUNTERS), "```", "",
@@ -354,7 +354,7 @@ def summarize(workload: str, d: str) -> None:
         wc = val["SQ_WAVE_CYCLES"]
         lds = val["SQ_LDS_IDX_ACTIVE"]
         lines += ["", "## Where the waves' time goes (rocprofv3 --pmc, one counter per pass)", "", "```",
-                  f"python -m paged_kv_cache_412_amd.profiling pipe --workload {workload} --out gpurun_out/prof",
+                  f"python -m paged_kv_cache_412_amd.profiling pipe --workload {workload} --out rocprof_out",
                   "  # = rocprofv3 --pmc <counter> -f csv ... -- python3 bench.py --workload "
                   f"{workload} --steps {PMC_STEPS} --warmup {PMC_WARMUP} --no-cpu-baseline --batches 0",
                   "  #   for each of: " + ", ".join(PIPE_COUNTERS), "```", "",
@@ -453,8 +453,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-calibration", action="store_true",
                     help="pmc: skip the calibration copy (taken once by the calibration step)")
     ap.add_argument("--workload", default="llama13b")
-    ap.add_argument("--out", default="gpurun_out/prof")
-    ap.add_argument("--dir", default="gpurun_out/prof")
+    ap.add_argument("--out", default="rocprof_out")
+    ap.add_argument("--dir", default="rocprof_out")
     a = ap.parse_args(argv)
     if a.step == "trace":
         trace(a.workload, a.out)
