@@ -330,9 +330,9 @@ def gpu_facts() -> dict:
             continue
     props = torch.cuda.get_device_properties(0)
     name = torch.cuda.get_device_name(0)
-    # without libdrm's marketing-name table the runtime reports no name; the
-    # kernel driver's sysfs entries still carry the product name, the PCI
-    # device id and the VBIOS part number
+    # without libdrm's marketing-name table the runtime reports no name or a
+    # generic one; the kernel driver's sysfs entries still carry the product
+    # name, the PCI device id and the VBIOS part number
     sysfs = {}
     for card in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
         for key in ("product_name", "device", "vbios_version"):
@@ -343,7 +343,8 @@ def gpu_facts() -> dict:
                 pass
         if sysfs:
             break
-    return {"gpu_name": name or sysfs.get("product_name", ""), "gcn_arch": getattr(props, "gcnArchName", None),
+    return {"gpu_name": name or sysfs.get("product_name", ""), "gpu_product": sysfs.get("product_name"),
+            "gcn_arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "pci_device_id": sysfs.get("device"),
             "vbios": sysfs.get("vbios_version"), "rocm_version": ver, "hip_runtime": torch.version.hip}
 
