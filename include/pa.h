@@ -34,7 +34,14 @@
  *     arguments, except pa_swap_blocks, which also asks the HIP runtime
  *     which kind of memory each pool is.  The library never
  *     allocates, frees or synchronises device memory; it keeps no state
- *     except a per-device cache of the compute-unit count.
+ *     except per-device caches (the compute-unit count, each kernel's
+ *     occupancy, and pa_decode_no_alloc's scratch address).
+ *   - The decode step's calls (pa_copy_blocks, pa_append_kv or the slot
+ *     mapping and cache write, pa_decode_partition, pa_decode_reduce) and
+ *     the prefill step's can be captured into a HIP graph on `stream` and
+ *     replayed: none records a memset or waits on the host, and the kernels
+ *     reset the workspace's arrival counters themselves.  Replays give the
+ *     eager call's results bit for bit.
  *   - Host-side validation failures return a pa_status other than PA_OK,
  *     enqueue nothing and print nothing.  PA_ERR_LAUNCH reports a failed
  *     kernel launch (hipGetLastError).  Faults inside kernels surface at the
